@@ -1,0 +1,232 @@
+"""SpargeAttention2 hot path on AMD Instinct MI355X (gfx950).
+
+Python binding of libsa2 (include/sa2.h).  Every step of the path runs in the
+library's HIP kernels; this module only checks tensors, allocates outputs with
+PyTorch and passes pointers and the current stream through ctypes.
+
+    mask = build_mask(q, k, bq=128, bk=64, k_frac=0.03, p=0.9)
+    o, lse = attn_fwd(q, k, v, mask)
+    dq, dk, dv = attn_bwd(q, k, v, o, lse, do, mask)
+    out = sparse_attention(q, k, v, mask)          # autograd-aware
+
+Tensors are CUDA (HIP) tensors of shape [B, H, N, d], contiguous, all
+torch.bfloat16 or all torch.float32.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import Sa2Mask, check
+
+__all__ = ["BlockMask", "build_mask", "attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv",
+           "sparse_attention", "SparseAttention", "version", "mask_workspace_bytes",
+           "bwd_workspace_bytes"]
+
+_DTYPES = {torch.bfloat16: _lib.SA2_BF16, torch.float32: _lib.SA2_F32}
+
+
+def version() -> str:
+    return _lib.lib().sa2_version().decode()
+
+
+def _dtype_code(*ts: torch.Tensor) -> int:
+    dt = ts[0].dtype
+    if dt not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dt}: use bfloat16 or float32")
+    for t in ts:
+        if t.dtype != dt:
+            raise TypeError("all tensors must share one dtype")
+        if not t.is_cuda:
+            raise ValueError("tensors must be on a GPU device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous [B, H, N, d]")
+        if t.device != ts[0].device:
+            raise ValueError("tensors must be on one device")
+    return _DTYPES[dt]
+
+
+def _shape(t: torch.Tensor):
+    if t.dim() != 4:
+        raise ValueError("expected a [B, H, N, d] tensor")
+    return tuple(int(x) for x in t.shape)
+
+
+def _stream(dev: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _ptr(t: torch.Tensor) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr())
+
+
+class BlockMask:
+    """The hybrid block mask of every (batch, head): bitmap plus row and column lists.
+
+    Arrays (device, caller-owned through this object):
+      bitmap  uint8 [B, H, Tq, Tk]
+      row_cnt int32 [B, H, Tq];  row_idx int32 [B, H, Tq, Tk] (first row_cnt valid)
+      col_cnt int32 [B, H, Tk];  col_idx int32 [B, H, Tk, Tq] (first col_cnt valid)
+    """
+
+    def __init__(self, B: int, H: int, N: int, bq: int, bk: int, device):
+        self.B, self.H, self.N, self.bq, self.bk = B, H, N, bq, bk
+        self.Tq = -(-N // bq)
+        self.Tk = -(-N // bk)
+        dev = torch.device(device)
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.bitmap = torch.empty((B, H, self.Tq, self.Tk), dtype=torch.uint8, device=dev)
+        self.row_cnt = torch.empty((B, H, self.Tq), **i32)
+        self.row_idx = torch.empty((B, H, self.Tq, self.Tk), **i32)
+        self.col_cnt = torch.empty((B, H, self.Tk), **i32)
+        self.col_idx = torch.empty((B, H, self.Tk, self.Tq), **i32)
+        self._c = Sa2Mask(B, H, N, bq, bk, self.Tq, self.Tk,
+                          self.bitmap.data_ptr(), self.row_cnt.data_ptr(),
+                          self.row_idx.data_ptr(), self.col_cnt.data_ptr(),
+                          self.col_idx.data_ptr())
+
+    @property
+    def device(self):
+        return self.bitmap.device
+
+    def c_struct(self) -> Sa2Mask:
+        return self._c
+
+    def density(self) -> float:
+        """Kept block pairs over all block pairs (sparsity = 1 - density)."""
+        return float(self.row_cnt.sum().item()) / float(self.B * self.H * self.Tq * self.Tk)
+
+    def row_list(self, b: int, h: int, i: int) -> torch.Tensor:
+        n = int(self.row_cnt[b, h, i].item())
+        return self.row_idx[b, h, i, :n]
+
+    def col_list(self, b: int, h: int, j: int) -> torch.Tensor:
+        n = int(self.col_cnt[b, h, j].item())
+        return self.col_idx[b, h, j, :n]
+
+
+def mask_workspace_bytes(B, H, N, d, bq, bk) -> int:
+    return int(_lib.lib().sa2_mask_workspace_bytes(B, H, N, d, bq, bk))
+
+
+def build_mask(q: torch.Tensor, k: torch.Tensor, bq: int, bk: int, k_frac: float, p: float,
+               mask: BlockMask | None = None, workspace: torch.Tensor | None = None) -> BlockMask:
+    """Hybrid Top-k + Top-p block mask of q, k (sa2_build_mask)."""
+    dt = _dtype_code(q, k)
+    B, H, N, d = _shape(q)
+    if _shape(k) != (B, H, N, d):
+        raise ValueError("q and k must have the same shape")
+    if mask is None:
+        mask = BlockMask(B, H, N, bq, bk, q.device)
+    need = mask_workspace_bytes(B, H, N, d, bq, bk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    L = _lib.lib()
+    st = L.sa2_build_mask(_ptr(q), _ptr(k), dt, B, H, N, d, bq, bk, float(k_frac), float(p),
+                          ctypes.byref(mask.c_struct()), _ptr(workspace), workspace.numel(),
+                          _stream(q.device))
+    check("sa2_build_mask", st)
+    return mask
+
+
+def attn_fwd(q, k, v, mask: BlockMask, o=None, lse=None):
+    """Block-sparse attention forward (sa2_attn_fwd) -> (o, lse)."""
+    dt = _dtype_code(q, k, v)
+    B, H, N, d = _shape(q)
+    if _shape(k) != (B, H, N, d) or _shape(v) != (B, H, N, d):
+        raise ValueError("q, k, v must have the same shape")
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    st = _lib.lib().sa2_attn_fwd(_ptr(q), _ptr(k), _ptr(v), dt, B, H, N, d,
+                                 ctypes.byref(mask.c_struct()), _ptr(o), _ptr(lse),
+                                 _stream(q.device))
+    check("sa2_attn_fwd", st)
+    return o, lse
+
+
+def bwd_workspace_bytes(B, H, N, d) -> int:
+    return int(_lib.lib().sa2_bwd_workspace_bytes(B, H, N, d))
+
+
+def attn_bwd(q, k, v, o, lse, dout, mask: BlockMask, dq=None, dk=None, dv=None,
+             workspace=None):
+    """Gradients of the block-sparse attention (sa2_attn_bwd) -> (dq, dk, dv)."""
+    dt = _dtype_code(q, k, v, o, dout)
+    B, H, N, d = _shape(q)
+    for t in (k, v, o, dout):
+        if _shape(t) != (B, H, N, d):
+            raise ValueError("q, k, v, o, dout must have the same shape")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = bwd_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = _lib.lib().sa2_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), dt,
+                                 B, H, N, d, ctypes.byref(mask.c_struct()), _ptr(dq), _ptr(dk),
+                                 _ptr(dv), _ptr(workspace), workspace.numel(),
+                                 _stream(q.device))
+    check("sa2_attn_bwd", st)
+    return dq, dk, dv
+
+
+def _bwd_prep(q, k, v, dout, lse, extra):
+    dt = _dtype_code(q, k, v, dout, *extra)
+    B, H, N, d = _shape(q)
+    for t in (k, v, dout, *extra):
+        if _shape(t) != (B, H, N, d):
+            raise ValueError("q, k, v, o, dout must have the same shape")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    return dt, B, H, N, d
+
+
+def attn_bwd_dq(q, k, v, o, lse, dout, mask: BlockMask, workspace: torch.Tensor, dq=None):
+    """dQ, and Delta into `workspace` for attn_bwd_dkdv (sa2_attn_bwd_dq)."""
+    dt, B, H, N, d = _bwd_prep(q, k, v, dout, lse, (o,))
+    dq = torch.empty_like(q) if dq is None else dq
+    st = _lib.lib().sa2_attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                                    dt, B, H, N, d, ctypes.byref(mask.c_struct()), _ptr(dq),
+                                    _ptr(workspace), workspace.numel(), _stream(q.device))
+    check("sa2_attn_bwd_dq", st)
+    return dq
+
+
+def attn_bwd_dkdv(q, k, v, lse, dout, mask: BlockMask, workspace: torch.Tensor, dk=None,
+                  dv=None):
+    """dK, dV using the Delta a prior attn_bwd_dq left in `workspace` (sa2_attn_bwd_dkdv)."""
+    dt, B, H, N, d = _bwd_prep(q, k, v, dout, lse, ())
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    st = _lib.lib().sa2_attn_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dout), dt, B, H,
+                                      N, d, ctypes.byref(mask.c_struct()), _ptr(dk), _ptr(dv),
+                                      _ptr(workspace), workspace.numel(), _stream(q.device))
+    check("sa2_attn_bwd_dkdv", st)
+    return dk, dv
+
+
+class SparseAttention(torch.autograd.Function):
+    """Trainable block-sparse attention: the mask is a constant of the graph."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, mask):
+        o, lse = attn_fwd(q, k, v, mask)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.mask = mask
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        dq, dk, dv = attn_bwd(q, k, v, o, lse, do.contiguous(), ctx.mask)
+        return dq, dk, dv, None
+
+
+def sparse_attention(q, k, v, mask: BlockMask):
+    return SparseAttention.apply(q, k, v, mask)

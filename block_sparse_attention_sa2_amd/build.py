@@ -1,0 +1,68 @@
+"""Build libsa2.so (the HIP kernels and their C ABI) for gfx950, in-tree.
+
+    python -m block_sparse_attention_sa2_amd.build
+
+Each source under csrc/ is compiled to an object in _build/ (in parallel),
+then linked into block_sparse_attention_sa2_amd/libsa2.so next to this file.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+from pathlib import Path
+
+PKG = Path(__file__).resolve().parent
+ROOT = PKG.parent
+CSRC = PKG / "csrc"
+INCLUDE = ROOT / "include"
+BUILD = ROOT / "_build"
+LIB = PKG / "libsa2.so"
+ARCH = "gfx950"
+
+HIPCC_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    # packed-fp32 instructions stay off: they are emitted only from plain code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    f"-I{INCLUDE}", f"-I{CSRC}",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and Path(cand).exists():
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libsa2)")
+
+
+def _compile(src: Path, obj: Path, verbose: bool) -> None:
+    cmd = [hipcc(), *HIPCC_FLAGS, "-c", str(src), "-o", str(obj)]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"compiling {src.name} failed:\n{res.stdout}\n{res.stderr}")
+    if verbose:
+        print(f"  compiled {src.name}", flush=True)
+
+
+def build(verbose: bool = True) -> Path:
+    """Compile every HIP source and link libsa2.so; returns the library path."""
+    BUILD.mkdir(exist_ok=True)
+    sources = sorted(CSRC.glob("*.hip"))
+    objs = [BUILD / (s.stem + ".o") for s in sources]
+    with cf.ThreadPoolExecutor(min(len(sources), os.cpu_count() or 4)) as ex:
+        list(ex.map(lambda so: _compile(so[0], so[1], verbose), zip(sources, objs)))
+    tmp = LIB.with_suffix(".so.tmp")
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", str(tmp), *map(str, objs)]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"linking libsa2.so failed:\n{res.stdout}\n{res.stderr}")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}", flush=True)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose="-q" not in sys.argv)

@@ -1,0 +1,660 @@
+// Block-sparse attention, forward and backward (SpargeAttention2:
+// gist.science section 2C — whole tiles are kept or dropped and dropped tiles
+// cost neither matmul nor softmax; abstract item ii — the sparse attention is
+// trainable, so the backward runs over the same mask).
+//
+// Tiles: a query block of bq = 64 or 128 rows per workgroup (32 rows per
+// wave), key tiles of 64 tokens staged through LDS, bf16 MFMA 32x32x16 with
+// fp32 accumulation, online softmax in base 2 with the 1/sqrt(d) scale and
+// log2(e) folded into one multiplier.
+//
+// Orientation: the forward and dQ kernels compute S^T = K Q^T, so each lane
+// owns one query row (its softmax statistics stay in the lane, with one
+// exchange across the two half-waves), and the outputs are produced
+// transposed (O^T = V^T P^T, dQ^T = K^T dS^T).  The V^T and K^T operands are
+// read straight from row-major LDS tiles with ds_read_b64_tr_b16.
+//
+// Backward: dq_kernel first (one workgroup per query block over its row
+// list; it also forms Delta = rowsum(dO * O) for its rows and leaves it in the
+// workspace), then dkdv_kernel (one workgroup per key block, walking the query
+// blocks of its column list; each wave owns a 32-row slice of every listed
+// query block and accumulates the whole 64 x d dK and dV tile, and the four
+// partial tiles are summed in LDS in a fixed order).  No atomics: results are
+// bitwise reproducible.
+#include <math.h>
+
+#include "sa2_common.h"
+
+namespace sa2 {
+
+// ---------------------------------------------------------------------------
+// Tile staging: rows key0 .. key0+63 of a [N, D] head, zero past N.
+// ---------------------------------------------------------------------------
+template <typename T, int D, int NT>
+__device__ inline void fetch_tile(const T* __restrict__ x, int key0, int N, int tid, bf16x8* r) {
+  constexpr int CPR = D / 8, CPT = 64 * CPR / NT;
+  static_assert(CPT * NT == 64 * CPR, "tile chunks must divide evenly");
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int ch = tid + c * NT, row = ch / CPR, c8 = ch % CPR;
+    const int key = key0 + row;
+    r[c] = key < N ? load8(x + (size_t)key * D + c8 * 8) : zero8();
+  }
+}
+
+template <int D, int NT, int S>
+__device__ inline void put_tile(uint16_t* lds, int tid, const bf16x8* r) {
+  constexpr int CPR = D / 8, CPT = 64 * CPR / NT;
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int ch = tid + c * NT, row = ch / CPR, c8 = ch % CPR;
+    *reinterpret_cast<bf16x8*>(lds + row * S + c8 * 8) = r[c];
+  }
+}
+
+// A operand X^T[n][k-slots] of a 32x32x16 MFMA from a row-major LDS tile X
+// (stride S), for the 16 rows k = kbase .. kbase+15 and the 32 columns
+// n = nbase .. nbase+31.  Slot 8h + i (h = lane/32) maps to row
+// kbase + 8(i/4) + 4h + i%4, the same order in which a 32x32 accumulator
+// holds its rows, so an accumulator tile can be fed as the B operand.
+template <int S>
+__device__ inline bf16x8 tr_operand(const uint16_t* lds, int kbase, int nbase, int lane) {
+  const int h = lane >> 5;
+  const int r = kbase + 4 * h + ((lane & 15) >> 2);
+  const int c = nbase + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const bf16x4 lo = lds_read_tr(lds + r * S + c);
+  const bf16x4 hi = lds_read_tr(lds + (r + 8) * S + c);
+  return cat(lo, hi);
+}
+
+// Eight accumulator values e0 .. e0+7 as a bf16 B operand.
+__device__ inline bf16x8 pack8(const f32x16& a, int e0) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (__bf16)a[e0 + i];
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// Forward
+// ---------------------------------------------------------------------------
+template <typename T, int D, int NW>
+__global__ __launch_bounds__(NW * 64)
+void fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+                const int32_t* __restrict__ row_cnt, const int32_t* __restrict__ row_idx, int N,
+                int Tq, int Tk, float scale_log2, T* __restrict__ o, float* __restrict__ lse) {
+  constexpr int NT = NW * 64;
+  constexpr int KS = D + 8, VS = D + 16;
+  constexpr int NK = D / 16, ND = D / 32;
+  constexpr int CPT = 64 * (D / 8) / NT;
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[64 * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[64 * VS];
+
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = wg / Tq, qi = wg % Tq;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const size_t base = (size_t)bh * N * D;
+  const T* kh = k + base;
+  const T* vh = v + base;
+  const int qrow = qi * (NW * 32) + w * 32 + l32;
+  const bool qvalid = qrow < N;
+
+  bf16x8 qf[NK];
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk)
+    qf[kk] = qvalid ? load8(q + base + (size_t)qrow * D + 16 * kk + 8 * h) : zero8();
+
+  f32x16 acc[ND];
+#pragma unroll
+  for (int db = 0; db < ND; ++db) acc[db] = zero16();
+  float m = -INFINITY, lsum = 0.f;
+
+  const int cnt = row_cnt[wg];
+  const int32_t* lst = row_idx + (size_t)wg * Tk;
+  bf16x8 kr[CPT], vr[CPT];
+  if (cnt > 0) {
+    fetch_tile<T, D, NT>(kh, lst[0] * 64, N, tid, kr);
+    fetch_tile<T, D, NT>(vh, lst[0] * 64, N, tid, vr);
+  }
+  for (int t = 0; t < cnt; ++t) {
+    const int key0 = lst[t] * 64;
+    __syncthreads();
+    put_tile<D, NT, KS>(k_lds, tid, kr);
+    put_tile<D, NT, VS>(v_lds, tid, vr);
+    __syncthreads();
+    if (t + 1 < cnt) {
+      const int nk0 = lst[t + 1] * 64;
+      fetch_tile<T, D, NT>(kh, nk0, N, tid, kr);
+      fetch_tile<T, D, NT>(vh, nk0, N, tid, vr);
+    }
+    // S^T for keys key0 .. key0+63 (two 32-key halves) against this lane's query
+    f32x16 s[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      s[b] = zero16();
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk)
+        s[b] = mfma32(lds_read8(k_lds + (32 * b + l32) * KS + 16 * kk + 8 * h), qf[kk], s[b]);
+    }
+    const bool tail = key0 + 64 > N;
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float x = s[b][e] * scale_log2;
+        if (tail && key0 + 32 * b + 8 * (e >> 2) + 4 * h + (e & 3) >= N) x = -INFINITY;
+        s[b][e] = x;
+        mloc = fmaxf(mloc, x);
+      }
+    mloc = wave_max32(mloc);
+    const float mnew = fmaxf(m, mloc);
+    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+    m = mnew;
+    float ps = 0.f;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float pv = __builtin_amdgcn_exp2f(s[b][e] - mnew);
+        s[b][e] = pv;
+        ps += pv;
+      }
+    lsum = lsum * alpha + ps;
+#pragma unroll
+    for (int db = 0; db < ND; ++db) acc[db] *= alpha;
+    // O^T += V^T P^T over four 16-key steps
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const bf16x8 pf = pack8(s[tt >> 1], 8 * (tt & 1));
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+        acc[db] = mfma32(tr_operand<VS>(v_lds, 16 * tt, 32 * db, lane), pf, acc[db]);
+    }
+  }
+  const float ltot = lsum + __shfl_xor(lsum, 32);
+  const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+  if (qvalid) {
+    T* orow = o + base + (size_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        store4(orow + 32 * db + 8 * g + 4 * h, acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv,
+               acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv);
+    if (h == 0)
+      lse[(size_t)bh * N + qrow] = ltot > 0.f ? (m + __log2f(ltot)) * kLn2 : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Backward dK, dV: one workgroup (4 waves) per key block of 64 keys.
+// ---------------------------------------------------------------------------
+template <typename T, int D, int BQ>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+                 const T* __restrict__ dout, const float* __restrict__ lse,
+                 const float* __restrict__ delta, const int32_t* __restrict__ col_cnt,
+                 const int32_t* __restrict__ col_idx, int N, int Tq, int Tk, float scale_log2,
+                 float scale, T* __restrict__ dk, T* __restrict__ dv) {
+  constexpr int NT = 256;
+  constexpr int KS = D + 8;   // K, V tiles: 16-byte fragment reads
+  constexpr int CS = D + 16;  // per-wave Q / dO slices: transposed reads
+  constexpr int NK = D / 16, ND = D / 32;
+  constexpr int CPT = 64 * (D / 8) / NT;
+  constexpr int SUB = BQ / 32;  // 32-row slices per query block
+  constexpr int RS = D + 4;     // fp32 reduction tile stride
+  constexpr int SLICE_BYTES = 2 * 4 * 32 * CS * 2;
+  static_assert(SLICE_BYTES >= 64 * RS * 4, "reduction tile must fit in the slice area");
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[64 * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[64 * KS];
+  __shared__ __attribute__((aligned(16))) unsigned char slice_mem[SLICE_BYTES];
+  __shared__ __attribute__((aligned(16))) float stat_lds[4][2][32];
+
+  uint16_t* q_lds = reinterpret_cast<uint16_t*>(slice_mem);  // [4][32*CS]
+  uint16_t* do_lds = q_lds + 4 * 32 * CS;                    // [4][32*CS]
+  float* red = reinterpret_cast<float*>(slice_mem);          // [64][RS] after the loop
+
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = wg / Tk, kj = wg % Tk;
+  const int key0 = kj * 64;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const size_t base = (size_t)bh * N * D;
+
+  {
+    bf16x8 r[CPT];
+    fetch_tile<T, D, NT>(k + base, key0, N, tid, r);
+    put_tile<D, NT, KS>(k_lds, tid, r);
+    fetch_tile<T, D, NT>(v + base, key0, N, tid, r);
+    put_tile<D, NT, KS>(v_lds, tid, r);
+  }
+  __syncthreads();
+
+  uint16_t* my_q = q_lds + w * 32 * CS;
+  uint16_t* my_do = do_lds + w * 32 * CS;
+  float* my_lse = stat_lds[w][0];
+  float* my_dl = stat_lds[w][1];
+
+  f32x16 accv[ND][2], acck[ND][2];
+#pragma unroll
+  for (int db = 0; db < ND; ++db)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      accv[db][kb] = zero16();
+      acck[db][kb] = zero16();
+    }
+
+  const int cnt = col_cnt[wg];
+  const int32_t* lst = col_idx + (size_t)wg * Tq;
+  const int total = cnt * SUB;
+  const bool ktail = key0 + 64 > N;
+
+  bf16x8 qf[NK], df[NK];
+  float stat = 0.f;
+  auto fetch = [&](int c) {
+    const int q0 = lst[c / SUB] * BQ + (c % SUB) * 32;
+    const int row = q0 + l32;
+    const bool ok = row < N;
+    const size_t off = base + (size_t)row * D + 8 * h;
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      qf[kk] = ok ? load8(q + off + 16 * kk) : zero8();
+      df[kk] = ok ? load8(dout + off + 16 * kk) : zero8();
+    }
+    // lanes 0-31 carry log2-scaled LSE (+inf for padding rows: P = 0),
+    // lanes 32-63 carry Delta
+    const size_t srow = (size_t)bh * N + row;
+    stat = h == 0 ? (ok ? lse[srow] * kLog2e : INFINITY) : (ok ? delta[srow] : 0.f);
+  };
+
+  int c = w;
+  if (c < total) fetch(c);
+  while (c < total) {
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      *reinterpret_cast<bf16x8*>(my_q + l32 * CS + 16 * kk + 8 * h) = qf[kk];
+      *reinterpret_cast<bf16x8*>(my_do + l32 * CS + 16 * kk + 8 * h) = df[kk];
+    }
+    stat_lds[w][h][l32] = stat;
+    wave_lds_sync();
+    // S = Q K^T and dP = dO V^T for this slice's 32 rows and the 64 keys
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = zero16();
+      dp[kb] = zero16();
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        s[kb] = mfma32(qf[kk], lds_read8(k_lds + (32 * kb + l32) * KS + 16 * kk + 8 * h), s[kb]);
+        dp[kb] = mfma32(df[kk], lds_read8(v_lds + (32 * kb + l32) * KS + 16 * kk + 8 * h), dp[kb]);
+      }
+    }
+    const int cn = c + 4;
+    if (cn < total) fetch(cn);
+    // P = exp(S/sqrt(d) - LSE), dS = P * (dP - Delta); rows 8g+4h+i of the slice
+    f32x4 L[4], Dl[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      L[g] = *reinterpret_cast<const f32x4*>(my_lse + 8 * g + 4 * h);
+      Dl[g] = *reinterpret_cast<const f32x4*>(my_dl + 8 * g + 4 * h);
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const bool kval = !ktail || key0 + 32 * kb + l32 < N;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float pv = __builtin_amdgcn_exp2f(s[kb][e] * scale_log2 - L[e >> 2][e & 3]);
+        pv = kval ? pv : 0.f;
+        s[kb][e] = pv;
+        dp[kb][e] = pv * (dp[kb][e] - Dl[e >> 2][e & 3]);
+      }
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS over the slice's 32 rows
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      bf16x8 pb[2], sb[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        pb[kb] = pack8(s[kb], 8 * t);
+        sb[kb] = pack8(dp[kb], 8 * t);
+      }
+#pragma unroll
+      for (int db = 0; db < ND; ++db) {
+        const bf16x8 ao = tr_operand<CS>(my_do, 16 * t, 32 * db, lane);
+        const bf16x8 aq = tr_operand<CS>(my_q, 16 * t, 32 * db, lane);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          accv[db][kb] = mfma32(ao, pb[kb], accv[db][kb]);
+          acck[db][kb] = mfma32(aq, sb[kb], acck[db][kb]);
+        }
+      }
+    }
+    c = cn;
+  }
+
+  // Sum the four waves' tiles in LDS (wave order 0..3), then store.
+  // Accumulator element e of (db, kb) is row d = 32db + 8(e/4) + 4h + e%4,
+  // column key = 32kb + l32 of the transposed tile.
+  for (int which = 0; which < 2; ++which) {
+    __syncthreads();
+    for (int ww = 0; ww < 4; ++ww) {
+      if (w == ww) {
+#pragma unroll
+        for (int db = 0; db < ND; ++db)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int dd = 32 * db + 8 * (e >> 2) + 4 * h + (e & 3);
+              float* p = red + (32 * kb + l32) * RS + dd;
+              const float val = which == 0 ? accv[db][kb][e] : acck[db][kb][e];
+              *p = (ww == 0) ? val : *p + val;
+            }
+      }
+      __syncthreads();
+    }
+    T* out = (which == 0 ? dv : dk) + base;
+    const float mul = which == 0 ? 1.f : scale;
+    for (int ch = tid; ch < 64 * D / 4; ch += NT) {
+      const int row = ch / (D / 4), c4 = (ch % (D / 4)) * 4;
+      const int key = key0 + row;
+      if (key < N) {
+        const float* p = red + row * RS + c4;
+        store4(out + (size_t)key * D + c4, p[0] * mul, p[1] * mul, p[2] * mul, p[3] * mul);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Backward dQ: one workgroup per query block, walking its row list.
+// ---------------------------------------------------------------------------
+template <typename T, int D, int NW>
+__global__ __launch_bounds__(NW * 64)
+void dq_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+               const T* __restrict__ o, const T* __restrict__ dout, const float* __restrict__ lse,
+               float* __restrict__ delta, const int32_t* __restrict__ row_cnt,
+               const int32_t* __restrict__ row_idx, int N, int Tq, int Tk, float scale_log2,
+               float scale, T* __restrict__ dq) {
+  constexpr int NT = NW * 64;
+  constexpr int KS = D + 16;  // K: fragment reads and transposed reads
+  constexpr int VS = D + 8;   // V: fragment reads
+  constexpr int NK = D / 16, ND = D / 32;
+  constexpr int CPT = 64 * (D / 8) / NT;
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[64 * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[64 * VS];
+
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = wg / Tq, qi = wg % Tq;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const size_t base = (size_t)bh * N * D;
+  const T* kh = k + base;
+  const T* vh = v + base;
+  const int qrow = qi * (NW * 32) + w * 32 + l32;
+  const bool qvalid = qrow < N;
+
+  bf16x8 qf[NK], df[NK];
+  float dpart = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk) {
+    const size_t off = base + (size_t)qrow * D + 16 * kk + 8 * h;
+    qf[kk] = qvalid ? load8(q + off) : zero8();
+    df[kk] = qvalid ? load8(dout + off) : zero8();
+    if (qvalid) {
+      float a[8], b[8];
+      load8_f32(o + off, a);
+      load8_f32(dout + off, b);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dpart += a[i] * b[i];
+    }
+  }
+  // Delta = rowsum(dO * O): the two half-waves hold alternate 8-wide pieces
+  // of the row.  It is kept for the dK/dV kernel.  Padding rows: dO = 0 and
+  // Delta = 0 give dS = 0 whatever P is.
+  const float dl = dpart + __shfl_xor(dpart, 32);
+  if (qvalid && h == 0) delta[(size_t)bh * N + qrow] = dl;
+  const float l2 = qvalid ? lse[(size_t)bh * N + qrow] * kLog2e : 0.f;
+
+  f32x16 acc[ND];
+#pragma unroll
+  for (int db = 0; db < ND; ++db) acc[db] = zero16();
+
+  const int cnt = row_cnt[wg];
+  const int32_t* lst = row_idx + (size_t)wg * Tk;
+  bf16x8 kr[CPT], vr[CPT];
+  if (cnt > 0) {
+    fetch_tile<T, D, NT>(kh, lst[0] * 64, N, tid, kr);
+    fetch_tile<T, D, NT>(vh, lst[0] * 64, N, tid, vr);
+  }
+  for (int t = 0; t < cnt; ++t) {
+    const int key0 = lst[t] * 64;
+    __syncthreads();
+    put_tile<D, NT, KS>(k_lds, tid, kr);
+    put_tile<D, NT, VS>(v_lds, tid, vr);
+    __syncthreads();
+    if (t + 1 < cnt) {
+      const int nk0 = lst[t + 1] * 64;
+      fetch_tile<T, D, NT>(kh, nk0, N, tid, kr);
+      fetch_tile<T, D, NT>(vh, nk0, N, tid, vr);
+    }
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      s[b] = zero16();
+      dp[b] = zero16();
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        s[b] = mfma32(lds_read8(k_lds + (32 * b + l32) * KS + 16 * kk + 8 * h), qf[kk], s[b]);
+        dp[b] = mfma32(lds_read8(v_lds + (32 * b + l32) * VS + 16 * kk + 8 * h), df[kk], dp[b]);
+      }
+    }
+    const bool tail = key0 + 64 > N;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float pv = __builtin_amdgcn_exp2f(s[b][e] * scale_log2 - l2);
+        if (tail && key0 + 32 * b + 8 * (e >> 2) + 4 * h + (e & 3) >= N) pv = 0.f;
+        s[b][e] = pv * (dp[b][e] - dl);
+      }
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const bf16x8 sf = pack8(s[tt >> 1], 8 * (tt & 1));
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+        acc[db] = mfma32(tr_operand<KS>(k_lds, 16 * tt, 32 * db, lane), sf, acc[db]);
+    }
+  }
+  if (qvalid) {
+    T* row = dq + base + (size_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        store4(row + 32 * db + 8 * g + 4 * h, acc[db][4 * g] * scale, acc[db][4 * g + 1] * scale,
+               acc[db][4 * g + 2] * scale, acc[db][4 * g + 3] * scale);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+static sa2_status check_common(const char* fn, int dtype, int B, int H, int N, int d,
+                               const sa2_mask* m) {
+  if (!m) return fail(SA2_EINVAL, std::string(fn) + ": null mask");
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0)
+    return fail(SA2_EINVAL, std::string(fn) + ": B, H, N, d must be positive");
+  if (dtype != SA2_BF16 && dtype != SA2_F32)
+    return fail(SA2_EINVAL, std::string(fn) + ": unknown dtype");
+  if (m->B != B || m->H != H || m->N != N || m->bq <= 0 || m->bk <= 0 ||
+      m->Tq != cdiv(N, m->bq) || m->Tk != cdiv(N, m->bk))
+    return fail(SA2_EINVAL, std::string(fn) + ": mask geometry does not match the call");
+  if (d != 64 && d != 128) return fail(SA2_EUNSUPPORTED, std::string(fn) + ": d must be 64 or 128");
+  if (m->bk != 64) return fail(SA2_EUNSUPPORTED, std::string(fn) + ": key blocks must be 64 tokens");
+  if (m->bq != 64 && m->bq != 128)
+    return fail(SA2_EUNSUPPORTED, std::string(fn) + ": query blocks must be 64 or 128 tokens");
+  if ((size_t)B * H * m->Tq > 0x7fffffff || (size_t)B * H * m->Tk > 0x7fffffff)
+    return fail(SA2_EUNSUPPORTED, std::string(fn) + ": too many blocks");
+  return SA2_OK;
+}
+
+template <typename T, int D, int NW>
+static void launch_fwd(const void* q, const void* k, const void* v, const sa2_mask* m, int BH,
+                       int N, float sl2, void* o, float* lse, hipStream_t s) {
+  fwd_kernel<T, D, NW><<<BH * m->Tq, NW * 64, 0, s>>>(
+      static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), m->row_cnt,
+      m->row_idx, N, m->Tq, m->Tk, sl2, static_cast<T*>(o), lse);
+}
+
+template <typename T, int D>
+static void dispatch_fwd(const void* q, const void* k, const void* v, const sa2_mask* m, int BH,
+                         int N, float sl2, void* o, float* lse, hipStream_t s) {
+  if (m->bq == 128) launch_fwd<T, D, 4>(q, k, v, m, BH, N, sl2, o, lse, s);
+  else launch_fwd<T, D, 2>(q, k, v, m, BH, N, sl2, o, lse, s);
+}
+
+struct BwdArgs {
+  const void *q, *k, *v, *o, *dout;
+  const float* lse;
+  const sa2_mask* m;
+  int BH, N;
+  float sl2, scale;
+  void *dq, *dk, *dv;
+  float* delta;
+  hipStream_t s;
+};
+
+template <typename T, int D>
+static void launch_dq(const BwdArgs& a) {
+  const sa2_mask* m = a.m;
+#define SA2_DQ_ARGS                                                                          \
+  static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),          \
+      static_cast<const T*>(a.o), static_cast<const T*>(a.dout), a.lse, a.delta, m->row_cnt,  \
+      m->row_idx, a.N, m->Tq, m->Tk, a.sl2, a.scale, static_cast<T*>(a.dq)
+  if (m->bq == 128) dq_kernel<T, D, 4><<<a.BH * m->Tq, 256, 0, a.s>>>(SA2_DQ_ARGS);
+  else dq_kernel<T, D, 2><<<a.BH * m->Tq, 128, 0, a.s>>>(SA2_DQ_ARGS);
+#undef SA2_DQ_ARGS
+}
+
+template <typename T, int D>
+static void launch_dkdv(const BwdArgs& a) {
+  const sa2_mask* m = a.m;
+#define SA2_DKDV_ARGS                                                                         \
+  static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),          \
+      static_cast<const T*>(a.dout), a.lse, a.delta, m->col_cnt, m->col_idx, a.N, m->Tq, m->Tk, \
+      a.sl2, a.scale, static_cast<T*>(a.dk), static_cast<T*>(a.dv)
+  if (m->bq == 128) dkdv_kernel<T, D, 128><<<a.BH * m->Tk, 256, 0, a.s>>>(SA2_DKDV_ARGS);
+  else dkdv_kernel<T, D, 64><<<a.BH * m->Tk, 256, 0, a.s>>>(SA2_DKDV_ARGS);
+#undef SA2_DKDV_ARGS
+}
+
+template <typename T, int D> struct DqLaunch { static void run(const BwdArgs& a) { launch_dq<T, D>(a); } };
+template <typename T, int D> struct DkdvLaunch { static void run(const BwdArgs& a) { launch_dkdv<T, D>(a); } };
+
+template <template <typename, int> class F>
+static void by_type(int dtype, int d, const BwdArgs& a) {
+  if (dtype == SA2_BF16) {
+    if (d == 128) F<bf16_t, 128>::run(a); else F<bf16_t, 64>::run(a);
+  } else {
+    if (d == 128) F<float, 128>::run(a); else F<float, 64>::run(a);
+  }
+}
+
+static sa2_status check_bwd(const char* fn, const void* q, const void* k, const void* v,
+                            const float* lse, const void* dout, int dtype, int B, int H, int N,
+                            int d, const sa2_mask* m, void* ws, size_t ws_bytes) {
+  if (!q || !k || !v || !lse || !dout || !ws) return fail(SA2_EINVAL, std::string(fn) + ": null pointer");
+  if (sa2_status st = check_common(fn, dtype, B, H, N, d, m)) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(lse) || !aligned16(dout))
+    return fail(SA2_EINVAL, std::string(fn) + ": pointers must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+    return fail(SA2_EINVAL, std::string(fn) + ": workspace not 256-byte aligned");
+  if (ws_bytes < sa2_bwd_workspace_bytes(B, H, N, d))
+    return fail(SA2_EINVAL, std::string(fn) + ": workspace smaller than sa2_bwd_workspace_bytes()");
+  return SA2_OK;
+}
+
+static BwdArgs bwd_args(const void* q, const void* k, const void* v, const void* o,
+                        const float* lse, const void* dout, int B, int H, int N, int d,
+                        const sa2_mask* m, void* dq, void* dk, void* dv, void* ws, void* stream) {
+  const double sc = 1.0 / sqrt((double)d);
+  return BwdArgs{q, k, v, o, dout, lse, m, B * H, N, (float)(1.4426950408889634 * sc),
+                 (float)sc, dq, dk, dv, static_cast<float*>(ws),
+                 reinterpret_cast<hipStream_t>(stream)};
+}
+
+}  // namespace sa2
+
+using namespace sa2;
+
+extern "C" sa2_status sa2_attn_fwd(const void* q, const void* k, const void* v, int dtype, int B,
+                                   int H, int N, int d, const sa2_mask* m, void* o, float* lse,
+                                   void* stream) {
+  if (!q || !k || !v || !o || !lse) return fail(SA2_EINVAL, "sa2_attn_fwd: null pointer");
+  if (sa2_status st = check_common("sa2_attn_fwd", dtype, B, H, N, d, m)) return st;
+  if (!m->row_cnt || !m->row_idx) return fail(SA2_EINVAL, "sa2_attn_fwd: mask row lists are null");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return fail(SA2_EINVAL, "sa2_attn_fwd: pointers must be 16-byte aligned");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int BH = B * H;
+  const float sl2 = (float)(1.4426950408889634 / sqrt((double)d));
+  if (dtype == SA2_BF16) {
+    if (d == 128) dispatch_fwd<bf16_t, 128>(q, k, v, m, BH, N, sl2, o, lse, s);
+    else dispatch_fwd<bf16_t, 64>(q, k, v, m, BH, N, sl2, o, lse, s);
+  } else {
+    if (d == 128) dispatch_fwd<float, 128>(q, k, v, m, BH, N, sl2, o, lse, s);
+    else dispatch_fwd<float, 64>(q, k, v, m, BH, N, sl2, o, lse, s);
+  }
+  return check_launch("fwd_kernel");
+}
+
+extern "C" size_t sa2_bwd_workspace_bytes(int B, int H, int N, int d) {
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return 0;
+  return ((size_t)B * H * N * 4 + 255) & ~(size_t)255;
+}
+
+extern "C" sa2_status sa2_attn_bwd_dq(const void* q, const void* k, const void* v,
+                                      const void* o, const float* lse, const void* dout,
+                                      int dtype, int B, int H, int N, int d, const sa2_mask* m,
+                                      void* dq, void* ws, size_t ws_bytes, void* stream) {
+  if (sa2_status st = check_bwd("sa2_attn_bwd_dq", q, k, v, lse, dout, dtype, B, H, N, d, m, ws,
+                                ws_bytes))
+    return st;
+  if (!o || !dq) return fail(SA2_EINVAL, "sa2_attn_bwd_dq: null pointer");
+  if (!aligned16(o) || !aligned16(dq))
+    return fail(SA2_EINVAL, "sa2_attn_bwd_dq: pointers must be 16-byte aligned");
+  if (!m->row_cnt || !m->row_idx) return fail(SA2_EINVAL, "sa2_attn_bwd_dq: mask row lists are null");
+  by_type<DqLaunch>(dtype, d, bwd_args(q, k, v, o, lse, dout, B, H, N, d, m, dq, nullptr, nullptr, ws, stream));
+  return check_launch("dq_kernel");
+}
+
+extern "C" sa2_status sa2_attn_bwd_dkdv(const void* q, const void* k, const void* v,
+                                        const float* lse, const void* dout, int dtype, int B,
+                                        int H, int N, int d, const sa2_mask* m, void* dk,
+                                        void* dv, void* ws, size_t ws_bytes, void* stream) {
+  if (sa2_status st = check_bwd("sa2_attn_bwd_dkdv", q, k, v, lse, dout, dtype, B, H, N, d, m,
+                                ws, ws_bytes))
+    return st;
+  if (!dk || !dv) return fail(SA2_EINVAL, "sa2_attn_bwd_dkdv: null pointer");
+  if (!aligned16(dk) || !aligned16(dv))
+    return fail(SA2_EINVAL, "sa2_attn_bwd_dkdv: pointers must be 16-byte aligned");
+  if (!m->col_cnt || !m->col_idx) return fail(SA2_EINVAL, "sa2_attn_bwd_dkdv: mask column lists are null");
+  by_type<DkdvLaunch>(dtype, d, bwd_args(q, k, v, nullptr, lse, dout, B, H, N, d, m, nullptr, dk, dv, ws, stream));
+  return check_launch("dkdv_kernel");
+}
+
+extern "C" sa2_status sa2_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                                   const float* lse, const void* dout, int dtype, int B, int H,
+                                   int N, int d, const sa2_mask* m, void* dq, void* dk, void* dv,
+                                   void* ws, size_t ws_bytes, void* stream) {
+  if (sa2_status st = sa2_attn_bwd_dq(q, k, v, o, lse, dout, dtype, B, H, N, d, m, dq, ws,
+                                      ws_bytes, stream))
+    return st == SA2_OK ? st : fail(st, std::string("sa2_attn_bwd: ") + sa2_last_error());
+  if (sa2_status st = sa2_attn_bwd_dkdv(q, k, v, lse, dout, dtype, B, H, N, d, m, dk, dv, ws,
+                                        ws_bytes, stream))
+    return fail(st, std::string("sa2_attn_bwd: ") + sa2_last_error());
+  return SA2_OK;
+}

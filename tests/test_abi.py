@@ -1,0 +1,108 @@
+"""The C ABI of libsa2 on a host without a GPU: it loads, exports what
+include/sa2.h declares, and rejects malformed calls before touching a device.
+"""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+from block_sparse_attention_sa2_amd import _lib
+
+HEADER = Path(__file__).resolve().parents[1] / "include" / "sa2.h"
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sa2_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    assert names == sorted(_lib.SIGNATURES), names
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert L.sa2_version().decode().startswith("sa2 ")
+
+
+def test_workspace_sizes():
+    L = _lib.lib()
+    B, H, N, d, bq, bk = 1, 12, 32760, 128, 128, 64
+    Tq, Tk = 256, 512
+    up = lambda x: (x + 255) // 256 * 256
+    want = up(B * H * Tq * d * 8) + up(B * H * Tk * d * 8) + up(B * H * Tq * Tk * 8)
+    assert L.sa2_mask_workspace_bytes(B, H, N, d, bq, bk) == want
+    assert L.sa2_mask_workspace_bytes(0, H, N, d, bq, bk) == 0
+    assert L.sa2_bwd_workspace_bytes(B, H, N, d) == up(B * H * N * 4)
+
+
+def _mask(B=1, H=1, N=256, bq=64, bk=64):
+    Tq, Tk = -(-N // bq), -(-N // bk)
+    fake = 1 << 20   # never dereferenced: validation fails first
+    return _lib.Sa2Mask(B, H, N, bq, bk, Tq, Tk, fake, fake, fake, fake, fake)
+
+
+FAKE = ctypes.c_void_p(1 << 20)
+
+
+def _status_and_msg(st):
+    return st, _lib.lib().sa2_last_error().decode()
+
+
+def test_build_mask_validation():
+    L = _lib.lib()
+    m = _mask()
+    ws = ctypes.c_void_p(1 << 20)
+    args = lambda **kw: dict(dict(q=FAKE, k=FAKE, dt=0, B=1, H=1, N=256, d=64, bq=64, bk=64,
+                                  kf=0.1, p=0.5, m=ctypes.byref(m), ws=ws, wsb=1 << 30), **kw)
+    call = lambda a: L.sa2_build_mask(a["q"], a["k"], a["dt"], a["B"], a["H"], a["N"], a["d"],
+                                      a["bq"], a["bk"], a["kf"], a["p"], a["m"], a["ws"],
+                                      a["wsb"], None)
+    cases = [
+        (dict(q=None), _lib.SA2_EINVAL),
+        (dict(N=0), _lib.SA2_EINVAL),
+        (dict(dt=7), _lib.SA2_EINVAL),
+        (dict(d=60), _lib.SA2_EUNSUPPORTED),
+        (dict(kf=0.0, p=0.0), _lib.SA2_EINVAL),
+        (dict(kf=float("nan")), _lib.SA2_EINVAL),
+        (dict(q=ctypes.c_void_p((1 << 20) + 4)), _lib.SA2_EINVAL),
+        (dict(ws=ctypes.c_void_p((1 << 20) + 64)), _lib.SA2_EINVAL),
+        (dict(N=300), _lib.SA2_EINVAL),          # mask geometry no longer matches
+        (dict(wsb=16), _lib.SA2_EINVAL),
+    ]
+    for kw, want in cases:
+        st, msg = _status_and_msg(call(args(**kw)))
+        assert st == want, (kw, st, msg)
+        assert msg.startswith("sa2_build_mask"), msg
+
+
+def test_attention_validation():
+    L = _lib.lib()
+    m = _mask()
+    st, msg = _status_and_msg(L.sa2_attn_fwd(FAKE, FAKE, FAKE, 0, 1, 1, 256, 96,
+                                             ctypes.byref(m), FAKE, FAKE, None))
+    assert st == _lib.SA2_EUNSUPPORTED and "d must be" in msg
+    m2 = _mask(bk=32)
+    st, msg = _status_and_msg(L.sa2_attn_fwd(FAKE, FAKE, FAKE, 0, 1, 1, 256, 64,
+                                             ctypes.byref(m2), FAKE, FAKE, None))
+    assert st == _lib.SA2_EUNSUPPORTED and "key blocks" in msg
+    st, msg = _status_and_msg(L.sa2_attn_fwd(FAKE, FAKE, None, 0, 1, 1, 256, 64,
+                                             ctypes.byref(m), FAKE, FAKE, None))
+    assert st == _lib.SA2_EINVAL
+    st, msg = _status_and_msg(L.sa2_attn_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 1, 1, 256,
+                                             64, ctypes.byref(m), FAKE, FAKE, FAKE, FAKE, 16,
+                                             None))
+    assert st == _lib.SA2_EINVAL and "workspace" in msg
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    import block_sparse_attention_sa2_amd as sa2
+    q = torch.zeros(1, 1, 64, 64)
+    with pytest.raises(ValueError):
+        sa2.build_mask(q, q, 64, 64, 0.5, 0.5)

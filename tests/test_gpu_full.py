@@ -1,0 +1,227 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times (one call per step over all heads).
+
+* Wan2.1-1.3B-shaped layer (H=12, N=32760 = 21x30x52, d=128, bf16, q-block
+  128, k-block 64, k = 3%, p tuned for 5% density), forward and backward:
+  the whole mask of every head against the oracle; O, LSE, dQ, dK, dV on
+  sampled blocks of every head (first, a random interior one, the ragged
+  last one); closed-form invariants of the gradients on every head.
+* 14B-720p-shaped layer (H=40, N=75600 = 21x45x80): the mask of heads 0 and
+  39 against the oracle, sampled attention blocks of those heads, and the
+  union invariants on every head.
+* Mask-rule stress (H=8, N=16384): three score regimes x four densities; the
+  hybrid mask contains the Top-k-only and Top-p-only masks on every head and
+  equals their union; head 0 against the oracle; sampled attention blocks.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_sa2_amd as sa2
+import oracle as O
+import workloads as W
+
+from parity import (GRAD_REL_FRO, check_forward, check_grad, check_lists, compare_mask,
+                    device_inputs, f64, rel_fro)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _head_np(ref, h):
+    return tuple(ref[t][0, h] for t in ("q", "k", "v", "do") if t in ref)
+
+
+def _row_lists(mask_np_bm):
+    return [np.nonzero(r)[0] for r in mask_np_bm]
+
+
+def _spot_check(w, ref, h, bm_h, o, lse, grads, rng, n_q=3, n_k=3):
+    """O/LSE and gradients of a few blocks of head h against the oracle."""
+    Q, K, V, dO = _head_np(ref, h)
+    rows = _row_lists(bm_h)
+    Tq, Tk = bm_h.shape
+    qbs = sorted({0, Tq - 1, *rng.integers(1, Tq - 1, size=n_q - 2).tolist()})
+    kbs = sorted({0, Tk - 1, *rng.integers(1, Tk - 1, size=n_k - 2).tolist()})
+    o_h, l_h = f64(o[0, h]), f64(lse[0, h])
+    for i in qbs:
+        lo, hi = O.block_range(i, w.bq, w.N)
+        oi, li = O.forward_query_block(Q, K, V, rows, w.bq, w.bk, i)
+        check_forward(o_h[lo:hi], l_h[lo:hi], oi, li, f"{w.name} h{h} qblock {i}")
+    if grads is None:
+        return
+    dq, dk, dv = (f64(g[0, h]) for g in grads)
+    mine, want = [], []
+    for i in qbs:
+        lo, hi = O.block_range(i, w.bq, w.N)
+        mine.append(dq[lo:hi])
+        want.append(O.dq_query_block(Q, K, V, dO, rows, w.bq, w.bk, i))
+    check_grad(np.concatenate(mine), np.concatenate(want), f"{w.name} h{h} dq")
+    mk, wk, mv, wv = [], [], [], []
+    for j in kbs:
+        lo, hi = O.block_range(j, w.bk, w.N)
+        k_j, v_j = O.dkdv_key_block(Q, K, V, dO, rows, w.bq, w.bk, j)
+        mk.append(dk[lo:hi]); wk.append(k_j)
+        mv.append(dv[lo:hi]); wv.append(v_j)
+    if np.linalg.norm(np.concatenate(wk)) > 0:
+        check_grad(np.concatenate(mk), np.concatenate(wk), f"{w.name} h{h} dk")
+        check_grad(np.concatenate(mv), np.concatenate(wv), f"{w.name} h{h} dv")
+
+
+def _invariants(q, k, dq, dk, dv, do, h):
+    """sum_u dK_u = 0, sum_u dV_u = sum_t dO_t, <Q, dQ> = <K, dK> (fixed mask)."""
+    Q, K = f64(q[0, h]), f64(k[0, h])
+    dQ, dK, dV, dO = (f64(t[0, h]) for t in (dq, dk, dv, do))
+    scale = np.abs(dK).sum(axis=0).max()
+    assert np.abs(dK.sum(axis=0)).max() <= GRAD_REL_FRO * scale, f"h{h}: sum dK"
+    assert rel_fro(dV.sum(axis=0), dO.sum(axis=0)) <= GRAD_REL_FRO, f"h{h}: sum dV"
+    a, b = (Q * dQ).sum(), (K * dK).sum()
+    assert abs(a - b) <= GRAD_REL_FRO * max(abs(a), abs(b), np.abs(Q * dQ).sum() * 1e-3), f"h{h}: <Q,dQ>"
+
+
+# ---------------------------------------------------------------------------
+# Wan2.1-1.3B-shaped layer, forward + backward
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def wan13():
+    w = W.WORKLOADS["c2"]
+    k_frac, p = W.tuned_params("c2")
+    _say(f"[wan1.3B] generating inputs H{w.H} N{w.N} d{w.d}")
+    dev, ref = device_inputs(w)
+    q, k, v, do = (dev[t] for t in ("q", "k", "v", "do"))
+    mask = sa2.build_mask(q, k, w.bq, w.bk, k_frac, p)
+    o, lse = sa2.attn_fwd(q, k, v, mask)
+    grads = sa2.attn_bwd(q, k, v, o, lse, do, mask)
+    torch.cuda.synchronize()
+    return dict(w=w, k_frac=k_frac, p=p, dev=dev, ref=ref, mask=mask, o=o, lse=lse, grads=grads)
+
+
+def test_wan13_mask_all_heads(wan13):
+    w, mask, ref = wan13["w"], wan13["mask"], wan13["ref"]
+    bm = mask.bitmap.cpu().numpy()
+    rc, ri = mask.row_cnt.cpu().numpy(), mask.row_idx.cpu().numpy()
+    cc, ci = mask.col_cnt.cpu().numpy(), mask.col_idx.cpu().numpy()
+    ties = mass = 0
+    for h in range(w.H):
+        Q, K = ref["q"][0, h], ref["k"][0, h]
+        hm = O.build_mask_head(Q, K, w.bq, w.bk, wan13["k_frac"], wan13["p"])
+        _, t_, m_ = compare_mask(hm, bm[0, h], wan13["p"])
+        ties += t_; mass += m_
+        check_lists(bm[0, h], rc[0, h], ri[0, h], cc[0, h], ci[0, h])
+    dens = mask.density()
+    _say(f"[wan1.3B] density {dens:.5f}, near-tie blocks {ties}, mass near-tie rows {mass}")
+    assert abs(dens - 0.05) <= 0.02 * 0.05 + 1e-4
+
+
+def test_wan13_attention_sampled(wan13):
+    w, ref = wan13["w"], wan13["ref"]
+    bm = wan13["mask"].bitmap.cpu().numpy()
+    rng = np.random.default_rng(0)
+    for h in range(w.H):
+        _spot_check(w, ref, h, bm[0, h], wan13["o"], wan13["lse"], wan13["grads"], rng)
+
+
+def test_wan13_gradient_invariants(wan13):
+    w, dev = wan13["w"], wan13["dev"]
+    dq, dk, dv = wan13["grads"]
+    for h in range(w.H):
+        _invariants(dev["q"], dev["k"], dq, dk, dv, dev["do"], h)
+
+
+# ---------------------------------------------------------------------------
+# 14B-720p-shaped layer
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def wan14():
+    w = W.WORKLOADS["c3"]
+    k_frac, p = W.tuned_params("c3")
+    _say(f"[wan14B] generating inputs H{w.H} N{w.N} d{w.d}")
+    dev, ref = device_inputs(w)
+    q, k, v, do = (dev[t] for t in ("q", "k", "v", "do"))
+    mask = sa2.build_mask(q, k, w.bq, w.bk, k_frac, p)
+    o, lse = sa2.attn_fwd(q, k, v, mask)
+    grads = sa2.attn_bwd(q, k, v, o, lse, do, mask)
+    torch.cuda.synchronize()
+    return dict(w=w, k_frac=k_frac, p=p, dev=dev, ref=ref, mask=mask, o=o, lse=lse, grads=grads)
+
+
+def test_wan14_mask_and_attention(wan14):
+    w, mask, ref = wan14["w"], wan14["mask"], wan14["ref"]
+    bm = mask.bitmap.cpu().numpy()
+    rc, ri = mask.row_cnt.cpu().numpy(), mask.row_idx.cpu().numpy()
+    cc, ci = mask.col_cnt.cpu().numpy(), mask.col_idx.cpu().numpy()
+    rng = np.random.default_rng(1)
+    for h in (0, w.H - 1):
+        hm = O.build_mask_head(ref["q"][0, h], ref["k"][0, h], w.bq, w.bk, wan14["k_frac"],
+                               wan14["p"])
+        compare_mask(hm, bm[0, h], wan14["p"])
+        check_lists(bm[0, h], rc[0, h], ri[0, h], cc[0, h], ci[0, h])
+        _spot_check(w, ref, h, bm[0, h], wan14["o"], wan14["lse"], wan14["grads"], rng)
+    dens = mask.density()
+    _say(f"[wan14B] density {dens:.5f}")
+    assert abs(dens - 0.05) <= 0.02 * 0.05 + 1e-4
+
+
+def test_wan14_rows_keep_the_topk_prefix(wan14):
+    """Every row of every head keeps at least kc blocks and its top-ranked block."""
+    w, mask = wan14["w"], wan14["mask"]
+    kc = O.topk_count(wan14["k_frac"], mask.Tk)
+    assert int(mask.row_cnt.min().item()) >= kc
+
+
+# ---------------------------------------------------------------------------
+# Mask-rule stress test
+# ---------------------------------------------------------------------------
+
+STRESS = [n for n in W.WORKLOADS if n.startswith("c4_")]
+
+
+@pytest.fixture(scope="module")
+def stress_inputs():
+    cache = {}
+
+    def get(regime):
+        if regime not in cache:
+            w = W.WORKLOADS[f"c4_{regime}_05"]
+            _say(f"[stress] generating {regime} inputs")
+            cache.clear()
+            cache[regime] = device_inputs(w)
+        return cache[regime]
+    return get
+
+
+@pytest.mark.parametrize("name", STRESS)
+def test_stress_union_and_oracle(name, stress_inputs):
+    w = W.WORKLOADS[name]
+    k_frac, p = W.tuned_params(name)
+    dev, ref = stress_inputs(w.gen)
+    q, k, v, do = (dev[t] for t in ("q", "k", "v", "do"))
+    _say(f"[stress] {name} k{k_frac:.5f} p{p:.5f}")
+    hy = sa2.build_mask(q, k, w.bq, w.bk, k_frac, p)
+    hy_bm = hy.bitmap.clone()
+    ko = sa2.build_mask(q, k, w.bq, w.bk, k_frac, 0.0).bitmap.clone()
+    po = sa2.build_mask(q, k, w.bq, w.bk, 0.0, p).bitmap.clone()
+    torch.cuda.synchronize()
+    assert torch.all(hy_bm >= ko) and torch.all(hy_bm >= po)
+    assert torch.equal(hy_bm, torch.maximum(ko, po))
+    o, lse = sa2.attn_fwd(q, k, v, hy)
+    grads = sa2.attn_bwd(q, k, v, o, lse, do, hy)
+    torch.cuda.synchronize()
+    bm = hy_bm.cpu().numpy()
+    hm = O.build_mask_head(ref["q"][0, 0], ref["k"][0, 0], w.bq, w.bk, k_frac, p)
+    compare_mask(hm, bm[0, 0], p)
+    _spot_check(w, ref, 0, bm[0, 0], o, lse, grads, np.random.default_rng(2))
+    dens = hy.density()
+    want = W.tuned_record(name)["density"]
+    _say(f"[stress] {name} density {dens:.5f} (oracle {want:.5f}, target {w.target_density})")
+    assert abs(dens - want) <= 1e-3 * want

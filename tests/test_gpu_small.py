@@ -1,0 +1,179 @@
+"""GPU parity on small shapes: every output element against the fp64 oracle.
+
+Covers the tiny CPU-checkable workload (B=1, H=2, N=1024, d=64, 64x64 blocks,
+k = 2 blocks, p = 0.9; plus its two variants that make Top-k, and both rules,
+active), ragged shapes spanning several tiles in both block geometries and
+both element types, and the degenerate cases: one partial block, dense masks
+(k = 100% or p = 1), a single rule, and reproducibility.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_sa2_amd as sa2
+import oracle as O
+import workloads as W
+
+from parity import (check_forward, check_grad, check_lists, compare_mask, device_inputs, f64)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _bf16(a: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(a).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def run_case(w: W.Workload, k_frac: float, p: float, backward: bool = True,
+             attn_on_bf16_operands: bool = False):
+    """Mask from the inputs as given; attention against the oracle.
+
+    attn_on_bf16_operands: the attention multiplies bf16-rounded operands by
+    contract; set it for fp32 inputs whose logits are so large that the input
+    rounding alone exceeds the tolerance, so that the oracle sees the same
+    operands (the mask is still compared on the unrounded inputs), and the O
+    tolerance then scales with max|O| (see parity.check_forward).
+    """
+    _say(f"[case] {w.name} B{w.B} H{w.H} N{w.N} d{w.d} bq{w.bq} bk{w.bk} {w.dtype} k{k_frac} p{p}")
+    dev, ref = device_inputs(w) if w.B == 1 else _multi_batch(w)
+    q, k, v = dev["q"], dev["k"], dev["v"]
+    mask = sa2.build_mask(q, k, w.bq, w.bk, k_frac, p)
+    o, lse = sa2.attn_fwd(q, k, v, mask)
+    if backward:
+        dq, dk, dv = sa2.attn_bwd(q, k, v, o, lse, dev["do"], mask)
+    torch.cuda.synchronize()
+    bm = mask.bitmap.cpu().numpy()
+    rc, ri = mask.row_cnt.cpu().numpy(), mask.row_idx.cpu().numpy()
+    cc, ci = mask.col_cnt.cpu().numpy(), mask.col_idx.cpu().numpy()
+    stats = []
+    for b in range(w.B):
+        for h in range(w.H):
+            Q, K, V = (ref[t][b, h] for t in ("q", "k", "v"))
+            hm = O.build_mask_head(Q, K, w.bq, w.bk, k_frac, p)
+            compare_mask(hm, bm[b, h], p)
+            check_lists(bm[b, h], rc[b, h], ri[b, h], cc[b, h], ci[b, h])
+            if attn_on_bf16_operands:
+                Q, K, V = _bf16(Q), _bf16(K), _bf16(V)
+            Oo, L, P = O.attention_dense(Q, K, V, bm[b, h], w.bq, w.bk)
+            stats.append(check_forward(f64(o[b, h]), f64(lse[b, h]), Oo, L, f"{w.name} b{b}h{h}",
+                                       scale_with_output=attn_on_bf16_operands))
+            if backward:
+                rq, rk, rv = O.attention_dense_bwd(Q, K, V, ref["do"][b, h], P)
+                for name, mine, want in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+                    check_grad(f64(mine[b, h]), want, f"{w.name} b{b}h{h} {name}")
+    return mask, stats
+
+
+def _multi_batch(w):
+    """B > 1: batch entries drawn as independent heads of a one-batch workload."""
+    from dataclasses import replace
+    w1 = replace(w, B=1, H=w.B * w.H)
+    dev, ref = device_inputs(w1)
+    shape = lambda t: t.reshape(w.B, w.H, w.N, w.d)
+    return ({k_: shape(t).contiguous() for k_, t in dev.items()},
+            {k_: a.reshape(w.B, w.H, w.N, w.d) for k_, a in ref.items()})
+
+
+def test_tiny_workload():
+    w = W.WORKLOADS["c0"]
+    mask, _ = run_case(w, *W.tuned_params("c0"))
+    assert np.all(mask.row_cnt.cpu().numpy() >= 2)
+
+
+def test_tiny_workload_topk_active():
+    # shared Q/K signal at amplitude 2: logits near 150, see run_case
+    w = W.WORKLOADS["c0b"]
+    mask, _ = run_case(w, *W.tuned_params("c0b"), attn_on_bf16_operands=True)
+    assert (mask.row_cnt.cpu().numpy() == 2).mean() > 0.5     # Top-k decides most rows
+
+
+def test_tiny_workload_both_rules_active():
+    w = W.WORKLOADS["c0c"]
+    run_case(w, *W.tuned_params("c0c"))
+
+
+SMALL = [
+    W.Workload("r128_bf16", 1, 2, 1000, 128, 128, 64, "normal", 11, "bf16", 0.1, 0.5),
+    W.Workload("r64_f32", 1, 2, 777, 64, 64, 64, "normal", 12, "f32", 0.1, 0.6),
+    W.Workload("r128_f32", 1, 1, 1111, 128, 128, 64, "normal", 13, "f32", 0.05, 0.7),
+    W.Workload("r64_bf16_d128", 1, 2, 900, 128, 64, 64, "normal", 14, "bf16", 0.2, 0.3),
+    W.Workload("r128_bf16_d64", 1, 1, 1300, 64, 128, 64, "normal", 15, "bf16", 0.08, 0.8),
+    W.Workload("smooth_4k", 1, 1, 4096, 128, 128, 64, "smooth", 16, "bf16", 0.05, 0.5,
+               grid=(4, 32, 32)),
+    W.Workload("batch2", 2, 2, 640, 64, 64, 64, "normal", 17, "bf16", 0.2, 0.5),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
+def test_ragged_shapes(w):
+    run_case(w, w.k_frac, w.p)
+
+
+def test_single_partial_block():
+    w = W.Workload("n50", 1, 2, 50, 64, 64, 64, "normal", 20, "bf16", 0.5, 0.5)
+    mask, _ = run_case(w, 0.5, 0.5)
+    assert mask.Tq == 1 and mask.Tk == 1
+
+
+@pytest.mark.parametrize("k_frac,p", [(1.0, 0.0), (0.0, 1.0), (0.3, 1.0)])
+def test_dense_masks(k_frac, p):
+    w = W.Workload("dense", 1, 1, 700, 64, 64, 64, "normal", 21, "bf16", k_frac, p)
+    mask, _ = run_case(w, k_frac, p)
+    assert mask.bitmap.all()
+
+
+@pytest.mark.parametrize("k_frac,p", [(0.1, 0.0), (0.0, 0.4)])
+def test_single_rule(k_frac, p):
+    w = W.Workload("one_rule", 1, 2, 1024, 64, 64, 64, "normal", 22, "bf16", k_frac, p)
+    run_case(w, k_frac, p)
+
+
+def test_both_rules_off_is_an_error():
+    q = torch.zeros(1, 1, 128, 64, device="cuda", dtype=torch.bfloat16)
+    with pytest.raises(RuntimeError, match="SA2_EINVAL"):
+        sa2.build_mask(q, q, 64, 64, 0.0, 0.0)
+
+
+def test_reproducible_and_fully_written():
+    """Two runs agree bit for bit; outputs pre-filled with NaN are fully overwritten."""
+    w = W.Workload("repro", 1, 2, 1500, 128, 128, 64, "normal", 23, "bf16", 0.1, 0.5)
+    dev, _ = device_inputs(w)
+    q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
+    outs = []
+    for _ in range(2):
+        mask = sa2.build_mask(q, k, w.bq, w.bk, w.k_frac, w.p)
+        o = torch.full_like(q, float("nan"))
+        lse = torch.full(q.shape[:3], float("nan"), device=q.device)
+        sa2.attn_fwd(q, k, v, mask, o=o, lse=lse)
+        grads = [torch.full_like(q, float("nan")) for _ in range(3)]
+        sa2.attn_bwd(q, k, v, o, lse, do, mask, *grads)
+        torch.cuda.synchronize()
+        for t in (o, lse, *grads):
+            assert torch.isfinite(t).all()
+        outs.append([mask.bitmap.clone(), o, lse, *grads])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+def test_autograd_wrapper():
+    w = W.Workload("autograd", 1, 1, 512, 64, 64, 64, "normal", 24, "bf16", 0.25, 0.5)
+    dev, ref = device_inputs(w)
+    q, k, v = (dev[t].clone().requires_grad_() for t in ("q", "k", "v"))
+    mask = sa2.build_mask(q.detach(), k.detach(), 64, 64, 0.25, 0.5)
+    out = sa2.sparse_attention(q, k, v, mask)
+    out.backward(dev["do"])
+    torch.cuda.synchronize()
+    bm = mask.bitmap.cpu().numpy()[0, 0]
+    Q, K, V, dO = (ref[t][0, 0] for t in ("q", "k", "v", "do"))
+    _, _, P = O.attention_dense(Q, K, V, bm, 64, 64)
+    for g, want, name in zip((q.grad, k.grad, v.grad), O.attention_dense_bwd(Q, K, V, dO, P),
+                             ("dq", "dk", "dv")):
+        check_grad(f64(g[0, 0]), want, name)

@@ -344,3 +344,21 @@ def test_backward_invariants():
     assert np.abs(dK.sum(axis=0)).max() < 1e-12          # softmax shift invariance
     assert np.abs(dV.sum(axis=0) - dO.sum(axis=0)).max() < 1e-12   # rows of P sum to 1
     assert abs((Q * dQ).sum() - (K * dK).sum()) < 1e-10
+
+
+def test_per_block_functions_match_the_whole_head():
+    N, d, bq, bk = 300, 16, 64, 32     # ragged on both axes
+    Q, K, V, dO = (_rand((N, d), s) for s in (50, 51, 52, 53))
+    hm = O.build_mask_head(Q, K, bq, bk, 0.15, 0.5)
+    rows = hm.row_lists()
+    Oo, lse, P = O.attention_dense(Q, K, V, hm.bitmap, bq, bk)
+    dQ, dK, dV = O.attention_dense_bwd(Q, K, V, dO, P)
+    for i in range(hm.S.shape[0]):
+        lo, hi = O.block_range(i, bq, N)
+        o_i, l_i = O.forward_query_block(Q, K, V, rows, bq, bk, i)
+        assert np.abs(o_i - Oo[lo:hi]).max() < 1e-13 and np.abs(l_i - lse[lo:hi]).max() < 1e-13
+        assert np.abs(O.dq_query_block(Q, K, V, dO, rows, bq, bk, i) - dQ[lo:hi]).max() < 1e-12
+    for j in range(hm.S.shape[1]):
+        lo, hi = O.block_range(j, bk, N)
+        k_j, v_j = O.dkdv_key_block(Q, K, V, dO, rows, bq, bk, j)
+        assert np.abs(k_j - dK[lo:hi]).max() < 1e-12 and np.abs(v_j - dV[lo:hi]).max() < 1e-12

@@ -134,18 +134,27 @@ def smooth_signal(grid, d: int, rng: np.random.Generator, amplitude: float = 0.5
     b = 2.0 * np.pi * (f[:, 1, None, :] * yx_y[None] + f[:, 2, None, :] * yx_x[None])  # [W, YX, d]
     left = amplitude * np.concatenate([np.sin(a), np.cos(a)], axis=0)      # [2W, T, d]
     right = np.concatenate([np.cos(b), np.sin(b)], axis=0)                  # [2W, YX, d]
-    s = np.matmul(left.transpose(2, 1, 0), right.transpose(2, 0, 1))       # [d, T, YX]
-    return s.reshape(d, T * Y * X)
+    import torch
+    s = torch.bmm(torch.from_numpy(np.ascontiguousarray(left.transpose(2, 1, 0))),
+                  torch.from_numpy(np.ascontiguousarray(right.transpose(2, 0, 1)))).numpy()
+    return s.reshape(d, T * Y * X)                                          # [d, T*YX]
 
 
-def _head(w: Workload, tensor: str, head: int) -> np.ndarray:
-    """One head of one tensor, float32 [N, d], before any cross-head edit."""
+def _head(w: Workload, tensor: str, head: int, out: np.ndarray | None = None) -> np.ndarray:
+    """One head of one tensor, float32 [N, d], before any cross-head edit.
+
+    Written into ``out`` (a float32 [N, d] array) when given.
+    """
     rng = _rng(w.seed, tensor, head)
     N, d = w.N, w.d
+    if out is None:
+        out = np.empty((N, d), dtype=np.float32)
     if w.gen == "normal" or tensor == "do" or (w.gen == "uniform" and tensor == "v"):
-        return rng.standard_normal((N, d)).astype(np.float32)
+        out[...] = rng.standard_normal((N, d))
+        return out
     if w.gen == "uniform":
-        return (0.05 * rng.standard_normal((N, d))).astype(np.float32)
+        out[...] = 0.05 * rng.standard_normal((N, d))
+        return out
     # smooth / sink: smooth signal plus 0.5 N(0,1) noise, built channel-major
     if w.shared_signal and tensor in ("q", "k"):
         sig = smooth_signal(w.grid, d, _rng(w.seed, "q", head), w.amplitude)
@@ -157,28 +166,23 @@ def _head(w: Workload, tensor: str, head: int) -> np.ndarray:
         # block really dominates its rows (drawn from its own stream)
         u = 0.5 * _rng(w.seed + 1000, "q", head).standard_normal(d)
         sig += u[:, None]
-    return _transpose_f32(sig)
-
-
-def _transpose_f32(x: np.ndarray) -> np.ndarray:
-    """[d, N] float64 -> contiguous [N, d] float32 (a blocked copy)."""
-    d, N = x.shape
-    out = np.empty((N, d), dtype=np.float32)
     step = 4096
-    for lo in range(0, N, step):
-        out[lo:lo + step] = x[:, lo:lo + step].T
+    for lo in range(0, N, step):                 # blocked [d, N] -> [N, d]
+        out[lo:lo + step] = sig[:, lo:lo + step].T
     return out
 
 
-def head_inputs(w: Workload, head: int, tensors=TENSORS) -> dict[str, np.ndarray]:
-    """All requested tensors of one head, float32 [N, d] (B = 1)."""
-    out = {t: _head(w, t, head) for t in tensors}
-    if w.gen == "sink" and "k" in out:
-        q = out["q"] if "q" in out else _head(w, "q", head)
+def head_inputs(w: Workload, head: int, tensors=TENSORS, out=None) -> dict[str, np.ndarray]:
+    """All requested tensors of one head, float32 [N, d] (B = 1).
+
+    ``out`` optionally maps tensor names to float32 [N, d] destinations.
+    """
+    res = {t: _head(w, t, head, None if out is None else out[t]) for t in tensors}
+    if w.gen == "sink" and "k" in res:
+        q = res["q"] if "q" in res else _head(w, "q", head)
         # attention sink: key tokens 0..63 (key block 0) += 6 * mean over tokens of Q
-        out["k"] = out["k"].copy()
-        out["k"][:64] += (6.0 * q.astype(np.float64).mean(axis=0)).astype(np.float32)
-    return out
+        res["k"][:64] += (6.0 * q.astype(np.float64).mean(axis=0)).astype(np.float32)
+    return res
 
 
 def make_inputs(w: Workload, heads=None, tensors=TENSORS) -> dict[str, np.ndarray]:
@@ -191,9 +195,19 @@ def make_inputs(w: Workload, heads=None, tensors=TENSORS) -> dict[str, np.ndarra
         raise ValueError("workloads here have B = 1")
     heads = list(range(w.H)) if heads is None else list(heads)
     tensors = tuple(t for t in TENSORS if t in tensors and (t != "do" or w.backward))
-    with _cf.ThreadPoolExecutor(_threads()) as ex:
-        per_head = list(ex.map(lambda h: head_inputs(w, h, tensors), heads))
-    return {t: np.stack([ph[t] for ph in per_head])[None] for t in tensors}
+    out = {t: np.empty((1, len(heads), w.N, w.d), dtype=np.float32) for t in tensors}
+    import torch
+    from threadpoolctl import threadpool_limits
+    nthreads = torch.get_num_threads()
+    torch.set_num_threads(1)          # parallel over heads instead
+    try:
+        with threadpool_limits(1), _cf.ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(lambda ih: head_inputs(w, ih[1], tensors,
+                                               {t: out[t][0, ih[0]] for t in tensors}),
+                        enumerate(heads)))
+    finally:
+        torch.set_num_threads(nthreads)
+    return out
 
 
 def to_device_dtype(arr: np.ndarray, dtype: str):
@@ -211,6 +225,11 @@ def tuned_params(name: str) -> tuple[float, float]:
     table = json.loads(TUNED_PARAMS_PATH.read_text())
     rec = table["workloads"][name]
     return float(rec["k_frac"]), float(rec["p"])
+
+
+def tuned_record(name: str) -> dict:
+    """The stored tuning record of a density-tuned workload (k_frac, p, density, ...)."""
+    return json.loads(TUNED_PARAMS_PATH.read_text())["workloads"][name]
 
 
 def with_heads(w: Workload, H: int) -> Workload:
