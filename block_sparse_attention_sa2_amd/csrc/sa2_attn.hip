@@ -79,7 +79,7 @@ __device__ inline bf16x8 pack8(const f32x16& a, int e0) {
 // Forward
 // ---------------------------------------------------------------------------
 template <typename T, int D, int NW>
-__global__ __launch_bounds__(NW * 64)
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                 const int32_t* __restrict__ row_cnt, const int32_t* __restrict__ row_idx, int N,
                 int Tq, int Tk, float scale_log2, T* __restrict__ o, float* __restrict__ lse) {
@@ -291,43 +291,44 @@ void dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
         dp[kb] = mfma32(df[kk], lds_read8(v_lds + (32 * kb + l32) * KS + 16 * kk + 8 * h), dp[kb]);
       }
     }
+    // the slice's Q and dO fragments are dead now: their registers take the
+    // next slice's loads, which complete behind the rest of this iteration
+    __builtin_amdgcn_sched_barrier(0);
     const int cn = c + 4;
     if (cn < total) fetch(cn);
-    // P = exp(S/sqrt(d) - LSE), dS = P * (dP - Delta); rows 8g+4h+i of the slice
-    f32x4 L[4], Dl[4];
+    __builtin_amdgcn_sched_barrier(0);
+    // P = exp(S/sqrt(d) - LSE), dS = P * (dP - Delta) for rows 8g+4h+i of the
+    // slice, packed to bf16 B operands at once: pb[kb][t] / sb[kb][t] hold
+    // accumulator elements 8t .. 8t+7 (rows 16t .. 16t+15 in slot order)
+    bf16x8 pb[2][2], sb[2][2];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      L[g] = *reinterpret_cast<const f32x4*>(my_lse + 8 * g + 4 * h);
-      Dl[g] = *reinterpret_cast<const f32x4*>(my_dl + 8 * g + 4 * h);
-    }
+      const f32x4 L = *reinterpret_cast<const f32x4*>(my_lse + 8 * g + 4 * h);
+      const f32x4 Dl = *reinterpret_cast<const f32x4*>(my_dl + 8 * g + 4 * h);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const bool kval = !ktail || key0 + 32 * kb + l32 < N;
+      for (int kb = 0; kb < 2; ++kb) {
+        const bool kval = !ktail || key0 + 32 * kb + l32 < N;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float pv = __builtin_amdgcn_exp2f(s[kb][e] * scale_log2 - L[e >> 2][e & 3]);
-        pv = kval ? pv : 0.f;
-        s[kb][e] = pv;
-        dp[kb][e] = pv * (dp[kb][e] - Dl[e >> 2][e & 3]);
+        for (int i = 0; i < 4; ++i) {
+          const int e = 4 * g + i;
+          float pv = __builtin_amdgcn_exp2f(s[kb][e] * scale_log2 - L[i]);
+          pv = kval ? pv : 0.f;
+          pb[kb][g >> 1][4 * (g & 1) + i] = (__bf16)pv;
+          sb[kb][g >> 1][4 * (g & 1) + i] = (__bf16)(pv * (dp[kb][e] - Dl[i]));
+        }
       }
     }
     // dV^T += dO^T P and dK^T += Q^T dS over the slice's 32 rows
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      bf16x8 pb[2], sb[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        pb[kb] = pack8(s[kb], 8 * t);
-        sb[kb] = pack8(dp[kb], 8 * t);
-      }
 #pragma unroll
       for (int db = 0; db < ND; ++db) {
         const bf16x8 ao = tr_operand<CS>(my_do, 16 * t, 32 * db, lane);
         const bf16x8 aq = tr_operand<CS>(my_q, 16 * t, 32 * db, lane);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          accv[db][kb] = mfma32(ao, pb[kb], accv[db][kb]);
-          acck[db][kb] = mfma32(aq, sb[kb], acck[db][kb]);
+          accv[db][kb] = mfma32(ao, pb[kb][t], accv[db][kb]);
+          acck[db][kb] = mfma32(aq, sb[kb][t], acck[db][kb]);
         }
       }
     }
@@ -372,7 +373,7 @@ void dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
 // Backward dQ: one workgroup per query block, walking its row list.
 // ---------------------------------------------------------------------------
 template <typename T, int D, int NW>
-__global__ __launch_bounds__(NW * 64)
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void dq_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                const T* __restrict__ o, const T* __restrict__ dout, const float* __restrict__ lse,
                float* __restrict__ delta, const int32_t* __restrict__ row_cnt,
