@@ -190,9 +190,18 @@ void fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
 
 // ---------------------------------------------------------------------------
 // Backward dK, dV: one workgroup (4 waves) per key block of 64 keys.
+//
+// Waves form two pairs.  Pair p walks the 32-row slices 2j + p of every
+// query block in the key block's column list; in a pair, wave kb accumulates
+// dK and dV of keys key0 + 32kb .. +31 over all of d (the two pairs' partial
+// sums are added at the end).  The two waves of a pair stage a slice
+// together (wave 0 loads Q, wave 1 loads dO; each keeps its own half as MFMA
+// A operands and reads the other half from LDS).  Both pairs step in lock
+// step: one workgroup barrier after staging, one before the slice buffers
+// are overwritten.
 // ---------------------------------------------------------------------------
 template <typename T, int D, int BQ>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                  const T* __restrict__ dout, const float* __restrict__ lse,
                  const float* __restrict__ delta, const int32_t* __restrict__ col_cnt,
@@ -200,27 +209,28 @@ void dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
                  float scale, T* __restrict__ dk, T* __restrict__ dv) {
   constexpr int NT = 256;
   constexpr int KS = D + 8;   // K, V tiles: 16-byte fragment reads
-  constexpr int CS = D + 16;  // per-wave Q / dO slices: transposed reads
+  constexpr int CS = D + 16;  // Q / dO slices: fragment and transposed reads
   constexpr int NK = D / 16, ND = D / 32;
   constexpr int CPT = 64 * (D / 8) / NT;
-  constexpr int SUB = BQ / 32;  // 32-row slices per query block
-  constexpr int RS = D + 4;     // fp32 reduction tile stride
-  constexpr int SLICE_BYTES = 2 * 4 * 32 * CS * 2;
-  static_assert(SLICE_BYTES >= 64 * RS * 4, "reduction tile must fit in the slice area");
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[64 * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[64 * KS];
-  __shared__ __attribute__((aligned(16))) unsigned char slice_mem[SLICE_BYTES];
-  __shared__ __attribute__((aligned(16))) float stat_lds[4][2][32];
+  constexpr int SUB = BQ / 32;   // 32-row slices per query block
+  constexpr int SPP = SUB / 2;   // slices per pair per query block
+  constexpr int RS = D + 4;      // fp32 staging of a wave's output tile
+  constexpr int TILE_BYTES = 2 * 64 * KS * 2;
+  constexpr int SLICE_BYTES = 2 * 2 * 32 * CS * 2;
+  static_assert(TILE_BYTES + SLICE_BYTES >= 2 * 2 * 32 * RS * 4, "output staging must fit");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[TILE_BYTES + SLICE_BYTES];
+  __shared__ __attribute__((aligned(16))) float st[2][2][32];  // [pair][lse2 | Delta][row]
 
-  uint16_t* q_lds = reinterpret_cast<uint16_t*>(slice_mem);  // [4][32*CS]
-  uint16_t* do_lds = q_lds + 4 * 32 * CS;                    // [4][32*CS]
-  float* red = reinterpret_cast<float*>(slice_mem);          // [64][RS] after the loop
+  uint16_t* k_lds = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* v_lds = k_lds + 64 * KS;
+  uint16_t* slices = v_lds + 64 * KS;                          // [pair][Q | dO][32*CS]
 
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = wg / Tk, kj = wg % Tk;
   const int key0 = kj * 64;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
+  const int pair = w >> 1, kb = w & 1;
   const size_t base = (size_t)bh * N * D;
 
   {
@@ -230,140 +240,139 @@ void dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
     fetch_tile<T, D, NT>(v + base, key0, N, tid, r);
     put_tile<D, NT, KS>(v_lds, tid, r);
   }
+  // the tiles are complete before any wave reads them, and before the output
+  // staging (which reuses this memory) of a key block with an empty list
   __syncthreads();
 
-  uint16_t* my_q = q_lds + w * 32 * CS;
-  uint16_t* my_do = do_lds + w * 32 * CS;
-  float* my_lse = stat_lds[w][0];
-  float* my_dl = stat_lds[w][1];
+  uint16_t* sq = slices + (2 * pair) * 32 * CS;   // this pair's Q slice
+  uint16_t* sd = sq + 32 * CS;                     // this pair's dO slice
+  uint16_t* mine = kb == 0 ? sq : sd;              // the half this wave stages
+  const T* src = kb == 0 ? q : dout;
+  const float* ssrc = kb == 0 ? lse : delta;
+  const bool kval = key0 + 32 * kb + l32 < N;      // this lane's key exists
+  const uint16_t* kf_row = k_lds + (32 * kb + l32) * KS + 8 * h;
+  const uint16_t* vf_row = v_lds + (32 * kb + l32) * KS + 8 * h;
 
-  f32x16 accv[ND][2], acck[ND][2];
+  f32x16 accv[ND], acck[ND];
 #pragma unroll
-  for (int db = 0; db < ND; ++db)
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      accv[db][kb] = zero16();
-      acck[db][kb] = zero16();
-    }
+  for (int db = 0; db < ND; ++db) {
+    accv[db] = zero16();
+    acck[db] = zero16();
+  }
 
   const int cnt = col_cnt[wg];
   const int32_t* lst = col_idx + (size_t)wg * Tq;
-  const int total = cnt * SUB;
-  const bool ktail = key0 + 64 > N;
+  const int steps = cnt * SPP;
 
-  bf16x8 qf[NK], df[NK];
+  // own[kk]: row l32 of this wave's half of the slice, d = 16kk + 8h .. +7
+  bf16x8 own[NK];
   float stat = 0.f;
-  auto fetch = [&](int c) {
-    const int q0 = lst[c / SUB] * BQ + (c % SUB) * 32;
-    const int row = q0 + l32;
+  auto fetch = [&](int s) {
+    const int row = lst[s / SPP] * BQ + 32 * (2 * (s % SPP) + pair) + l32;
     const bool ok = row < N;
-    const size_t off = base + (size_t)row * D + 8 * h;
+    const T* p = src + base + (size_t)row * D + 8 * h;
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-      qf[kk] = ok ? load8(q + off + 16 * kk) : zero8();
-      df[kk] = ok ? load8(dout + off + 16 * kk) : zero8();
-    }
-    // lanes 0-31 carry log2-scaled LSE (+inf for padding rows: P = 0),
-    // lanes 32-63 carry Delta
-    const size_t srow = (size_t)bh * N + row;
-    stat = h == 0 ? (ok ? lse[srow] * kLog2e : INFINITY) : (ok ? delta[srow] : 0.f);
+    for (int kk = 0; kk < NK; ++kk) own[kk] = ok ? load8(p + 16 * kk) : zero8();
+    // wave 0: log2-scaled LSE (+inf on padding rows: P = 0); wave 1: Delta
+    const float x = ok ? ssrc[(size_t)bh * N + row] : 0.f;
+    stat = kb == 0 ? (ok ? x * kLog2e : INFINITY) : x;
   };
 
-  int c = w;
-  if (c < total) fetch(c);
-  while (c < total) {
+  if (steps > 0) fetch(0);
+  for (int s = 0; s < steps; ++s) {
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-      *reinterpret_cast<bf16x8*>(my_q + l32 * CS + 16 * kk + 8 * h) = qf[kk];
-      *reinterpret_cast<bf16x8*>(my_do + l32 * CS + 16 * kk + 8 * h) = df[kk];
-    }
-    stat_lds[w][h][l32] = stat;
-    wave_lds_sync();
-    // S = Q K^T and dP = dO V^T for this slice's 32 rows and the 64 keys
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = zero16();
-      dp[kb] = zero16();
+    for (int kk = 0; kk < NK; ++kk)
+      *reinterpret_cast<bf16x8*>(mine + l32 * CS + 16 * kk + 8 * h) = own[kk];
+    if (h == 0) st[pair][kb][l32] = stat;
+    __syncthreads();
+    // S = Q K^T and dP = dO V^T: the slice's 32 rows against this wave's 32 keys
+    f32x16 sa = zero16(), dpa = zero16();
+    if (kb == 0) {
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
-        s[kb] = mfma32(qf[kk], lds_read8(k_lds + (32 * kb + l32) * KS + 16 * kk + 8 * h), s[kb]);
-        dp[kb] = mfma32(df[kk], lds_read8(v_lds + (32 * kb + l32) * KS + 16 * kk + 8 * h), dp[kb]);
+        sa = mfma32(own[kk], lds_read8(kf_row + 16 * kk), sa);
+        dpa = mfma32(lds_read8(sd + l32 * CS + 16 * kk + 8 * h), lds_read8(vf_row + 16 * kk), dpa);
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        sa = mfma32(lds_read8(sq + l32 * CS + 16 * kk + 8 * h), lds_read8(kf_row + 16 * kk), sa);
+        dpa = mfma32(own[kk], lds_read8(vf_row + 16 * kk), dpa);
       }
     }
-    // the slice's Q and dO fragments are dead now: their registers take the
-    // next slice's loads, which complete behind the rest of this iteration
     __builtin_amdgcn_sched_barrier(0);
-    const int cn = c + 4;
-    if (cn < total) fetch(cn);
+    if (s + 1 < steps) fetch(s + 1);
     __builtin_amdgcn_sched_barrier(0);
-    // P = exp(S/sqrt(d) - LSE), dS = P * (dP - Delta) for rows 8g+4h+i of the
-    // slice, packed to bf16 B operands at once: pb[kb][t] / sb[kb][t] hold
-    // accumulator elements 8t .. 8t+7 (rows 16t .. 16t+15 in slot order)
-    bf16x8 pb[2][2], sb[2][2];
+    // P = exp(S/sqrt(d) - LSE) and dS = P * (dP - Delta) for rows 8g+4h+i,
+    // packed at once into the B operands of the two 16-row steps
+    bf16x8 pb[2], sb[2];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const f32x4 L = *reinterpret_cast<const f32x4*>(my_lse + 8 * g + 4 * h);
-      const f32x4 Dl = *reinterpret_cast<const f32x4*>(my_dl + 8 * g + 4 * h);
+      const f32x4 L = *reinterpret_cast<const f32x4*>(&st[pair][0][8 * g + 4 * h]);
+      const f32x4 Dl = *reinterpret_cast<const f32x4*>(&st[pair][1][8 * g + 4 * h]);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bool kval = !ktail || key0 + 32 * kb + l32 < N;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int e = 4 * g + i;
-          float pv = __builtin_amdgcn_exp2f(s[kb][e] * scale_log2 - L[i]);
-          pv = kval ? pv : 0.f;
-          pb[kb][g >> 1][4 * (g & 1) + i] = (__bf16)pv;
-          sb[kb][g >> 1][4 * (g & 1) + i] = (__bf16)(pv * (dp[kb][e] - Dl[i]));
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int e = 4 * g + i;
+        float pv = __builtin_amdgcn_exp2f(sa[e] * scale_log2 - L[i]);
+        pv = kval ? pv : 0.f;
+        pb[g >> 1][4 * (g & 1) + i] = (__bf16)pv;
+        sb[g >> 1][4 * (g & 1) + i] = (__bf16)(pv * (dpa[e] - Dl[i]));
       }
     }
-    // dV^T += dO^T P and dK^T += Q^T dS over the slice's 32 rows
+    // dV^T += dO^T P and dK^T += Q^T dS over the slice's rows
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int db = 0; db < ND; ++db) {
-        const bf16x8 ao = tr_operand<CS>(my_do, 16 * t, 32 * db, lane);
-        const bf16x8 aq = tr_operand<CS>(my_q, 16 * t, 32 * db, lane);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          accv[db][kb] = mfma32(ao, pb[kb][t], accv[db][kb]);
-          acck[db][kb] = mfma32(aq, sb[kb][t], acck[db][kb]);
-        }
+        accv[db] = mfma32(tr_operand<CS>(sd, 16 * t, 32 * db, lane), pb[t], accv[db]);
+        acck[db] = mfma32(tr_operand<CS>(sq, 16 * t, 32 * db, lane), sb[t], acck[db]);
       }
-    }
-    c = cn;
+    __syncthreads();
   }
 
-  // Sum the four waves' tiles in LDS (wave order 0..3), then store.
-  // Accumulator element e of (db, kb) is row d = 32db + 8(e/4) + 4h + e%4,
-  // column key = 32kb + l32 of the transposed tile.
-  for (int which = 0; which < 2; ++which) {
-    __syncthreads();
-    for (int ww = 0; ww < 4; ++ww) {
-      if (w == ww) {
+  // The two waves of a key half (one per pair) hold partial sums over
+  // different slices.  Pair 1 hands its tiles to pair 0 through LDS; pair 0
+  // adds them (always in this order) and stores.  Accumulator element e of
+  // block db is d = 32db + 8(e/4) + 4h + e%4 at key 32kb + l32; the sum goes
+  // back to LDS so that the stores are whole 4-element runs of a key's row.
+  float* tile[2];
 #pragma unroll
-        for (int db = 0; db < ND; ++db)
+  for (int which = 0; which < 2; ++which)
+    tile[which] = reinterpret_cast<float*>(smem) + (kb * 2 + which) * 32 * RS;
+  if (pair == 1) {
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
+    for (int which = 0; which < 2; ++which)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-              const int dd = 32 * db + 8 * (e >> 2) + 4 * h + (e & 3);
-              float* p = red + (32 * kb + l32) * RS + dd;
-              const float val = which == 0 ? accv[db][kb][e] : acck[db][kb][e];
-              *p = (ww == 0) ? val : *p + val;
-            }
-      }
-      __syncthreads();
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          tile[which][l32 * RS + 32 * db + 8 * (e >> 2) + 4 * h + (e & 3)] =
+              which == 0 ? accv[db][e] : acck[db][e];
+  }
+  __syncthreads();
+  if (pair == 0) {
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+      const float mul = which == 0 ? 1.f : scale;
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          float* p = tile[which] + l32 * RS + 32 * db + 8 * (e >> 2) + 4 * h + (e & 3);
+          *p = ((which == 0 ? accv[db][e] : acck[db][e]) + *p) * mul;
+        }
     }
-    T* out = (which == 0 ? dv : dk) + base;
-    const float mul = which == 0 ? 1.f : scale;
-    for (int ch = tid; ch < 64 * D / 4; ch += NT) {
-      const int row = ch / (D / 4), c4 = (ch % (D / 4)) * 4;
-      const int key = key0 + row;
-      if (key < N) {
-        const float* p = red + row * RS + c4;
-        store4(out + (size_t)key * D + c4, p[0] * mul, p[1] * mul, p[2] * mul, p[3] * mul);
+    wave_lds_sync();
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+      T* out = (which == 0 ? dv : dk) + base;
+      for (int ch = lane; ch < 32 * D / 4; ch += 64) {
+        const int r = ch / (D / 4), c4 = (ch % (D / 4)) * 4;
+        const int key = key0 + 32 * kb + r;
+        if (key < N) {
+          const float* p = tile[which] + r * RS + c4;
+          store4(out + (size_t)key * D + c4, p[0], p[1], p[2], p[3]);
+        }
       }
     }
   }
