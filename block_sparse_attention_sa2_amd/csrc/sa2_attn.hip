@@ -27,6 +27,38 @@
 
 namespace sa2 {
 
+// LDS layouts of a 64-row tile of bf16 rows of D elements, chosen by how the
+// tile is read (a wave64 LDS access is served 16 lanes or 32 lanes at a time):
+//   kRows  16-byte MFMA fragments, 16 lanes reading one 16-byte unit of 16
+//          consecutive rows: rows padded by 8 elements (a stride of 4 mod 64
+//          banks), so the 16 units land on distinct banks;
+//   kCols  transposed reads, 32 lanes reading 4 consecutive rows x 64 bytes:
+//          rows padded by 32 elements (a stride of 16 mod 64 banks);
+//   kBoth  read both ways: for D = 128 unpadded rows, with unit u of row r
+//          stored at unit u ^ (4(r % 4) + (r / 4) % 4), which is conflict-free
+//          for both patterns; for other D, padded by 16 elements;
+//   kPad16 read both ways, rows padded by 16 elements (2-way conflicts on
+//          both patterns, but no address registers).
+// Padded layouts keep every per-step address a compile-time offset from one
+// per-lane base; the permuted one costs a few address registers, which the
+// dQ kernel cannot spare.
+enum Layout { kRows = 0, kCols = 1, kBoth = 2, kPad16 = 3 };
+
+template <int D, int L>
+struct Tile {
+  static constexpr bool kSwizzled = L == kBoth && D == 128;
+  static constexpr int kRowElems =
+      L == kRows ? D + 8 : L == kCols ? D + 32 : kSwizzled ? D : D + 16;
+  __device__ static inline int off(int r, int col) {
+    if constexpr (kSwizzled) {
+      const int sw = ((r & 3) << 2) | ((r >> 2) & 3);
+      return r * D + (((col >> 3) ^ sw) << 3) + (col & 7);
+    } else {
+      return r * kRowElems + col;
+    }
+  }
+};
+
 // ---------------------------------------------------------------------------
 // Tile staging: rows key0 .. key0+63 of a [N, D] head, zero past N.
 // ---------------------------------------------------------------------------
@@ -42,30 +74,35 @@ __device__ inline void fetch_tile(const T* __restrict__ x, int key0, int N, int 
   }
 }
 
-template <int D, int NT, int S>
+template <int D, int L, int NT>
 __device__ inline void put_tile(uint16_t* lds, int tid, const bf16x8* r) {
   constexpr int CPR = D / 8, CPT = 64 * CPR / NT;
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
     const int ch = tid + c * NT, row = ch / CPR, c8 = ch % CPR;
-    *reinterpret_cast<bf16x8*>(lds + row * S + c8 * 8) = r[c];
+    *reinterpret_cast<bf16x8*>(lds + Tile<D, L>::off(row, c8 * 8)) = r[c];
   }
 }
 
-// A operand X^T[n][k-slots] of a 32x32x16 MFMA from a row-major LDS tile X
-// (stride S), for the 16 rows k = kbase .. kbase+15 and the 32 columns
-// n = nbase .. nbase+31.  Slot 8h + i (h = lane/32) maps to row
-// kbase + 8(i/4) + 4h + i%4, the same order in which a 32x32 accumulator
-// holds its rows, so an accumulator tile can be fed as the B operand.
-template <int S>
+// A operand X^T[n][k-slots] of a 32x32x16 MFMA from a row-major LDS tile X,
+// for the 16 rows k = kbase .. kbase+15 and the 32 columns n = nbase ..
+// nbase+31.  Slot 8h + i (h = lane/32) maps to row kbase + 8(i/4) + 4h + i%4,
+// the same order in which a 32x32 accumulator holds its rows, so an
+// accumulator tile can be fed as the B operand.
+template <int D, int L>
 __device__ inline bf16x8 tr_operand(const uint16_t* lds, int kbase, int nbase, int lane) {
   const int h = lane >> 5;
   const int r = kbase + 4 * h + ((lane & 15) >> 2);
   const int c = nbase + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const bf16x4 lo = lds_read_tr(lds + r * S + c);
-  const bf16x4 hi = lds_read_tr(lds + (r + 8) * S + c);
+  const bf16x4 lo = lds_read_tr(lds + Tile<D, L>::off(r, c));
+  const bf16x4 hi = lds_read_tr(lds + Tile<D, L>::off(r + 8, c));
   return cat(lo, hi);
 }
+
+// Rows of the running max only move when the tile maximum exceeds them by
+// more than this (log2 units): P then stays below 2^8, and the rescale of the
+// output accumulators is skipped on most tiles.
+constexpr float kRescaleThreshold = 8.0f;
 
 // Eight accumulator values e0 .. e0+7 as a bf16 B operand.
 __device__ inline bf16x8 pack8(const f32x16& a, int e0) {
@@ -79,16 +116,17 @@ __device__ inline bf16x8 pack8(const f32x16& a, int e0) {
 // Forward
 // ---------------------------------------------------------------------------
 template <typename T, int D, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4 ? 2 : 1, 2)))
 void fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                 const int32_t* __restrict__ row_cnt, const int32_t* __restrict__ row_idx, int N,
                 int Tq, int Tk, float scale_log2, T* __restrict__ o, float* __restrict__ lse) {
   constexpr int NT = NW * 64;
-  constexpr int KS = D + 8, VS = D + 16;
+  using KT = Tile<D, kRows>;
+  using VT = Tile<D, kCols>;
   constexpr int NK = D / 16, ND = D / 32;
   constexpr int CPT = 64 * (D / 8) / NT;
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[64 * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[64 * VS];
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[64 * KT::kRowElems];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[64 * VT::kRowElems];
 
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = wg / Tq, qi = wg % Tq;
@@ -120,8 +158,8 @@ void fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
   for (int t = 0; t < cnt; ++t) {
     const int key0 = lst[t] * 64;
     __syncthreads();
-    put_tile<D, NT, KS>(k_lds, tid, kr);
-    put_tile<D, NT, VS>(v_lds, tid, vr);
+    put_tile<D, kRows, NT>(k_lds, tid, kr);
+    put_tile<D, kCols, NT>(v_lds, tid, vr);
     __syncthreads();
     if (t + 1 < cnt) {
       const int nk0 = lst[t + 1] * 64;
@@ -135,42 +173,46 @@ void fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
       s[b] = zero16();
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk)
-        s[b] = mfma32(lds_read8(k_lds + (32 * b + l32) * KS + 16 * kk + 8 * h), qf[kk], s[b]);
+        s[b] = mfma32(lds_read8(k_lds + KT::off(32 * b + l32, 16 * kk + 8 * h)), qf[kk], s[b]);
     }
-    const bool tail = key0 + 64 > N;
-    float mloc = -INFINITY;
+    if (key0 + 64 > N) {  // the partial last key block (a uniform branch)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (key0 + 32 * b + 8 * (e >> 2) + 4 * h + (e & 3) >= N) s[b][e] = -INFINITY;
+    }
+    float mx = s[0][0];
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float x = s[b][e] * scale_log2;
-        if (tail && key0 + 32 * b + 8 * (e >> 2) + 4 * h + (e & 3) >= N) x = -INFINITY;
-        s[b][e] = x;
-        mloc = fmaxf(mloc, x);
-      }
-    mloc = wave_max32(mloc);
-    const float mnew = fmaxf(m, mloc);
-    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-    m = mnew;
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[b][e]);
+    mx = wave_max32(mx) * scale_log2;
+    if (__any(mx > m + kRescaleThreshold)) {
+      const float mnew = fmaxf(m, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+      m = mnew;
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < ND; ++db) acc[db] *= alpha;
+    }
     float ps = 0.f;
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float pv = __builtin_amdgcn_exp2f(s[b][e] - mnew);
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][e], scale_log2, -m));
         s[b][e] = pv;
         ps += pv;
       }
-    lsum = lsum * alpha + ps;
-#pragma unroll
-    for (int db = 0; db < ND; ++db) acc[db] *= alpha;
+    lsum += ps;
     // O^T += V^T P^T over four 16-key steps
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
       const bf16x8 pf = pack8(s[tt >> 1], 8 * (tt & 1));
 #pragma unroll
       for (int db = 0; db < ND; ++db)
-        acc[db] = mfma32(tr_operand<VS>(v_lds, 16 * tt, 32 * db, lane), pf, acc[db]);
+        acc[db] = mfma32(tr_operand<D, kCols>(v_lds, 16 * tt, 32 * db, lane), pf, acc[db]);
     }
   }
   const float ltot = lsum + __shfl_xor(lsum, 32);
@@ -208,22 +250,24 @@ void dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
                  const int32_t* __restrict__ col_idx, int N, int Tq, int Tk, float scale_log2,
                  float scale, T* __restrict__ dk, T* __restrict__ dv) {
   constexpr int NT = 256;
-  constexpr int KS = D + 8;   // K, V tiles: 16-byte fragment reads
-  constexpr int CS = D + 16;  // Q / dO slices: fragment and transposed reads
+  using KT = Tile<D, kRows>;   // K, V tiles: fragment reads
+  using ST = Tile<D, kBoth>;   // Q / dO slices: fragment and transposed reads
   constexpr int NK = D / 16, ND = D / 32;
   constexpr int CPT = 64 * (D / 8) / NT;
   constexpr int SUB = BQ / 32;   // 32-row slices per query block
   constexpr int SPP = SUB / 2;   // slices per pair per query block
   constexpr int RS = D + 4;      // fp32 staging of a wave's output tile
-  constexpr int TILE_BYTES = 2 * 64 * KS * 2;
-  constexpr int SLICE_BYTES = 2 * 2 * 32 * CS * 2;
-  static_assert(TILE_BYTES + SLICE_BYTES >= 2 * 2 * 32 * RS * 4, "output staging must fit");
-  __shared__ __attribute__((aligned(16))) unsigned char smem[TILE_BYTES + SLICE_BYTES];
+  constexpr int TILE_BYTES = 2 * 64 * KT::kRowElems * 2;
+  constexpr int SLICE_BYTES = 2 * 2 * 32 * ST::kRowElems * 2;
+  constexpr int STAGE_BYTES = 2 * 2 * 32 * RS * 4;  // [key half][dV | dK] fp32 tiles
+  constexpr int SMEM_BYTES = TILE_BYTES + SLICE_BYTES > STAGE_BYTES ? TILE_BYTES + SLICE_BYTES
+                                                                    : STAGE_BYTES;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM_BYTES];
   __shared__ __attribute__((aligned(16))) float st[2][2][32];  // [pair][lse2 | Delta][row]
 
   uint16_t* k_lds = reinterpret_cast<uint16_t*>(smem);
-  uint16_t* v_lds = k_lds + 64 * KS;
-  uint16_t* slices = v_lds + 64 * KS;                          // [pair][Q | dO][32*CS]
+  uint16_t* v_lds = k_lds + 64 * KT::kRowElems;
+  uint16_t* slices = v_lds + 64 * KT::kRowElems;               // [pair][Q | dO][32 rows]
 
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = wg / Tk, kj = wg % Tk;
@@ -236,22 +280,20 @@ void dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
   {
     bf16x8 r[CPT];
     fetch_tile<T, D, NT>(k + base, key0, N, tid, r);
-    put_tile<D, NT, KS>(k_lds, tid, r);
+    put_tile<D, kRows, NT>(k_lds, tid, r);
     fetch_tile<T, D, NT>(v + base, key0, N, tid, r);
-    put_tile<D, NT, KS>(v_lds, tid, r);
+    put_tile<D, kRows, NT>(v_lds, tid, r);
   }
   // the tiles are complete before any wave reads them, and before the output
   // staging (which reuses this memory) of a key block with an empty list
   __syncthreads();
 
-  uint16_t* sq = slices + (2 * pair) * 32 * CS;   // this pair's Q slice
-  uint16_t* sd = sq + 32 * CS;                     // this pair's dO slice
+  uint16_t* sq = slices + (2 * pair) * 32 * ST::kRowElems;   // this pair's Q slice
+  uint16_t* sd = sq + 32 * ST::kRowElems;                     // this pair's dO slice
   uint16_t* mine = kb == 0 ? sq : sd;              // the half this wave stages
   const T* src = kb == 0 ? q : dout;
   const float* ssrc = kb == 0 ? lse : delta;
-  const bool kval = key0 + 32 * kb + l32 < N;      // this lane's key exists
-  const uint16_t* kf_row = k_lds + (32 * kb + l32) * KS + 8 * h;
-  const uint16_t* vf_row = v_lds + (32 * kb + l32) * KS + 8 * h;
+  const int krow = 32 * kb + l32;                  // this lane's row of K, V
 
   f32x16 accv[ND], acck[ND];
 #pragma unroll
@@ -282,7 +324,7 @@ void dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
   for (int s = 0; s < steps; ++s) {
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk)
-      *reinterpret_cast<bf16x8*>(mine + l32 * CS + 16 * kk + 8 * h) = own[kk];
+      *reinterpret_cast<bf16x8*>(mine + ST::off(l32, 16 * kk + 8 * h)) = own[kk];
     if (h == 0) st[pair][kb][l32] = stat;
     __syncthreads();
     // S = Q K^T and dP = dO V^T: the slice's 32 rows against this wave's 32 keys
@@ -290,21 +332,25 @@ void dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
     if (kb == 0) {
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
-        sa = mfma32(own[kk], lds_read8(kf_row + 16 * kk), sa);
-        dpa = mfma32(lds_read8(sd + l32 * CS + 16 * kk + 8 * h), lds_read8(vf_row + 16 * kk), dpa);
+        const int c = 16 * kk + 8 * h;
+        sa = mfma32(own[kk], lds_read8(k_lds + KT::off(krow, c)), sa);
+        dpa = mfma32(lds_read8(sd + ST::off(l32, c)), lds_read8(v_lds + KT::off(krow, c)), dpa);
       }
     } else {
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
-        sa = mfma32(lds_read8(sq + l32 * CS + 16 * kk + 8 * h), lds_read8(kf_row + 16 * kk), sa);
-        dpa = mfma32(own[kk], lds_read8(vf_row + 16 * kk), dpa);
+        const int c = 16 * kk + 8 * h;
+        sa = mfma32(lds_read8(sq + ST::off(l32, c)), lds_read8(k_lds + KT::off(krow, c)), sa);
+        dpa = mfma32(own[kk], lds_read8(v_lds + KT::off(krow, c)), dpa);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
     if (s + 1 < steps) fetch(s + 1);
     __builtin_amdgcn_sched_barrier(0);
     // P = exp(S/sqrt(d) - LSE) and dS = P * (dP - Delta) for rows 8g+4h+i,
-    // packed at once into the B operands of the two 16-row steps
+    // packed at once into the B operands of the two 16-row steps.  Keys past
+    // N need no mask: their K and V rows are zero and they only feed their
+    // own (unstored) dK, dV rows.
     bf16x8 pb[2], sb[2];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -313,8 +359,7 @@ void dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int e = 4 * g + i;
-        float pv = __builtin_amdgcn_exp2f(sa[e] * scale_log2 - L[i]);
-        pv = kval ? pv : 0.f;
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[e], scale_log2, -L[i]));
         pb[g >> 1][4 * (g & 1) + i] = (__bf16)pv;
         sb[g >> 1][4 * (g & 1) + i] = (__bf16)(pv * (dpa[e] - Dl[i]));
       }
@@ -324,8 +369,8 @@ void dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int db = 0; db < ND; ++db) {
-        accv[db] = mfma32(tr_operand<CS>(sd, 16 * t, 32 * db, lane), pb[t], accv[db]);
-        acck[db] = mfma32(tr_operand<CS>(sq, 16 * t, 32 * db, lane), sb[t], acck[db]);
+        accv[db] = mfma32(tr_operand<D, kBoth>(sd, 16 * t, 32 * db, lane), pb[t], accv[db]);
+        acck[db] = mfma32(tr_operand<D, kBoth>(sq, 16 * t, 32 * db, lane), sb[t], acck[db]);
       }
     __syncthreads();
   }
@@ -379,22 +424,222 @@ void dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
 }
 
 // ---------------------------------------------------------------------------
+// Backward dK, dV for bf16 and d = 128: one workgroup (8 waves) per key block.
+//
+// Wave (pair p, kb) owns keys key0 + 32kb .. +31: their K fragments live in
+// registers for the whole kernel, their dK and dV tiles (32 x 128) in
+// accumulators.  Pair p takes the 32-row slices 4j + p of the flattened list
+// of (listed query block, slice) pairs.  Slices (Q, dO) and their LSE / Delta
+// are copied from global memory straight into LDS (global_load_lds, 16 bytes
+// per lane into lane-consecutive LDS units; which global unit a lane loads
+// realises the permuted row layout) into a double buffer, so the copy of the
+// next slice is in flight during the current one and costs no registers.
+// One workgroup barrier per step: after it, every wave's copy for this step
+// has landed (each waits for its own first) and every wave has finished with
+// the other buffer, which then receives the next copy.
+// ---------------------------------------------------------------------------
+template <int BQ>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void dkdv_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                       const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
+                       const float* __restrict__ lse, const float* __restrict__ delta,
+                       const int32_t* __restrict__ col_cnt, const int32_t* __restrict__ col_idx,
+                       int N, int Tq, int Tk, float scale_log2, float scale,
+                       bf16_t* __restrict__ dk, bf16_t* __restrict__ dv) {
+  constexpr int D = 128, NT = 512;
+  using VT = Tile<D, kRows>;   // V tile: fragment reads
+  using ST = Tile<D, kBoth>;   // slices: permuted, unpadded rows of 256 bytes
+  static_assert(ST::kSwizzled, "slices are copied as whole 256-byte rows");
+  constexpr int NK = D / 16, ND = D / 32;
+  constexpr int SUB = BQ / 32;                       // slices per query block
+  constexpr int SLICE = 32 * D;                      // elements of one slice tensor
+  constexpr int V_BYTES = 64 * VT::kRowElems * 2;
+  constexpr int STAGE_BYTES = 2 * 4 * 2 * SLICE * 2; // [buffer][pair][Q | dO]
+  constexpr int ST_BYTES = 2 * 4 * 64 * 4;           // [buffer][pair][lse | Delta][32]
+  constexpr int RS = D + 4;
+  constexpr int RED_BYTES = 3 * 2 * 32 * RS * 4;     // partial tiles of pairs 1..3
+  static_assert(RED_BYTES <= STAGE_BYTES, "reduction reuses the slice buffers");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[V_BYTES + STAGE_BYTES + ST_BYTES];
+  uint16_t* v_lds = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* stage = reinterpret_cast<uint16_t*>(smem + V_BYTES);
+  float* stats = reinterpret_cast<float*>(smem + V_BYTES + STAGE_BYTES);
+
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = wg / Tk, kj = wg % Tk;
+  const int key0 = kj * 64;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int pair = w >> 1, kb = w & 1;
+  const size_t base = (size_t)bh * N * D;
+
+  // K fragments of this wave's keys (B operand of S = Q K^T), zero past N
+  bf16x8 kf[NK];
+  {
+    const int key = key0 + 32 * kb + l32;
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk)
+      kf[kk] = key < N ? load8(k + base + (size_t)key * D + 16 * kk + 8 * h) : zero8();
+    bf16x8 r[2];
+    fetch_tile<bf16_t, D, NT>(v + base, key0, N, tid, r);
+    put_tile<D, kRows, NT>(v_lds, tid, r);
+  }
+
+  const int cnt = col_cnt[wg];
+  const int32_t* lst = col_idx + (size_t)wg * Tq;
+  const int total = cnt * SUB;
+  const int steps = (total + 3) / 4;
+
+  // Copy slice g = 4s + pair of step s into buffer b: wave kb = 0 copies Q
+  // and the 32 rows' LSE and Delta, wave kb = 1 copies dO.  Rows past N are
+  // read from row N-1 (their P is zeroed below).
+  auto copy_step = [&](int s, int b) {
+    const int g = 4 * s + pair;
+    if (g >= total) return;
+    const int row0 = lst[g / SUB] * BQ + 32 * (g % SUB);
+    const bf16_t* src = (kb == 0 ? q : dout) + base;
+    uint16_t* dst = stage + ((b * 4 + pair) * 2 + kb) * SLICE;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 4 * i + (lane >> 4);
+      const int sw = ((r & 3) << 2) | ((r >> 2) & 3);
+      const int u = (lane & 15) ^ sw;          // the logical unit this lane's LDS unit holds
+      const int row = min(row0 + r, N - 1);
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(src + (size_t)row * D + 8 * u),
+          (__attribute__((address_space(3))) void*)(dst + i * 512), 16, 0, 0);
+    }
+    if (kb == 0) {
+      const int rr = min(row0 + l32, N - 1);
+      const float* sp = (h == 0 ? lse : delta) + (size_t)bh * N + rr;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)sp,
+                                       (__attribute__((address_space(3))) void*)(stats + (b * 4 + pair) * 64),
+                                       4, 0, 0);
+    }
+  };
+
+  f32x16 accv[ND], acck[ND];
+#pragma unroll
+  for (int db = 0; db < ND; ++db) {
+    accv[db] = zero16();
+    acck[db] = zero16();
+  }
+  const int krow = 32 * kb + l32;
+
+  if (steps > 0) copy_step(0, 0);
+  for (int s = 0; s < steps; ++s) {
+    const int b = s & 1;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (s + 1 < steps) copy_step(s + 1, b ^ 1);
+    const int g = 4 * s + pair;
+    if (g < total) {
+      const int row0 = lst[g / SUB] * BQ + 32 * (g % SUB);
+      const uint16_t* sq = stage + ((b * 4 + pair) * 2) * SLICE;
+      const uint16_t* sd = sq + SLICE;
+      const float* stl = stats + (b * 4 + pair) * 64;
+      // S = Q K^T and dP = dO V^T for the slice's 32 rows and this wave's keys
+      f32x16 sa = zero16(), dpa = zero16();
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        const int c = 16 * kk + 8 * h;
+        sa = mfma32(lds_read8(sq + ST::off(l32, c)), kf[kk], sa);
+        dpa = mfma32(lds_read8(sd + ST::off(l32, c)), lds_read8(v_lds + VT::off(krow, c)), dpa);
+      }
+      // P and dS for rows 8g+4h+i, packed into the B operands of the two
+      // 16-row steps (keys past N need no mask: they only feed their own,
+      // unstored, dK and dV rows)
+      bf16x8 pb[2], sb[2];
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        const f32x4 L = *reinterpret_cast<const f32x4*>(stl + 8 * gg + 4 * h);
+        const f32x4 Dl = *reinterpret_cast<const f32x4*>(stl + 32 + 8 * gg + 4 * h);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = 4 * gg + i;
+          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[e], scale_log2, -L[i] * kLog2e));
+          pb[gg >> 1][4 * (gg & 1) + i] = (__bf16)pv;
+          sb[gg >> 1][4 * (gg & 1) + i] = (__bf16)(pv * (dpa[e] - Dl[i]));
+        }
+      }
+      if (row0 + 32 > N) {  // the partial last query block: rows past N add nothing
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (row0 + 8 * (e >> 2) + 4 * h + (e & 3) >= N) {
+            pb[e >> 3][e & 7] = (__bf16)0.f;
+            sb[e >> 3][e & 7] = (__bf16)0.f;
+          }
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS over the slice's rows
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int db = 0; db < ND; ++db) {
+          accv[db] = mfma32(tr_operand<D, kBoth>(sd, 16 * t, 32 * db, lane), pb[t], accv[db]);
+          acck[db] = mfma32(tr_operand<D, kBoth>(sq, 16 * t, 32 * db, lane), sb[t], acck[db]);
+        }
+    }
+  }
+
+  // Sum the four pairs' partial tiles: pairs 1..3 write theirs to LDS, pair 0
+  // adds them in pair order and stores.  Element e of block db is
+  // d = 32db + 8(e/4) + 4h + e%4 at key 32kb + l32.
+  float* red = reinterpret_cast<float*>(stage);
+  for (int which = 0; which < 2; ++which) {
+    __syncthreads();
+    if (pair > 0) {
+      float* t = red + ((pair - 1) * 2 + kb) * 32 * RS;
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          t[l32 * RS + 32 * db + 8 * (e >> 2) + 4 * h + (e & 3)] =
+              which == 0 ? accv[db][e] : acck[db][e];
+    }
+    __syncthreads();
+    if (pair == 0) {
+      const float mul = which == 0 ? 1.f : scale;
+      float* t0 = red + kb * 32 * RS;   // pair 1's tile, overwritten with the sum
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int off = l32 * RS + 32 * db + 8 * (e >> 2) + 4 * h + (e & 3);
+          float sum = which == 0 ? accv[db][e] : acck[db][e];
+#pragma unroll
+          for (int pp = 0; pp < 3; ++pp) sum += red[(pp * 2 + kb) * 32 * RS + off];
+          t0[off] = sum * mul;
+        }
+      wave_lds_sync();
+      bf16_t* out = (which == 0 ? dv : dk) + base;
+      for (int ch = lane; ch < 32 * D / 4; ch += 64) {
+        const int r = ch / (D / 4), c4 = (ch % (D / 4)) * 4;
+        const int key = key0 + 32 * kb + r;
+        if (key < N) {
+          const float* pp = t0 + r * RS + c4;
+          store4(out + (size_t)key * D + c4, pp[0], pp[1], pp[2], pp[3]);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Backward dQ: one workgroup per query block, walking its row list.
 // ---------------------------------------------------------------------------
 template <typename T, int D, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4 ? 2 : 1, 2)))
 void dq_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                const T* __restrict__ o, const T* __restrict__ dout, const float* __restrict__ lse,
                float* __restrict__ delta, const int32_t* __restrict__ row_cnt,
                const int32_t* __restrict__ row_idx, int N, int Tq, int Tk, float scale_log2,
                float scale, T* __restrict__ dq) {
   constexpr int NT = NW * 64;
-  constexpr int KS = D + 16;  // K: fragment reads and transposed reads
-  constexpr int VS = D + 8;   // V: fragment reads
+  using KT = Tile<D, kPad16>;  // K: fragment and transposed reads
+  using VT = Tile<D, kRows>;   // V: fragment reads
   constexpr int NK = D / 16, ND = D / 32;
   constexpr int CPT = 64 * (D / 8) / NT;
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[64 * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[64 * VS];
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[64 * KT::kRowElems];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[64 * VT::kRowElems];
 
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = wg / Tq, qi = wg % Tq;
@@ -442,8 +687,8 @@ void dq_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __rest
   for (int t = 0; t < cnt; ++t) {
     const int key0 = lst[t] * 64;
     __syncthreads();
-    put_tile<D, NT, KS>(k_lds, tid, kr);
-    put_tile<D, NT, VS>(v_lds, tid, vr);
+    put_tile<D, kPad16, NT>(k_lds, tid, kr);
+    put_tile<D, kRows, NT>(v_lds, tid, vr);
     __syncthreads();
     if (t + 1 < cnt) {
       const int nk0 = lst[t + 1] * 64;
@@ -457,25 +702,32 @@ void dq_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __rest
       dp[b] = zero16();
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
-        s[b] = mfma32(lds_read8(k_lds + (32 * b + l32) * KS + 16 * kk + 8 * h), qf[kk], s[b]);
-        dp[b] = mfma32(lds_read8(v_lds + (32 * b + l32) * VS + 16 * kk + 8 * h), df[kk], dp[b]);
+        const int c = 16 * kk + 8 * h;
+        s[b] = mfma32(lds_read8(k_lds + KT::off(32 * b + l32, c)), qf[kk], s[b]);
+        dp[b] = mfma32(lds_read8(v_lds + VT::off(32 * b + l32, c)), df[kk], dp[b]);
       }
     }
-    const bool tail = key0 + 64 > N;
+    // dS = P * (dP - Delta)
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        float pv = __builtin_amdgcn_exp2f(s[b][e] * scale_log2 - l2);
-        if (tail && key0 + 32 * b + 8 * (e >> 2) + 4 * h + (e & 3) >= N) pv = 0.f;
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][e], scale_log2, -l2));
         s[b][e] = pv * (dp[b][e] - dl);
       }
+    if (key0 + 64 > N) {  // keys past N enter the dQ contraction: zero them
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (key0 + 32 * b + 8 * (e >> 2) + 4 * h + (e & 3) >= N) s[b][e] = 0.f;
+    }
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
       const bf16x8 sf = pack8(s[tt >> 1], 8 * (tt & 1));
 #pragma unroll
       for (int db = 0; db < ND; ++db)
-        acc[db] = mfma32(tr_operand<KS>(k_lds, 16 * tt, 32 * db, lane), sf, acc[db]);
+        acc[db] = mfma32(tr_operand<D, kPad16>(k_lds, 16 * tt, 32 * db, lane), sf, acc[db]);
     }
   }
   if (qvalid) {
@@ -552,6 +804,17 @@ static void launch_dq(const BwdArgs& a) {
 template <typename T, int D>
 static void launch_dkdv(const BwdArgs& a) {
   const sa2_mask* m = a.m;
+  if constexpr (D == 128 && sizeof(T) == 2) {
+#define SA2_DKDV_ASYNC_ARGS                                                                  \
+  static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k),                            \
+      static_cast<const bf16_t*>(a.v), static_cast<const bf16_t*>(a.dout), a.lse, a.delta,     \
+      m->col_cnt, m->col_idx, a.N, m->Tq, m->Tk, a.sl2, a.scale, static_cast<bf16_t*>(a.dk),   \
+      static_cast<bf16_t*>(a.dv)
+    if (m->bq == 128) dkdv_async_kernel<128><<<a.BH * m->Tk, 512, 0, a.s>>>(SA2_DKDV_ASYNC_ARGS);
+    else dkdv_async_kernel<64><<<a.BH * m->Tk, 512, 0, a.s>>>(SA2_DKDV_ASYNC_ARGS);
+#undef SA2_DKDV_ASYNC_ARGS
+    return;
+  }
 #define SA2_DKDV_ARGS                                                                         \
   static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),          \
       static_cast<const T*>(a.dout), a.lse, a.delta, m->col_cnt, m->col_idx, a.N, m->Tq, m->Tk, \
