@@ -42,7 +42,22 @@ def parse():
     ap.add_argument("--workload", default="c2", help="workload key (default: 1.3B layer fwd+bwd)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=3, help="heads the oracle times")
+    ap.add_argument("--no-work-order", action="store_true",
+                    help="schedule the attention kernels in their fixed order")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only copy BYTES once on the GPU (calibrates the HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_probe(nbytes: int) -> None:
+    """One device-to-device copy of a known size, for scaling FETCH_SIZE/WRITE_SIZE."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": src.numel() * 4}), flush=True)
 
 
 def cpu_baseline(w, k_frac, p, ref, heads, eff_flops_layer):
@@ -67,6 +82,9 @@ def cpu_baseline(w, k_frac, p, ref, heads, eff_flops_layer):
 
 def main():
     args = parse()
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the hot path is measured per GPU (heads shard "
               "with no exchange); run it with --gpus 1", file=sys.stderr)
@@ -97,7 +115,7 @@ def main():
     B, H, N, d = q.shape
 
     # everything the step touches is allocated once, outside the timed region
-    mask = sa2.BlockMask(B, H, N, w.bq, w.bk, dev)
+    mask = sa2.BlockMask(B, H, N, w.bq, w.bk, dev, work_order=not args.no_work_order)
     mws = torch.empty(sa2.mask_workspace_bytes(B, H, N, d, w.bq, w.bk), dtype=torch.uint8, device=dev)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)

@@ -71,7 +71,7 @@ class BlockMask:
       col_cnt int32 [B, H, Tk];  col_idx int32 [B, H, Tk, Tq] (first col_cnt valid)
     """
 
-    def __init__(self, B: int, H: int, N: int, bq: int, bk: int, device):
+    def __init__(self, B: int, H: int, N: int, bq: int, bk: int, device, work_order: bool = True):
         self.B, self.H, self.N, self.bq, self.bk = B, H, N, bq, bk
         self.Tq = -(-N // bq)
         self.Tk = -(-N // bk)
@@ -82,10 +82,15 @@ class BlockMask:
         self.row_idx = torch.empty((B, H, self.Tq, self.Tk), **i32)
         self.col_cnt = torch.empty((B, H, self.Tk), **i32)
         self.col_idx = torch.empty((B, H, self.Tk, self.Tq), **i32)
+        # optional work orders (longest lists first); None: fixed XCD-aware order
+        self.row_order = torch.empty((B * H * self.Tq,), **i32) if work_order else None
+        self.col_order = torch.empty((B * H * self.Tk,), **i32) if work_order else None
         self._c = Sa2Mask(B, H, N, bq, bk, self.Tq, self.Tk,
                           self.bitmap.data_ptr(), self.row_cnt.data_ptr(),
                           self.row_idx.data_ptr(), self.col_cnt.data_ptr(),
-                          self.col_idx.data_ptr())
+                          self.col_idx.data_ptr(),
+                          self.row_order.data_ptr() if work_order else None,
+                          self.col_order.data_ptr() if work_order else None)
 
     @property
     def device(self):
@@ -112,14 +117,15 @@ def mask_workspace_bytes(B, H, N, d, bq, bk) -> int:
 
 
 def build_mask(q: torch.Tensor, k: torch.Tensor, bq: int, bk: int, k_frac: float, p: float,
-               mask: BlockMask | None = None, workspace: torch.Tensor | None = None) -> BlockMask:
+               mask: BlockMask | None = None, workspace: torch.Tensor | None = None,
+               work_order: bool = True) -> BlockMask:
     """Hybrid Top-k + Top-p block mask of q, k (sa2_build_mask)."""
     dt = _dtype_code(q, k)
     B, H, N, d = _shape(q)
     if _shape(k) != (B, H, N, d):
         raise ValueError("q and k must have the same shape")
     if mask is None:
-        mask = BlockMask(B, H, N, bq, bk, q.device)
+        mask = BlockMask(B, H, N, bq, bk, q.device, work_order=work_order)
     need = mask_workspace_bytes(B, H, N, d, bq, bk)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)

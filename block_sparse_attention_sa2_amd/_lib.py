@@ -19,6 +19,7 @@ class Sa2Mask(ctypes.Structure):
         ("Tk", ctypes.c_int32),
         ("bitmap", ctypes.c_void_p), ("row_cnt", ctypes.c_void_p), ("row_idx", ctypes.c_void_p),
         ("col_cnt", ctypes.c_void_p), ("col_idx", ctypes.c_void_p),
+        ("row_order", ctypes.c_void_p), ("col_order", ctypes.c_void_p),
     ]
 
 

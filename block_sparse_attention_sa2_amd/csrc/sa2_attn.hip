@@ -118,8 +118,9 @@ __device__ inline bf16x8 pack8(const f32x16& a, int e0) {
 template <typename T, int D, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4 ? 2 : 1, 2)))
 void fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-                const int32_t* __restrict__ row_cnt, const int32_t* __restrict__ row_idx, int N,
-                int Tq, int Tk, float scale_log2, T* __restrict__ o, float* __restrict__ lse) {
+                const int32_t* __restrict__ row_cnt, const int32_t* __restrict__ row_idx,
+                const int32_t* __restrict__ order, int N, int Tq, int Tk, float scale_log2,
+                T* __restrict__ o, float* __restrict__ lse) {
   constexpr int NT = NW * 64;
   using KT = Tile<D, kRows>;
   using VT = Tile<D, kCols>;
@@ -128,7 +129,7 @@ void fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[64 * KT::kRowElems];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[64 * VT::kRowElems];
 
-  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int wg = order ? order[blockIdx.x] : xcd_remap(blockIdx.x, gridDim.x);
   const int bh = wg / Tq, qi = wg % Tq;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
@@ -247,8 +248,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                  const T* __restrict__ dout, const float* __restrict__ lse,
                  const float* __restrict__ delta, const int32_t* __restrict__ col_cnt,
-                 const int32_t* __restrict__ col_idx, int N, int Tq, int Tk, float scale_log2,
-                 float scale, T* __restrict__ dk, T* __restrict__ dv) {
+                 const int32_t* __restrict__ col_idx, const int32_t* __restrict__ order, int N,
+                 int Tq, int Tk, float scale_log2, float scale, T* __restrict__ dk,
+                 T* __restrict__ dv) {
   constexpr int NT = 256;
   using KT = Tile<D, kRows>;   // K, V tiles: fragment reads
   using ST = Tile<D, kBoth>;   // Q / dO slices: fragment and transposed reads
@@ -269,7 +271,7 @@ void dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
   uint16_t* v_lds = k_lds + 64 * KT::kRowElems;
   uint16_t* slices = v_lds + 64 * KT::kRowElems;               // [pair][Q | dO][32 rows]
 
-  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int wg = order ? order[blockIdx.x] : xcd_remap(blockIdx.x, gridDim.x);
   const int bh = wg / Tk, kj = wg % Tk;
   const int key0 = kj * 64;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -444,8 +446,9 @@ void dkdv_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ 
                        const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
                        const float* __restrict__ lse, const float* __restrict__ delta,
                        const int32_t* __restrict__ col_cnt, const int32_t* __restrict__ col_idx,
-                       int N, int Tq, int Tk, float scale_log2, float scale,
-                       bf16_t* __restrict__ dk, bf16_t* __restrict__ dv) {
+                       const int32_t* __restrict__ order, int N, int Tq, int Tk,
+                       float scale_log2, float scale, bf16_t* __restrict__ dk,
+                       bf16_t* __restrict__ dv) {
   constexpr int D = 128, NT = 512;
   using VT = Tile<D, kRows>;   // V tile: fragment reads
   using ST = Tile<D, kBoth>;   // slices: permuted, unpadded rows of 256 bytes
@@ -464,7 +467,7 @@ void dkdv_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ 
   uint16_t* stage = reinterpret_cast<uint16_t*>(smem + V_BYTES);
   float* stats = reinterpret_cast<float*>(smem + V_BYTES + STAGE_BYTES);
 
-  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int wg = order ? order[blockIdx.x] : xcd_remap(blockIdx.x, gridDim.x);
   const int bh = wg / Tk, kj = wg % Tk;
   const int key0 = kj * 64;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -631,8 +634,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4
 void dq_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                const T* __restrict__ o, const T* __restrict__ dout, const float* __restrict__ lse,
                float* __restrict__ delta, const int32_t* __restrict__ row_cnt,
-               const int32_t* __restrict__ row_idx, int N, int Tq, int Tk, float scale_log2,
-               float scale, T* __restrict__ dq) {
+               const int32_t* __restrict__ row_idx, const int32_t* __restrict__ order, int N,
+               int Tq, int Tk, float scale_log2, float scale, T* __restrict__ dq) {
   constexpr int NT = NW * 64;
   using KT = Tile<D, kPad16>;  // K: fragment and transposed reads
   using VT = Tile<D, kRows>;   // V: fragment reads
@@ -641,7 +644,7 @@ void dq_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __rest
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[64 * KT::kRowElems];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[64 * VT::kRowElems];
 
-  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int wg = order ? order[blockIdx.x] : xcd_remap(blockIdx.x, gridDim.x);
   const int bh = wg / Tq, qi = wg % Tq;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
@@ -768,7 +771,7 @@ static void launch_fwd(const void* q, const void* k, const void* v, const sa2_ma
                        int N, float sl2, void* o, float* lse, hipStream_t s) {
   fwd_kernel<T, D, NW><<<BH * m->Tq, NW * 64, 0, s>>>(
       static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), m->row_cnt,
-      m->row_idx, N, m->Tq, m->Tk, sl2, static_cast<T*>(o), lse);
+      m->row_idx, m->row_order, N, m->Tq, m->Tk, sl2, static_cast<T*>(o), lse);
 }
 
 template <typename T, int D>
@@ -795,7 +798,7 @@ static void launch_dq(const BwdArgs& a) {
 #define SA2_DQ_ARGS                                                                          \
   static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),          \
       static_cast<const T*>(a.o), static_cast<const T*>(a.dout), a.lse, a.delta, m->row_cnt,  \
-      m->row_idx, a.N, m->Tq, m->Tk, a.sl2, a.scale, static_cast<T*>(a.dq)
+      m->row_idx, m->row_order, a.N, m->Tq, m->Tk, a.sl2, a.scale, static_cast<T*>(a.dq)
   if (m->bq == 128) dq_kernel<T, D, 4><<<a.BH * m->Tq, 256, 0, a.s>>>(SA2_DQ_ARGS);
   else dq_kernel<T, D, 2><<<a.BH * m->Tq, 128, 0, a.s>>>(SA2_DQ_ARGS);
 #undef SA2_DQ_ARGS
@@ -808,8 +811,8 @@ static void launch_dkdv(const BwdArgs& a) {
 #define SA2_DKDV_ASYNC_ARGS                                                                  \
   static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k),                            \
       static_cast<const bf16_t*>(a.v), static_cast<const bf16_t*>(a.dout), a.lse, a.delta,     \
-      m->col_cnt, m->col_idx, a.N, m->Tq, m->Tk, a.sl2, a.scale, static_cast<bf16_t*>(a.dk),   \
-      static_cast<bf16_t*>(a.dv)
+      m->col_cnt, m->col_idx, m->col_order, a.N, m->Tq, m->Tk, a.sl2, a.scale,                 \
+      static_cast<bf16_t*>(a.dk), static_cast<bf16_t*>(a.dv)
     if (m->bq == 128) dkdv_async_kernel<128><<<a.BH * m->Tk, 512, 0, a.s>>>(SA2_DKDV_ASYNC_ARGS);
     else dkdv_async_kernel<64><<<a.BH * m->Tk, 512, 0, a.s>>>(SA2_DKDV_ASYNC_ARGS);
 #undef SA2_DKDV_ASYNC_ARGS
@@ -817,8 +820,8 @@ static void launch_dkdv(const BwdArgs& a) {
   }
 #define SA2_DKDV_ARGS                                                                         \
   static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),          \
-      static_cast<const T*>(a.dout), a.lse, a.delta, m->col_cnt, m->col_idx, a.N, m->Tq, m->Tk, \
-      a.sl2, a.scale, static_cast<T*>(a.dk), static_cast<T*>(a.dv)
+      static_cast<const T*>(a.dout), a.lse, a.delta, m->col_cnt, m->col_idx, m->col_order, a.N,  \
+      m->Tq, m->Tk, a.sl2, a.scale, static_cast<T*>(a.dk), static_cast<T*>(a.dv)
   if (m->bq == 128) dkdv_kernel<T, D, 128><<<a.BH * m->Tk, 256, 0, a.s>>>(SA2_DKDV_ARGS);
   else dkdv_kernel<T, D, 64><<<a.BH * m->Tk, 256, 0, a.s>>>(SA2_DKDV_ARGS);
 #undef SA2_DKDV_ARGS

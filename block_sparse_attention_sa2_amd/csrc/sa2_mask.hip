@@ -2,12 +2,13 @@
 // section 2A, with Top-p as the smallest set reaching cumulative mass p,
 // section 1).
 //
-// Four kernels on the caller's stream:
+// Kernels on the caller's stream:
 //   pool       q-bar / k-bar: fp64 means of each block's tokens (HBM stream)
 //   score      S-bar = q-bar k-bar^T / sqrt(d), fp64, 64x64 tiles
 //   select     one workgroup per query-block row: softmax, rank, cut, emit
 //              the bitmap row, row count and ascending row list
 //   columns    transposed lists (query blocks per key block), ascending
+//   order      optional work orders (longest lists first)
 // fp64 throughout keeps the ranking and the Top-p cut equal to an exact
 // evaluation except where two scores, or the mass and p, agree to ~1e-15.
 #include <math.h>
@@ -304,6 +305,54 @@ void columns_kernel(const uint8_t* __restrict__ bitmap, int Tq, int Tk,
   if (part == 3) col_cnt[(size_t)bh * Tk + j] = off;
 }
 
+// ---------------------------------------------------------------------------
+// Work orders: row (column) indices sorted by decreasing count, so that the
+// attention kernels start the longest lists first.  One workgroup per order
+// (block 0 rows, block 1 columns) counts, scans and places in LDS; the order
+// among equal counts is whatever the LDS atomics give (it affects scheduling
+// only).
+// ---------------------------------------------------------------------------
+constexpr int kOrderThreads = 1024;
+
+__global__ __launch_bounds__(kOrderThreads)
+void order_kernel(const int32_t* __restrict__ row_cnt, int nrows, int row_max,
+                  const int32_t* __restrict__ col_cnt, int ncols, int col_max,
+                  int32_t* __restrict__ row_order, int32_t* __restrict__ col_order) {
+  __shared__ int hist[kMaxTk + 1];
+  __shared__ int scan[kOrderThreads];
+  const int32_t* cnt = blockIdx.x == 0 ? row_cnt : col_cnt;
+  int32_t* order = blockIdx.x == 0 ? row_order : col_order;
+  const int n = blockIdx.x == 0 ? nrows : ncols;
+  const int nb = (blockIdx.x == 0 ? row_max : col_max) + 1;   // counts 0 .. max
+  const int tid = threadIdx.x;
+  for (int c = tid; c < nb; c += kOrderThreads) hist[c] = 0;
+  __syncthreads();
+  for (int i = tid; i < n; i += kOrderThreads) atomicAdd(&hist[cnt[i]], 1);
+  __syncthreads();
+  // first position of each count in descending-count order
+  const int per = (nb + kOrderThreads - 1) / kOrderThreads;
+  const int lo = tid * per, hi = min(nb, lo + per);   // positions in descending order
+  int local = 0;
+  for (int r = lo; r < hi; ++r) local += hist[nb - 1 - r];
+  scan[tid] = local;
+  __syncthreads();
+  for (int off = 1; off < kOrderThreads; off <<= 1) {
+    const int add = tid >= off ? scan[tid - off] : 0;
+    __syncthreads();
+    scan[tid] += add;
+    __syncthreads();
+  }
+  int run = scan[tid] - local;
+  for (int r = lo; r < hi; ++r) {
+    const int c = nb - 1 - r;
+    const int h = hist[c];
+    hist[c] = run;
+    run += h;
+  }
+  __syncthreads();
+  for (int i = tid; i < n; i += kOrderThreads) order[atomicAdd(&hist[cnt[i]], 1)] = i;
+}
+
 static int next_pow2(int x) {
   int p = 1;
   while (p < x) p <<= 1;
@@ -352,6 +401,7 @@ extern "C" sa2_status sa2_build_mask(const void* q, const void* k, int dtype, in
   if (!m->bitmap || !m->row_cnt || !m->row_idx || !m->col_cnt || !m->col_idx)
     return fail(SA2_EINVAL, "sa2_build_mask: mask array is null");
   if (Tk > kMaxTk) return fail(SA2_EUNSUPPORTED, "sa2_build_mask: more than 4096 key blocks");
+  if (Tq > kMaxTk) return fail(SA2_EUNSUPPORTED, "sa2_build_mask: more than 4096 query blocks");
   const size_t need = sa2_mask_workspace_bytes(B, H, N, d, bq, bk);
   if (ws_bytes < need)
     return fail(SA2_EINVAL, "sa2_build_mask: workspace smaller than sa2_mask_workspace_bytes()");
@@ -363,8 +413,12 @@ extern "C" sa2_status sa2_build_mask(const void* q, const void* k, int dtype, in
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   char* w = static_cast<char*>(ws);
   double* qbar = reinterpret_cast<double*>(w);
-  double* kbar = reinterpret_cast<double*>(w + up((size_t)BH * Tq * d * 8));
-  double* sbar = reinterpret_cast<double*>(w + up((size_t)BH * Tq * d * 8) + up((size_t)BH * Tk * d * 8));
+  w += up((size_t)BH * Tq * d * 8);
+  double* kbar = reinterpret_cast<double*>(w);
+  w += up((size_t)BH * Tk * d * 8);
+  double* sbar = reinterpret_cast<double*>(w);
+  w += up((size_t)BH * Tq * Tk * 8);
+  const bool orders = m->row_order != nullptr && m->col_order != nullptr;
 
   const int nblk = BH * (Tq + Tk);
   if (dtype == SA2_BF16)
@@ -392,5 +446,10 @@ extern "C" sa2_status sa2_build_mask(const void* q, const void* k, int dtype, in
   columns_kernel<<<dim3(cdiv(Tk, 64), BH), 256, 0, s>>>(m->bitmap, Tq, Tk, m->col_cnt,
                                                         m->col_idx);
   if (sa2_status st = check_launch("columns_kernel")) return st;
+  if (orders) {
+    order_kernel<<<2, kOrderThreads, 0, s>>>(m->row_cnt, BH * Tq, Tk, m->col_cnt, BH * Tk, Tq,
+                                             m->row_order, m->col_order);
+    if (sa2_status st = check_launch("order_kernel")) return st;
+  }
   return SA2_OK;
 }

@@ -67,11 +67,18 @@ typedef enum { SA2_BF16 = 0, SA2_F32 = 1 } sa2_dtype;
  *   col_cnt  int32 [B, H, Tk]: query blocks that keep each key block.
  *   col_idx  int32 [B, H, Tk, Tq]: the first col_cnt entries are those query
  *            blocks, ascending (the transposed index the backward walks).
+ *   row_order, col_order  optional (may be NULL) int32 [B*H*Tq], [B*H*Tk]:
+ *            a work order for the attention kernels, the flat (b*H + h)*Tq + i
+ *            (resp. *Tk + j) indices sorted by decreasing row_cnt (col_cnt),
+ *            so that the longest lists start first.  The order among equal
+ *            counts is unspecified; it changes scheduling only, never results.
+ *            When NULL the kernels use a fixed XCD-aware order.
  *
- * sa2_build_mask writes all five arrays; the attention calls read row_cnt /
- * row_idx (forward, dQ) and col_cnt / col_idx (dK, dV).  A caller may supply
- * its own mask to the attention calls as long as the lists are ascending,
- * duplicate-free, in range, and every row_cnt is at least 1.
+ * sa2_build_mask writes all these arrays; the attention calls read row_cnt /
+ * row_idx (forward, dQ) and col_cnt / col_idx (dK, dV), and the orders when
+ * present.  A caller may supply its own mask to the attention calls as long as
+ * the lists are ascending, duplicate-free and in range, every row_cnt is at
+ * least 1, and the orders (if given) are permutations.
  */
 typedef struct sa2_mask {
   int32_t B, H, N, bq, bk, Tq, Tk;
@@ -80,6 +87,8 @@ typedef struct sa2_mask {
   int32_t* row_idx;
   int32_t* col_cnt;
   int32_t* col_idx;
+  int32_t* row_order;
+  int32_t* col_order;
 } sa2_mask;
 
 /* Library version string, e.g. "sa2 0.1.0 gfx950". */
@@ -116,7 +125,7 @@ size_t sa2_mask_workspace_bytes(int B, int H, int N, int d, int bq, int bk);
  * inputs exactly as stored.  mask: geometry fields filled in by the caller
  * (Tq, Tk as above) and all five arrays allocated.  workspace: at least
  * sa2_mask_workspace_bytes(...) bytes of device memory, 256-byte aligned.
- * Limits: Tk <= 4096.  k_frac <= 0 together with p <= 0 (both rules off)
+ * Limits: Tq, Tk <= 4096.  k_frac <= 0 together with p <= 0 (both rules off)
  * is SA2_EINVAL; NaN parameters are SA2_EINVAL.
  */
 sa2_status sa2_build_mask(const void* q, const void* k, int dtype,

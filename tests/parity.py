@@ -84,6 +84,17 @@ def check_lists(bitmap: np.ndarray, row_cnt, row_idx, col_cnt, col_idx):
         assert np.array_equal(col_idx[j, :len(want)], want), f"column {j} list"
 
 
+def check_orders(row_cnt: np.ndarray, col_cnt: np.ndarray, row_order, col_order):
+    """Work orders: permutations of the flat row / column indices with
+    non-increasing counts (the order among equal counts is free)."""
+    for cnt, order in ((row_cnt.reshape(-1), row_order), (col_cnt.reshape(-1), col_order)):
+        if order is None:
+            continue
+        order = np.asarray(order)
+        assert np.array_equal(np.sort(order), np.arange(cnt.size)), "order is not a permutation"
+        assert np.all(np.diff(cnt[order]) <= 0), "order is not by decreasing count"
+
+
 def rel_fro(a: np.ndarray, b: np.ndarray) -> float:
     nb = np.linalg.norm(b)
     return float(np.linalg.norm(a - b) / (nb if nb > 0 else 1.0))

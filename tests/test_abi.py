@@ -44,7 +44,7 @@ def test_workspace_sizes():
 def _mask(B=1, H=1, N=256, bq=64, bk=64):
     Tq, Tk = -(-N // bq), -(-N // bk)
     fake = 1 << 20   # never dereferenced: validation fails first
-    return _lib.Sa2Mask(B, H, N, bq, bk, Tq, Tk, fake, fake, fake, fake, fake)
+    return _lib.Sa2Mask(B, H, N, bq, bk, Tq, Tk, fake, fake, fake, fake, fake, None, None)
 
 
 FAKE = ctypes.c_void_p(1 << 20)

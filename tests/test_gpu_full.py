@@ -25,8 +25,8 @@ import block_sparse_attention_sa2_amd as sa2
 import oracle as O
 import workloads as W
 
-from parity import (GRAD_REL_FRO, check_forward, check_grad, check_lists, compare_mask,
-                    device_inputs, f64, rel_fro)
+from parity import (GRAD_REL_FRO, check_forward, check_grad, check_lists, check_orders,
+                    compare_mask, device_inputs, f64, rel_fro)
 
 pytestmark = pytest.mark.gpu
 
@@ -110,6 +110,7 @@ def test_wan13_mask_all_heads(wan13):
     bm = mask.bitmap.cpu().numpy()
     rc, ri = mask.row_cnt.cpu().numpy(), mask.row_idx.cpu().numpy()
     cc, ci = mask.col_cnt.cpu().numpy(), mask.col_idx.cpu().numpy()
+    check_orders(rc, cc, mask.row_order.cpu().numpy(), mask.col_order.cpu().numpy())
     ties = mass = 0
     for h in range(w.H):
         Q, K = ref["q"][0, h], ref["k"][0, h]

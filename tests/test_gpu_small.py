@@ -18,7 +18,8 @@ import block_sparse_attention_sa2_amd as sa2
 import oracle as O
 import workloads as W
 
-from parity import (check_forward, check_grad, check_lists, compare_mask, device_inputs, f64)
+from parity import (check_forward, check_grad, check_lists, check_orders, compare_mask,
+                    device_inputs, f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -56,6 +57,7 @@ def run_case(w: W.Workload, k_frac: float, p: float, backward: bool = True,
     bm = mask.bitmap.cpu().numpy()
     rc, ri = mask.row_cnt.cpu().numpy(), mask.row_idx.cpu().numpy()
     cc, ci = mask.col_cnt.cpu().numpy(), mask.col_idx.cpu().numpy()
+    check_orders(rc, cc, mask.row_order.cpu().numpy(), mask.col_order.cpu().numpy())
     stats = []
     for b in range(w.B):
         for h in range(w.H):
@@ -166,6 +168,22 @@ def test_reproducible_and_fully_written():
         torch.cuda.synchronize()
         for t in (o, lse, *grads):
             assert torch.isfinite(t).all()
+        outs.append([mask.bitmap.clone(), o, lse, *grads])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+def test_without_work_orders():
+    """With no work orders the kernels use their fixed order: same results."""
+    w = W.Workload("noorder", 1, 2, 1000, 128, 128, 64, "normal", 25, "bf16", 0.1, 0.5)
+    dev, _ = device_inputs(w)
+    q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
+    outs = []
+    for wo in (True, False):
+        mask = sa2.build_mask(q, k, w.bq, w.bk, w.k_frac, w.p, work_order=wo)
+        o, lse = sa2.attn_fwd(q, k, v, mask)
+        grads = sa2.attn_bwd(q, k, v, o, lse, do, mask)
+        torch.cuda.synchronize()
         outs.append([mask.bitmap.clone(), o, lse, *grads])
     for a, b in zip(*outs):
         assert torch.equal(a, b)
