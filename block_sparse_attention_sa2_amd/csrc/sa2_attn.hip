@@ -15,8 +15,8 @@
 // read straight from row-major LDS tiles with ds_read_b64_tr_b16.
 //
 // Backward: dq_kernel first (one workgroup per query block over its row
-// list; it also forms Delta = rowsum(dO * O) for its rows and leaves it in the
-// workspace), then dkdv_kernel (one workgroup per key block, walking the query
+// list; it also forms Delta = rowsum(dO * O) and the log2-scaled LSE of its
+// rows and leaves them in the workspace), then dkdv_kernel (one workgroup per key block, walking the query
 // blocks of its column list; each wave owns a 32-row slice of every listed
 // query block and accumulates the whole 64 x d dK and dV tile, and the four
 // partial tiles are summed in LDS in a fixed order).  No atomics: results are
@@ -246,7 +246,7 @@ void fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
 template <typename T, int D, int BQ>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-                 const T* __restrict__ dout, const float* __restrict__ lse,
+                 const T* __restrict__ dout, const float* __restrict__ lse2,
                  const float* __restrict__ delta, const int32_t* __restrict__ col_cnt,
                  const int32_t* __restrict__ col_idx, const int32_t* __restrict__ order, int N,
                  int Tq, int Tk, float scale_log2, float scale, T* __restrict__ dk,
@@ -294,7 +294,7 @@ void dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
   uint16_t* sd = sq + 32 * ST::kRowElems;                     // this pair's dO slice
   uint16_t* mine = kb == 0 ? sq : sd;              // the half this wave stages
   const T* src = kb == 0 ? q : dout;
-  const float* ssrc = kb == 0 ? lse : delta;
+  const float* ssrc = kb == 0 ? lse2 : delta;
   const int krow = 32 * kb + l32;                  // this lane's row of K, V
 
   f32x16 accv[ND], acck[ND];
@@ -319,7 +319,7 @@ void dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
     for (int kk = 0; kk < NK; ++kk) own[kk] = ok ? load8(p + 16 * kk) : zero8();
     // wave 0: log2-scaled LSE (+inf on padding rows: P = 0); wave 1: Delta
     const float x = ok ? ssrc[(size_t)bh * N + row] : 0.f;
-    stat = kb == 0 ? (ok ? x * kLog2e : INFINITY) : x;
+    stat = kb == 0 ? (ok ? x : INFINITY) : x;
   };
 
   if (steps > 0) fetch(0);
@@ -444,7 +444,7 @@ template <int BQ>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void dkdv_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                        const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
-                       const float* __restrict__ lse, const float* __restrict__ delta,
+                       const float* __restrict__ lse2, const float* __restrict__ delta,
                        const int32_t* __restrict__ col_cnt, const int32_t* __restrict__ col_idx,
                        const int32_t* __restrict__ order, int N, int Tq, int Tk,
                        float scale_log2, float scale, bf16_t* __restrict__ dk,
@@ -493,30 +493,30 @@ void dkdv_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ 
   const int steps = (total + 3) / 4;
 
   // Copy slice g = 4s + pair of step s into buffer b: wave kb = 0 copies Q
-  // and the 32 rows' LSE and Delta, wave kb = 1 copies dO.  Rows past N are
-  // read from row N-1 (their P is zeroed below).
+  // and the 32 rows' log2-scaled LSE and Delta, wave kb = 1 copies dO.  Lane
+  // l's 16 bytes of copy i land in LDS unit 64i + l, which holds row
+  // r = 4i + l/16 and logical unit (l % 16) ^ swz(r).  Rows past N are read
+  // from row N-1 (their P is zeroed below).
+  const bf16_t* src = (kb == 0 ? q : dout) + base;
+  const float* ssrc = (h == 0 ? lse2 : delta) + (size_t)bh * N;
   auto copy_step = [&](int s, int b) {
     const int g = 4 * s + pair;
     if (g >= total) return;
     const int row0 = lst[g / SUB] * BQ + 32 * (g % SUB);
-    const bf16_t* src = (kb == 0 ? q : dout) + base;
     uint16_t* dst = stage + ((b * 4 + pair) * 2 + kb) * SLICE;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int r = 4 * i + (lane >> 4);
       const int sw = ((r & 3) << 2) | ((r >> 2) & 3);
-      const int u = (lane & 15) ^ sw;          // the logical unit this lane's LDS unit holds
       const int row = min(row0 + r, N - 1);
       __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(src + (size_t)row * D + 8 * u),
+          (const __attribute__((address_space(1))) void*)(src + row * D + 8 * ((lane & 15) ^ sw)),
           (__attribute__((address_space(3))) void*)(dst + i * 512), 16, 0, 0);
     }
     if (kb == 0) {
-      const int rr = min(row0 + l32, N - 1);
-      const float* sp = (h == 0 ? lse : delta) + (size_t)bh * N + rr;
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)sp,
-                                       (__attribute__((address_space(3))) void*)(stats + (b * 4 + pair) * 64),
-                                       4, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(ssrc + min(row0 + l32, N - 1)),
+          (__attribute__((address_space(3))) void*)(stats + (b * 4 + pair) * 64), 4, 0, 0);
     }
   };
 
@@ -551,26 +551,29 @@ void dkdv_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ 
       // P and dS for rows 8g+4h+i, packed into the B operands of the two
       // 16-row steps (keys past N need no mask: they only feed their own,
       // unstored, dK and dV rows)
+      if (row0 + 32 > N) {  // the partial last query block: rows past N add nothing
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (row0 + 8 * (e >> 2) + 4 * h + (e & 3) >= N) sa[e] = -INFINITY;
+      }
       bf16x8 pb[2], sb[2];
 #pragma unroll
       for (int gg = 0; gg < 4; ++gg) {
         const f32x4 L = *reinterpret_cast<const f32x4*>(stl + 8 * gg + 4 * h);
         const f32x4 Dl = *reinterpret_cast<const f32x4*>(stl + 32 + 8 * gg + 4 * h);
+        float pv[4], ds[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int e = 4 * gg + i;
-          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[e], scale_log2, -L[i] * kLog2e));
-          pb[gg >> 1][4 * (gg & 1) + i] = (__bf16)pv;
-          sb[gg >> 1][4 * (gg & 1) + i] = (__bf16)(pv * (dpa[e] - Dl[i]));
+          pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[e], scale_log2, -L[i]));
+          ds[i] = pv[i] * (dpa[e] - Dl[i]);
         }
-      }
-      if (row0 + 32 > N) {  // the partial last query block: rows past N add nothing
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (row0 + 8 * (e >> 2) + 4 * h + (e & 3) >= N) {
-            pb[e >> 3][e & 7] = (__bf16)0.f;
-            sb[e >> 3][e & 7] = (__bf16)0.f;
-          }
+        // two packed conversions per four values
+        const int t = gg >> 1, o = 4 * (gg & 1);
+        pb[t][o] = (__bf16)pv[0]; pb[t][o + 1] = (__bf16)pv[1];
+        pb[t][o + 2] = (__bf16)pv[2]; pb[t][o + 3] = (__bf16)pv[3];
+        sb[t][o] = (__bf16)ds[0]; sb[t][o + 1] = (__bf16)ds[1];
+        sb[t][o + 2] = (__bf16)ds[2]; sb[t][o + 3] = (__bf16)ds[3];
       }
       // dV^T += dO^T P and dK^T += Q^T dS over the slice's rows
 #pragma unroll
@@ -633,7 +636,8 @@ template <typename T, int D, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4 ? 2 : 1, 2)))
 void dq_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                const T* __restrict__ o, const T* __restrict__ dout, const float* __restrict__ lse,
-               float* __restrict__ delta, const int32_t* __restrict__ row_cnt,
+               float* __restrict__ delta, float* __restrict__ lse2,
+               const int32_t* __restrict__ row_cnt,
                const int32_t* __restrict__ row_idx, const int32_t* __restrict__ order, int N,
                int Tq, int Tk, float scale_log2, float scale, T* __restrict__ dq) {
   constexpr int NT = NW * 64;
@@ -673,8 +677,11 @@ void dq_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __rest
   // of the row.  It is kept for the dK/dV kernel.  Padding rows: dO = 0 and
   // Delta = 0 give dS = 0 whatever P is.
   const float dl = dpart + __shfl_xor(dpart, 32);
-  if (qvalid && h == 0) delta[(size_t)bh * N + qrow] = dl;
   const float l2 = qvalid ? lse[(size_t)bh * N + qrow] * kLog2e : 0.f;
+  if (qvalid && h == 0) {
+    delta[(size_t)bh * N + qrow] = dl;
+    lse2[(size_t)bh * N + qrow] = l2;
+  }
 
   f32x16 acc[ND];
 #pragma unroll
@@ -698,39 +705,37 @@ void dq_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __rest
       fetch_tile<T, D, NT>(kh, nk0, N, tid, kr);
       fetch_tile<T, D, NT>(vh, nk0, N, tid, vr);
     }
-    f32x16 s[2], dp[2];
+    // the two 32-key halves one after the other, so that only one half's S
+    // and dP are live at a time
+    const bool tail = key0 + 64 > N;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      s[b] = zero16();
-      dp[b] = zero16();
+      f32x16 sb = zero16(), dpb = zero16();
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
         const int c = 16 * kk + 8 * h;
-        s[b] = mfma32(lds_read8(k_lds + KT::off(32 * b + l32, c)), qf[kk], s[b]);
-        dp[b] = mfma32(lds_read8(v_lds + VT::off(32 * b + l32, c)), df[kk], dp[b]);
+        sb = mfma32(lds_read8(k_lds + KT::off(32 * b + l32, c)), qf[kk], sb);
+        dpb = mfma32(lds_read8(v_lds + VT::off(32 * b + l32, c)), df[kk], dpb);
       }
-    }
-    // dS = P * (dP - Delta)
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
+      // dS = P * (dP - Delta)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][e], scale_log2, -l2));
-        s[b][e] = pv * (dp[b][e] - dl);
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[e], scale_log2, -l2));
+        sb[e] = pv * (dpb[e] - dl);
       }
-    if (key0 + 64 > N) {  // keys past N enter the dQ contraction: zero them
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
+      if (tail) {  // keys past N enter the dQ contraction: zero them
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-          if (key0 + 32 * b + 8 * (e >> 2) + 4 * h + (e & 3) >= N) s[b][e] = 0.f;
-    }
+          if (key0 + 32 * b + 8 * (e >> 2) + 4 * h + (e & 3) >= N) sb[e] = 0.f;
+      }
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      const bf16x8 sf = pack8(s[tt >> 1], 8 * (tt & 1));
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const bf16x8 sf = pack8(sb, 8 * t2);
 #pragma unroll
-      for (int db = 0; db < ND; ++db)
-        acc[db] = mfma32(tr_operand<D, kPad16>(k_lds, 16 * tt, 32 * db, lane), sf, acc[db]);
+        for (int db = 0; db < ND; ++db)
+          acc[db] = mfma32(tr_operand<D, kPad16>(k_lds, 32 * b + 16 * t2, 32 * db, lane), sf,
+                           acc[db]);
+      }
     }
   }
   if (qvalid) {
@@ -789,6 +794,7 @@ struct BwdArgs {
   float sl2, scale;
   void *dq, *dk, *dv;
   float* delta;
+  float* lse2;
   hipStream_t s;
 };
 
@@ -797,7 +803,8 @@ static void launch_dq(const BwdArgs& a) {
   const sa2_mask* m = a.m;
 #define SA2_DQ_ARGS                                                                          \
   static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),          \
-      static_cast<const T*>(a.o), static_cast<const T*>(a.dout), a.lse, a.delta, m->row_cnt,  \
+      static_cast<const T*>(a.o), static_cast<const T*>(a.dout), a.lse, a.delta, a.lse2,      \
+      m->row_cnt,                                                                             \
       m->row_idx, m->row_order, a.N, m->Tq, m->Tk, a.sl2, a.scale, static_cast<T*>(a.dq)
   if (m->bq == 128) dq_kernel<T, D, 4><<<a.BH * m->Tq, 256, 0, a.s>>>(SA2_DQ_ARGS);
   else dq_kernel<T, D, 2><<<a.BH * m->Tq, 128, 0, a.s>>>(SA2_DQ_ARGS);
@@ -810,7 +817,7 @@ static void launch_dkdv(const BwdArgs& a) {
   if constexpr (D == 128 && sizeof(T) == 2) {
 #define SA2_DKDV_ASYNC_ARGS                                                                  \
   static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k),                            \
-      static_cast<const bf16_t*>(a.v), static_cast<const bf16_t*>(a.dout), a.lse, a.delta,     \
+      static_cast<const bf16_t*>(a.v), static_cast<const bf16_t*>(a.dout), a.lse2, a.delta,    \
       m->col_cnt, m->col_idx, m->col_order, a.N, m->Tq, m->Tk, a.sl2, a.scale,                 \
       static_cast<bf16_t*>(a.dk), static_cast<bf16_t*>(a.dv)
     if (m->bq == 128) dkdv_async_kernel<128><<<a.BH * m->Tk, 512, 0, a.s>>>(SA2_DKDV_ASYNC_ARGS);
@@ -820,7 +827,7 @@ static void launch_dkdv(const BwdArgs& a) {
   }
 #define SA2_DKDV_ARGS                                                                         \
   static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),          \
-      static_cast<const T*>(a.dout), a.lse, a.delta, m->col_cnt, m->col_idx, m->col_order, a.N,  \
+      static_cast<const T*>(a.dout), a.lse2, a.delta, m->col_cnt, m->col_idx, m->col_order, a.N, \
       m->Tq, m->Tk, a.sl2, a.scale, static_cast<T*>(a.dk), static_cast<T*>(a.dv)
   if (m->bq == 128) dkdv_kernel<T, D, 128><<<a.BH * m->Tk, 256, 0, a.s>>>(SA2_DKDV_ARGS);
   else dkdv_kernel<T, D, 64><<<a.BH * m->Tk, 256, 0, a.s>>>(SA2_DKDV_ARGS);
@@ -853,13 +860,18 @@ static sa2_status check_bwd(const char* fn, const void* q, const void* k, const 
   return SA2_OK;
 }
 
+static size_t bwd_half_bytes(int B, int H, int N) {
+  return ((size_t)B * H * N * 4 + 255) & ~(size_t)255;
+}
+
 static BwdArgs bwd_args(const void* q, const void* k, const void* v, const void* o,
                         const float* lse, const void* dout, int B, int H, int N, int d,
                         const sa2_mask* m, void* dq, void* dk, void* dv, void* ws, void* stream) {
   const double sc = 1.0 / sqrt((double)d);
+  float* delta = static_cast<float*>(ws);
+  float* lse2 = reinterpret_cast<float*>(static_cast<char*>(ws) + bwd_half_bytes(B, H, N));
   return BwdArgs{q, k, v, o, dout, lse, m, B * H, N, (float)(1.4426950408889634 * sc),
-                 (float)sc, dq, dk, dv, static_cast<float*>(ws),
-                 reinterpret_cast<hipStream_t>(stream)};
+                 (float)sc, dq, dk, dv, delta, lse2, reinterpret_cast<hipStream_t>(stream)};
 }
 
 }  // namespace sa2
@@ -889,7 +901,7 @@ extern "C" sa2_status sa2_attn_fwd(const void* q, const void* k, const void* v, 
 
 extern "C" size_t sa2_bwd_workspace_bytes(int B, int H, int N, int d) {
   if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return 0;
-  return ((size_t)B * H * N * 4 + 255) & ~(size_t)255;
+  return 2 * (((size_t)B * H * N * 4 + 255) & ~(size_t)255);
 }
 
 extern "C" sa2_status sa2_attn_bwd_dq(const void* q, const void* k, const void* v,

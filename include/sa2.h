@@ -151,8 +151,9 @@ sa2_status sa2_attn_fwd(const void* q, const void* k, const void* v, int dtype,
                         void* o, float* lse, void* stream);
 
 /*
- * Bytes of device workspace the backward calls need: one fp32 per token
- * (B*H*N floats, the row sums Delta_t = sum_c dO_tc * O_tc).
+ * Bytes of device workspace the backward calls need: two fp32 per token
+ * (2*B*H*N floats, each half rounded up to 256 bytes): the row sums
+ * Delta_t = sum_c dO_tc * O_tc and the LSE in base 2 (lse_t * log2(e)).
  */
 size_t sa2_bwd_workspace_bytes(int B, int H, int N, int d);
 
@@ -181,8 +182,8 @@ sa2_status sa2_attn_bwd(const void* q, const void* k, const void* v,
 
 /*
  * First half of sa2_attn_bwd: dQ = dS K / sqrt(d) over each query block's
- * row list, and Delta_t = sum_c dO_tc O_tc, which it leaves in `workspace`
- * (fp32 [B, H, N]) for sa2_attn_bwd_dkdv.  Arguments as for sa2_attn_bwd.
+ * row list, and Delta_t = sum_c dO_tc O_tc and lse_t * log2(e), which it
+ * leaves in `workspace` for sa2_attn_bwd_dkdv.  Arguments as for sa2_attn_bwd.
  */
 sa2_status sa2_attn_bwd_dq(const void* q, const void* k, const void* v,
                            const void* o, const float* lse, const void* dout,
@@ -192,7 +193,8 @@ sa2_status sa2_attn_bwd_dq(const void* q, const void* k, const void* v,
 
 /*
  * Second half of sa2_attn_bwd: dV = P^T dO and dK = dS^T Q / sqrt(d) over
- * each key block's column list.  Reads Delta from `workspace`, so it must
+ * each key block's column list.  Reads Delta and the base-2 LSE from
+ * `workspace` (lse itself is still checked), so it must
  * follow sa2_attn_bwd_dq on the same inputs, mask and workspace, on the same
  * stream (or after it completes).  Arguments as for sa2_attn_bwd.
  */
