@@ -232,6 +232,254 @@ void fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
 }
 
 // ---------------------------------------------------------------------------
+// Asynchronous K/V tile copies (bf16, d = 128).  A 64-key tile of K and of V
+// (16 KB each, rows of 256 bytes in the permuted kBoth layout) is copied
+// global -> LDS with global_load_lds: lane l's 16 bytes of copy i land in LDS
+// unit 64i + l, i.e. row 4i + l/16, and the lane loads the logical unit
+// (l % 16) ^ swz(row) of that row.  Each of the NW waves copies 16 / NW
+// four-row groups of each tensor.  Keys past N are read from row N-1; the
+// kernels mask or zero them.
+// ---------------------------------------------------------------------------
+template <int NW>
+__device__ inline void copy_kv_tile(const bf16_t* __restrict__ kh, const bf16_t* __restrict__ vh,
+                                    int key0, int N, uint16_t* kdst, uint16_t* vdst, int w,
+                                    int lane) {
+  constexpr int D = 128, PER = 16 / NW;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = w * PER + j;                 // copy index 0..15 within the tile
+    const int r = 4 * i + (lane >> 4);
+    const int sw = ((r & 3) << 2) | ((r >> 2) & 3);
+    const int row = min(key0 + r, N - 1);
+    const int off = row * D + 8 * ((lane & 15) ^ sw);
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kh + off),
+                                     (__attribute__((address_space(3))) void*)(kdst + i * 512),
+                                     16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vh + off),
+                                     (__attribute__((address_space(3))) void*)(vdst + i * 512),
+                                     16, 0, 0);
+  }
+}
+
+// Forward for bf16 and d = 128 with double-buffered asynchronous K/V tiles:
+// one workgroup barrier per tile, after which this tile's copy has landed
+// (every wave waits for its own first) and the other buffer is free for the
+// next tile's copy.
+template <int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4 ? 2 : 1, 2)))
+void fwd_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                      const bf16_t* __restrict__ v, const int32_t* __restrict__ row_cnt,
+                      const int32_t* __restrict__ row_idx, const int32_t* __restrict__ order,
+                      int N, int Tq, int Tk, float scale_log2, bf16_t* __restrict__ o,
+                      float* __restrict__ lse) {
+  constexpr int D = 128;
+  using KT = Tile<D, kBoth>;
+  constexpr int NK = D / 16, ND = D / 32;
+  constexpr int TILE = 64 * D;
+  __shared__ __attribute__((aligned(16))) uint16_t kbuf[2 * TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t vbuf[2 * TILE];
+
+  const int wg = order ? order[blockIdx.x] : xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = wg / Tq, qi = wg % Tq;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const size_t base = (size_t)bh * N * D;
+  const bf16_t* kh = k + base;
+  const bf16_t* vh = v + base;
+  const int qrow = qi * (NW * 32) + w * 32 + l32;
+  const bool qvalid = qrow < N;
+
+  bf16x8 qf[NK];
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk)
+    qf[kk] = qvalid ? load8(q + base + (size_t)qrow * D + 16 * kk + 8 * h) : zero8();
+
+  f32x16 acc[ND];
+#pragma unroll
+  for (int db = 0; db < ND; ++db) acc[db] = zero16();
+  float m = -INFINITY, lsum = 0.f;
+
+  const int cnt = row_cnt[wg];
+  const int32_t* lst = row_idx + (size_t)wg * Tk;
+  if (cnt > 0) copy_kv_tile<NW>(kh, vh, lst[0] * 64, N, kbuf, vbuf, w, lane);
+  for (int t = 0; t < cnt; ++t) {
+    const int key0 = lst[t] * 64;
+    const uint16_t* kt = kbuf + (t & 1) * TILE;
+    const uint16_t* vt = vbuf + (t & 1) * TILE;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (t + 1 < cnt)
+      copy_kv_tile<NW>(kh, vh, lst[t + 1] * 64, N, kbuf + ((t + 1) & 1) * TILE,
+                       vbuf + ((t + 1) & 1) * TILE, w, lane);
+    f32x16 s[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      s[b] = zero16();
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk)
+        s[b] = mfma32(lds_read8(kt + KT::off(32 * b + l32, 16 * kk + 8 * h)), qf[kk], s[b]);
+    }
+    if (key0 + 64 > N) {  // the partial last key block (a uniform branch)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (key0 + 32 * b + 8 * (e >> 2) + 4 * h + (e & 3) >= N) s[b][e] = -INFINITY;
+    }
+    float mx = s[0][0];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[b][e]);
+    mx = wave_max32(mx) * scale_log2;
+    if (__any(mx > m + kRescaleThreshold)) {
+      const float mnew = fmaxf(m, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+      m = mnew;
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < ND; ++db) acc[db] *= alpha;
+    }
+    float ps = 0.f;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][e], scale_log2, -m));
+        s[b][e] = pv;
+        ps += pv;
+      }
+    lsum += ps;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const bf16x8 pf = pack8(s[tt >> 1], 8 * (tt & 1));
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+        acc[db] = mfma32(tr_operand<D, kBoth>(vt, 16 * tt, 32 * db, lane), pf, acc[db]);
+    }
+  }
+  const float ltot = lsum + __shfl_xor(lsum, 32);
+  const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+  if (qvalid) {
+    bf16_t* orow = o + base + (size_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        store4(orow + 32 * db + 8 * g + 4 * h, acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv,
+               acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv);
+    if (h == 0)
+      lse[(size_t)bh * N + qrow] = ltot > 0.f ? (m + __log2f(ltot)) * kLn2 : -INFINITY;
+  }
+}
+
+// dQ for bf16 and d = 128 with the same double-buffered asynchronous tiles.
+template <int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4 ? 2 : 1, 2)))
+void dq_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                     const bf16_t* __restrict__ v, const bf16_t* __restrict__ o,
+                     const bf16_t* __restrict__ dout, const float* __restrict__ lse,
+                     float* __restrict__ delta, float* __restrict__ lse2,
+                     const int32_t* __restrict__ row_cnt, const int32_t* __restrict__ row_idx,
+                     const int32_t* __restrict__ order, int N, int Tq, int Tk, float scale_log2,
+                     float scale, bf16_t* __restrict__ dq) {
+  constexpr int D = 128;
+  using KT = Tile<D, kBoth>;
+  constexpr int NK = D / 16, ND = D / 32;
+  constexpr int TILE = 64 * D;
+  __shared__ __attribute__((aligned(16))) uint16_t kbuf[2 * TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t vbuf[2 * TILE];
+
+  const int wg = order ? order[blockIdx.x] : xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = wg / Tq, qi = wg % Tq;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const size_t base = (size_t)bh * N * D;
+  const bf16_t* kh = k + base;
+  const bf16_t* vh = v + base;
+  const int qrow = qi * (NW * 32) + w * 32 + l32;
+  const bool qvalid = qrow < N;
+
+  bf16x8 qf[NK], df[NK];
+  float dpart = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk) {
+    const size_t off = base + (size_t)qrow * D + 16 * kk + 8 * h;
+    qf[kk] = qvalid ? load8(q + off) : zero8();
+    df[kk] = qvalid ? load8(dout + off) : zero8();
+    if (qvalid) {
+      float a[8], b[8];
+      load8_f32(o + off, a);
+      load8_f32(dout + off, b);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dpart += a[i] * b[i];
+    }
+  }
+  const float dl = dpart + __shfl_xor(dpart, 32);
+  const float l2 = qvalid ? lse[(size_t)bh * N + qrow] * kLog2e : 0.f;
+  if (qvalid && h == 0) {
+    delta[(size_t)bh * N + qrow] = dl;
+    lse2[(size_t)bh * N + qrow] = l2;
+  }
+
+  f32x16 acc[ND];
+#pragma unroll
+  for (int db = 0; db < ND; ++db) acc[db] = zero16();
+
+  const int cnt = row_cnt[wg];
+  const int32_t* lst = row_idx + (size_t)wg * Tk;
+  if (cnt > 0) copy_kv_tile<NW>(kh, vh, lst[0] * 64, N, kbuf, vbuf, w, lane);
+  for (int t = 0; t < cnt; ++t) {
+    const int key0 = lst[t] * 64;
+    const uint16_t* kt = kbuf + (t & 1) * TILE;
+    const uint16_t* vt = vbuf + (t & 1) * TILE;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (t + 1 < cnt)
+      copy_kv_tile<NW>(kh, vh, lst[t + 1] * 64, N, kbuf + ((t + 1) & 1) * TILE,
+                       vbuf + ((t + 1) & 1) * TILE, w, lane);
+    const bool tail = key0 + 64 > N;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      f32x16 sb = zero16(), dpb = zero16();
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        const int c = 16 * kk + 8 * h;
+        sb = mfma32(lds_read8(kt + KT::off(32 * b + l32, c)), qf[kk], sb);
+        dpb = mfma32(lds_read8(vt + KT::off(32 * b + l32, c)), df[kk], dpb);
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[e], scale_log2, -l2));
+        sb[e] = pv * (dpb[e] - dl);
+      }
+      if (tail) {  // keys past N enter the dQ contraction: zero them
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (key0 + 32 * b + 8 * (e >> 2) + 4 * h + (e & 3) >= N) sb[e] = 0.f;
+      }
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const bf16x8 sf = pack8(sb, 8 * t2);
+#pragma unroll
+        for (int db = 0; db < ND; ++db)
+          acc[db] = mfma32(tr_operand<D, kBoth>(kt, 32 * b + 16 * t2, 32 * db, lane), sf,
+                           acc[db]);
+      }
+    }
+  }
+  if (qvalid) {
+    bf16_t* row = dq + base + (size_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        store4(row + 32 * db + 8 * g + 4 * h, acc[db][4 * g] * scale, acc[db][4 * g + 1] * scale,
+               acc[db][4 * g + 2] * scale, acc[db][4 * g + 3] * scale);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Backward dK, dV: one workgroup (4 waves) per key block of 64 keys.
 //
 // Waves form two pairs.  Pair p walks the 32-row slices 2j + p of every
@@ -779,9 +1027,23 @@ static void launch_fwd(const void* q, const void* k, const void* v, const sa2_ma
       m->row_idx, m->row_order, N, m->Tq, m->Tk, sl2, static_cast<T*>(o), lse);
 }
 
+template <int NW>
+static void launch_fwd_async(const void* q, const void* k, const void* v, const sa2_mask* m,
+                             int BH, int N, float sl2, void* o, float* lse, hipStream_t s) {
+  fwd_async_kernel<NW><<<BH * m->Tq, NW * 64, 0, s>>>(
+      static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
+      static_cast<const bf16_t*>(v), m->row_cnt, m->row_idx, m->row_order, N, m->Tq, m->Tk, sl2,
+      static_cast<bf16_t*>(o), lse);
+}
+
 template <typename T, int D>
 static void dispatch_fwd(const void* q, const void* k, const void* v, const sa2_mask* m, int BH,
                          int N, float sl2, void* o, float* lse, hipStream_t s) {
+  if constexpr (D == 128 && sizeof(T) == 2) {
+    if (m->bq == 128) launch_fwd_async<4>(q, k, v, m, BH, N, sl2, o, lse, s);
+    else launch_fwd_async<2>(q, k, v, m, BH, N, sl2, o, lse, s);
+    return;
+  }
   if (m->bq == 128) launch_fwd<T, D, 4>(q, k, v, m, BH, N, sl2, o, lse, s);
   else launch_fwd<T, D, 2>(q, k, v, m, BH, N, sl2, o, lse, s);
 }
@@ -801,6 +1063,17 @@ struct BwdArgs {
 template <typename T, int D>
 static void launch_dq(const BwdArgs& a) {
   const sa2_mask* m = a.m;
+  if constexpr (D == 128 && sizeof(T) == 2) {
+#define SA2_DQ_ASYNC_ARGS                                                                     \
+  static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k),                            \
+      static_cast<const bf16_t*>(a.v), static_cast<const bf16_t*>(a.o),                        \
+      static_cast<const bf16_t*>(a.dout), a.lse, a.delta, a.lse2, m->row_cnt, m->row_idx,      \
+      m->row_order, a.N, m->Tq, m->Tk, a.sl2, a.scale, static_cast<bf16_t*>(a.dq)
+    if (m->bq == 128) dq_async_kernel<4><<<a.BH * m->Tq, 256, 0, a.s>>>(SA2_DQ_ASYNC_ARGS);
+    else dq_async_kernel<2><<<a.BH * m->Tq, 128, 0, a.s>>>(SA2_DQ_ASYNC_ARGS);
+#undef SA2_DQ_ASYNC_ARGS
+    return;
+  }
 #define SA2_DQ_ARGS                                                                          \
   static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),          \
       static_cast<const T*>(a.o), static_cast<const T*>(a.dout), a.lse, a.delta, a.lse2,      \
