@@ -177,11 +177,12 @@ void fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
         s[b] = mfma32(lds_read8(k_lds + KT::off(32 * b + l32, 16 * kk + 8 * h)), qf[kk], s[b]);
     }
     if (key0 + 64 > N) {  // the partial last key block (a uniform branch)
+      const int lim = N - key0 - 4 * h;   // keys of this lane at offsets >= lim are past N
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-          if (key0 + 32 * b + 8 * (e >> 2) + 4 * h + (e & 3) >= N) s[b][e] = -INFINITY;
+          if (32 * b + 8 * (e >> 2) + (e & 3) >= lim) s[b][e] = -INFINITY;
     }
     float mx = s[0][0];
 #pragma unroll
@@ -232,39 +233,66 @@ void fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
 }
 
 // ---------------------------------------------------------------------------
-// Asynchronous K/V tile copies (bf16, d = 128).  A 64-key tile of K and of V
-// (16 KB each, rows of 256 bytes in the permuted kBoth layout) is copied
-// global -> LDS with global_load_lds: lane l's 16 bytes of copy i land in LDS
-// unit 64i + l, i.e. row 4i + l/16, and the lane loads the logical unit
-// (l % 16) ^ swz(row) of that row.  Each of the NW waves copies 16 / NW
-// four-row groups of each tensor.  Keys past N are read from row N-1; the
-// kernels mask or zero them.
+// Asynchronous tile copies (bf16, d = 128), global -> LDS through buffer
+// resources.  Rows of 256 bytes are copied in groups of four: lane l's 16
+// bytes of group i land in LDS unit 64i + l, i.e. row 4i + l/16 and unit
+// l % 16, which in the permuted kBoth layout holds the logical unit
+// (l % 16) ^ swz(row).  swz(4i + l/16) = 4(l/16) + i % 4, so the lane's
+// source offset within its group depends only on i % 4: four per-lane
+// constants (unit_offsets) and an immediate 1024 (i % 4) serve every copy.
+// Rows past N read as zeros (the resource ends at row N).
 // ---------------------------------------------------------------------------
-template <int NW>
-__device__ inline void copy_kv_tile(const bf16_t* __restrict__ kh, const bf16_t* __restrict__ vh,
-                                    int key0, int N, uint16_t* kdst, uint16_t* vdst, int w,
-                                    int lane) {
-  constexpr int D = 128, PER = 16 / NW;
+__device__ inline void unit_offsets(int lane, uint32_t* uo) {
+  const int rr = lane >> 4;
 #pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int i = w * PER + j;                 // copy index 0..15 within the tile
-    const int r = 4 * i + (lane >> 4);
-    const int sw = ((r & 3) << 2) | ((r >> 2) & 3);
-    const int row = min(key0 + r, N - 1);
-    const int off = row * D + 8 * ((lane & 15) ^ sw);
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kh + off),
-                                     (__attribute__((address_space(3))) void*)(kdst + i * 512),
-                                     16, 0, 0);
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vh + off),
-                                     (__attribute__((address_space(3))) void*)(vdst + i * 512),
-                                     16, 0, 0);
+  for (int j = 0; j < 4; ++j) uo[j] = rr * 256 + 16 * ((lane & 15) ^ ((rr << 2) | j));
+}
+
+// Groups g0 .. g0+4G-1 of the rows starting at row0 of a head (256-byte
+// rows), into dst (the tile's LDS base).  g0 and row0 are wave-uniform.
+template <int G>
+__device__ inline void copy_groups(rsrc_t r, int row0, int g0, uint16_t* dst,
+                                   const uint32_t* uo) {
+  static_for<0, G>([&](auto jj) {
+    constexpr int J = decltype(jj)::value;
+    const int g = g0 + 4 * J;
+    const uint32_t soff = (uint32_t)(row0 + 4 * g) * 256u;
+    uint16_t* d = dst + g * 512;
+    static_for<0, 4>([&](auto ii) {
+      constexpr int I = decltype(ii)::value;
+      buf_lds16<1024 * I>(r, d, uo[I], soff);
+    });
+  });
+}
+
+// A 64-key tile of K and of V: each of the NW waves copies 16 / NW groups.
+template <int NW>
+__device__ inline void copy_kv_tile(rsrc_t rk, rsrc_t rv, int key0, uint16_t* kdst,
+                                    uint16_t* vdst, int w, const uint32_t* uo) {
+  constexpr int PER = 16 / NW;
+  static_assert(PER % 4 == 0, "a wave copies whole runs of four groups");
+  copy_groups<PER / 4>(rk, key0, w * PER, kdst, uo);
+  copy_groups<PER / 4>(rv, key0, w * PER, vdst, uo);
+}
+
+// Double buffering of asynchronous copies.  The two buffers are separate LDS
+// arrays and the tile loop is unrolled by two, so that each step names its
+// buffers statically: the compiler then sees that the copy in flight (into
+// the other array) cannot alias this step's LDS reads and does not wait for
+// it.  With one array indexed by the step parity it would wait for the copy
+// before the first read, which serialises copy and compute.  One workgroup
+// barrier per step: after it, every wave's copy for this step has landed
+// (each waits for its own first) and every wave is done with the other
+// buffer, which then receives the next copy.
+template <typename F>
+__device__ inline void double_buffered(int cnt, F&& step) {
+  for (int t = 0; t < cnt; t += 2) {
+    step(t, Int<0>{});
+    if (t + 1 < cnt) step(t + 1, Int<1>{});
   }
 }
 
-// Forward for bf16 and d = 128 with double-buffered asynchronous K/V tiles:
-// one workgroup barrier per tile, after which this tile's copy has landed
-// (every wave waits for its own first) and the other buffer is free for the
-// next tile's copy.
+// Forward for bf16 and d = 128 with double-buffered asynchronous K/V tiles.
 template <int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4 ? 2 : 1, 2)))
 void fwd_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
@@ -276,16 +304,18 @@ void fwd_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
   using KT = Tile<D, kBoth>;
   constexpr int NK = D / 16, ND = D / 32;
   constexpr int TILE = 64 * D;
-  __shared__ __attribute__((aligned(16))) uint16_t kbuf[2 * TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t vbuf[2 * TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t kbuf0[TILE], kbuf1[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t vbuf0[TILE], vbuf1[TILE];
 
   const int wg = order ? order[blockIdx.x] : xcd_remap(blockIdx.x, gridDim.x);
   const int bh = wg / Tq, qi = wg % Tq;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
   const int h = lane >> 5, l32 = lane & 31;
   const size_t base = (size_t)bh * N * D;
-  const bf16_t* kh = k + base;
-  const bf16_t* vh = v + base;
+  const rsrc_t rk = make_rsrc(k + base, (uint32_t)N * D * 2);
+  const rsrc_t rv = make_rsrc(v + base, (uint32_t)N * D * 2);
+  uint32_t uo[4];
+  unit_offsets(lane, uo);
   const int qrow = qi * (NW * 32) + w * 32 + l32;
   const bool qvalid = qrow < N;
 
@@ -299,18 +329,24 @@ void fwd_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
   for (int db = 0; db < ND; ++db) acc[db] = zero16();
   float m = -INFINITY, lsum = 0.f;
 
+  // the list is walked with scalar loads, one entry ahead of its copy
   const int cnt = row_cnt[wg];
   const int32_t* lst = row_idx + (size_t)wg * Tk;
-  if (cnt > 0) copy_kv_tile<NW>(kh, vh, lst[0] * 64, N, kbuf, vbuf, w, lane);
-  for (int t = 0; t < cnt; ++t) {
-    const int key0 = lst[t] * 64;
-    const uint16_t* kt = kbuf + (t & 1) * TILE;
-    const uint16_t* vt = vbuf + (t & 1) * TILE;
+  int key_cur = cnt > 0 ? lst[0] * 64 : 0;
+  if (cnt > 0) copy_kv_tile<NW>(rk, rv, key_cur, kbuf0, vbuf0, w, uo);
+  int key_nxt = cnt > 1 ? lst[1] * 64 : 0;
+
+  double_buffered(cnt, [&](int t, auto parity) {
+    constexpr bool odd = decltype(parity)::value == 1;
+    const uint16_t* kt = odd ? kbuf1 : kbuf0;
+    const uint16_t* vt = odd ? vbuf1 : vbuf0;
+    const int key0 = key_cur;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (t + 1 < cnt)
-      copy_kv_tile<NW>(kh, vh, lst[t + 1] * 64, N, kbuf + ((t + 1) & 1) * TILE,
-                       vbuf + ((t + 1) & 1) * TILE, w, lane);
+    if (t + 1 < cnt) copy_kv_tile<NW>(rk, rv, key_nxt, odd ? kbuf0 : kbuf1, odd ? vbuf0 : vbuf1, w, uo);
+    key_cur = key_nxt;
+    if (t + 2 < cnt) key_nxt = lst[t + 2] * 64;
+
     f32x16 s[2];
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
@@ -320,11 +356,12 @@ void fwd_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
         s[b] = mfma32(lds_read8(kt + KT::off(32 * b + l32, 16 * kk + 8 * h)), qf[kk], s[b]);
     }
     if (key0 + 64 > N) {  // the partial last key block (a uniform branch)
+      const int lim = N - key0 - 4 * h;   // keys of this lane at offsets >= lim are past N
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-          if (key0 + 32 * b + 8 * (e >> 2) + 4 * h + (e & 3) >= N) s[b][e] = -INFINITY;
+          if (32 * b + 8 * (e >> 2) + (e & 3) >= lim) s[b][e] = -INFINITY;
     }
     float mx = s[0][0];
 #pragma unroll
@@ -357,7 +394,8 @@ void fwd_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
       for (int db = 0; db < ND; ++db)
         acc[db] = mfma32(tr_operand<D, kBoth>(vt, 16 * tt, 32 * db, lane), pf, acc[db]);
     }
-  }
+  });
+
   const float ltot = lsum + __shfl_xor(lsum, 32);
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
   if (qvalid) {
@@ -379,24 +417,26 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4
 void dq_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                      const bf16_t* __restrict__ v, const bf16_t* __restrict__ o,
                      const bf16_t* __restrict__ dout, const float* __restrict__ lse,
-                     float* __restrict__ delta, float* __restrict__ lse2,
-                     const int32_t* __restrict__ row_cnt, const int32_t* __restrict__ row_idx,
+                     float* __restrict__ stats, const int32_t* __restrict__ row_cnt,
+                     const int32_t* __restrict__ row_idx,
                      const int32_t* __restrict__ order, int N, int Tq, int Tk, float scale_log2,
                      float scale, bf16_t* __restrict__ dq) {
   constexpr int D = 128;
   using KT = Tile<D, kBoth>;
   constexpr int NK = D / 16, ND = D / 32;
   constexpr int TILE = 64 * D;
-  __shared__ __attribute__((aligned(16))) uint16_t kbuf[2 * TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t vbuf[2 * TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t kbuf0[TILE], kbuf1[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t vbuf0[TILE], vbuf1[TILE];
 
   const int wg = order ? order[blockIdx.x] : xcd_remap(blockIdx.x, gridDim.x);
   const int bh = wg / Tq, qi = wg % Tq;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
   const int h = lane >> 5, l32 = lane & 31;
   const size_t base = (size_t)bh * N * D;
-  const bf16_t* kh = k + base;
-  const bf16_t* vh = v + base;
+  const rsrc_t rk = make_rsrc(k + base, (uint32_t)N * D * 2);
+  const rsrc_t rv = make_rsrc(v + base, (uint32_t)N * D * 2);
+  uint32_t uo[4];
+  unit_offsets(lane, uo);
   const int qrow = qi * (NW * 32) + w * 32 + l32;
   const bool qvalid = qrow < N;
 
@@ -415,12 +455,12 @@ void dq_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       for (int i = 0; i < 8; ++i) dpart += a[i] * b[i];
     }
   }
+  // Delta = rowsum(dO * O): the two half-waves hold alternate 8-wide pieces
+  // of the row.  Both statistics of every row of the block, padding rows
+  // (zeros) included, are kept for the dK/dV kernel.
   const float dl = dpart + __shfl_xor(dpart, 32);
   const float l2 = qvalid ? lse[(size_t)bh * N + qrow] * kLog2e : 0.f;
-  if (qvalid && h == 0) {
-    delta[(size_t)bh * N + qrow] = dl;
-    lse2[(size_t)bh * N + qrow] = l2;
-  }
+  stats[stat_lse2(bh, stat_groups(N), qrow) + 32 * h] = h ? dl : l2;
 
   f32x16 acc[ND];
 #pragma unroll
@@ -428,16 +468,23 @@ void dq_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
 
   const int cnt = row_cnt[wg];
   const int32_t* lst = row_idx + (size_t)wg * Tk;
-  if (cnt > 0) copy_kv_tile<NW>(kh, vh, lst[0] * 64, N, kbuf, vbuf, w, lane);
-  for (int t = 0; t < cnt; ++t) {
-    const int key0 = lst[t] * 64;
-    const uint16_t* kt = kbuf + (t & 1) * TILE;
-    const uint16_t* vt = vbuf + (t & 1) * TILE;
+  int key_cur = cnt > 0 ? lst[0] * 64 : 0;
+  if (cnt > 0) copy_kv_tile<NW>(rk, rv, key_cur, kbuf0, vbuf0, w, uo);
+  int key_nxt = cnt > 1 ? lst[1] * 64 : 0;
+
+  double_buffered(cnt, [&](int t, auto parity) {
+    constexpr bool odd = decltype(parity)::value == 1;
+    const uint16_t* kt = odd ? kbuf1 : kbuf0;
+    const uint16_t* vt = odd ? vbuf1 : vbuf0;
+    const int key0 = key_cur;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (t + 1 < cnt)
-      copy_kv_tile<NW>(kh, vh, lst[t + 1] * 64, N, kbuf + ((t + 1) & 1) * TILE,
-                       vbuf + ((t + 1) & 1) * TILE, w, lane);
+    if (t + 1 < cnt) copy_kv_tile<NW>(rk, rv, key_nxt, odd ? kbuf0 : kbuf1, odd ? vbuf0 : vbuf1, w, uo);
+    key_cur = key_nxt;
+    if (t + 2 < cnt) key_nxt = lst[t + 2] * 64;
+
+    // the two 32-key halves one after the other, so that only one half's S
+    // and dP are live at a time
     const bool tail = key0 + 64 > N;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
@@ -448,15 +495,17 @@ void dq_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         sb = mfma32(lds_read8(kt + KT::off(32 * b + l32, c)), qf[kk], sb);
         dpb = mfma32(lds_read8(vt + KT::off(32 * b + l32, c)), df[kk], dpb);
       }
+      // dS = P * (dP - Delta)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[e], scale_log2, -l2));
         sb[e] = pv * (dpb[e] - dl);
       }
-      if (tail) {  // keys past N enter the dQ contraction: zero them
+      if (tail) {  // keys past N (zero rows) enter the dQ contraction: zero their dS
+        const int lim = N - key0 - 4 * h;
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-          if (key0 + 32 * b + 8 * (e >> 2) + 4 * h + (e & 3) >= N) sb[e] = 0.f;
+          if (32 * b + 8 * (e >> 2) + (e & 3) >= lim) sb[e] = 0.f;
       }
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
@@ -467,7 +516,8 @@ void dq_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                            acc[db]);
       }
     }
-  }
+  });
+
   if (qvalid) {
     bf16_t* row = dq + base + (size_t)qrow * D;
 #pragma unroll
@@ -494,8 +544,8 @@ void dq_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
 template <typename T, int D, int BQ>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-                 const T* __restrict__ dout, const float* __restrict__ lse2,
-                 const float* __restrict__ delta, const int32_t* __restrict__ col_cnt,
+                 const T* __restrict__ dout, const float* __restrict__ stats,
+                 const int32_t* __restrict__ col_cnt,
                  const int32_t* __restrict__ col_idx, const int32_t* __restrict__ order, int N,
                  int Tq, int Tk, float scale_log2, float scale, T* __restrict__ dk,
                  T* __restrict__ dv) {
@@ -542,7 +592,7 @@ void dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
   uint16_t* sd = sq + 32 * ST::kRowElems;                     // this pair's dO slice
   uint16_t* mine = kb == 0 ? sq : sd;              // the half this wave stages
   const T* src = kb == 0 ? q : dout;
-  const float* ssrc = kb == 0 ? lse2 : delta;
+  const int G = stat_groups(N);
   const int krow = 32 * kb + l32;                  // this lane's row of K, V
 
   f32x16 accv[ND], acck[ND];
@@ -566,7 +616,7 @@ void dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) own[kk] = ok ? load8(p + 16 * kk) : zero8();
     // wave 0: log2-scaled LSE (+inf on padding rows: P = 0); wave 1: Delta
-    const float x = ok ? ssrc[(size_t)bh * N + row] : 0.f;
+    const float x = ok ? stats[stat_lse2(bh, G, row) + 32 * kb] : 0.f;
     stat = kb == 0 ? (ok ? x : INFINITY) : x;
   };
 
@@ -680,20 +730,17 @@ void dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
 // registers for the whole kernel, their dK and dV tiles (32 x 128) in
 // accumulators.  Pair p takes the 32-row slices 4j + p of the flattened list
 // of (listed query block, slice) pairs.  Slices (Q, dO) and their LSE / Delta
-// are copied from global memory straight into LDS (global_load_lds, 16 bytes
-// per lane into lane-consecutive LDS units; which global unit a lane loads
-// realises the permuted row layout) into a double buffer, so the copy of the
-// next slice is in flight during the current one and costs no registers.
-// One workgroup barrier per step: after it, every wave's copy for this step
-// has landed (each waits for its own first) and every wave has finished with
-// the other buffer, which then receives the next copy.
+// are copied from global memory straight into LDS (buffer loads to LDS, see
+// copy_groups) into a double buffer (see double_buffered), so the copy of
+// the next slice is in flight during the current one and costs no
+// registers.
 // ---------------------------------------------------------------------------
 template <int BQ>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void dkdv_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                        const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
-                       const float* __restrict__ lse2, const float* __restrict__ delta,
-                       const int32_t* __restrict__ col_cnt, const int32_t* __restrict__ col_idx,
+                       const float* __restrict__ stats, const int32_t* __restrict__ col_cnt,
+                       const int32_t* __restrict__ col_idx,
                        const int32_t* __restrict__ order, int N, int Tq, int Tk,
                        float scale_log2, float scale, bf16_t* __restrict__ dk,
                        bf16_t* __restrict__ dv) {
@@ -704,21 +751,17 @@ void dkdv_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ 
   constexpr int NK = D / 16, ND = D / 32;
   constexpr int SUB = BQ / 32;                       // slices per query block
   constexpr int SLICE = 32 * D;                      // elements of one slice tensor
-  constexpr int V_BYTES = 64 * VT::kRowElems * 2;
-  constexpr int STAGE_BYTES = 2 * 4 * 2 * SLICE * 2; // [buffer][pair][Q | dO]
-  constexpr int ST_BYTES = 2 * 4 * 64 * 4;           // [buffer][pair][lse | Delta][32]
-  constexpr int RS = D + 4;
-  constexpr int RED_BYTES = 3 * 2 * 32 * RS * 4;     // partial tiles of pairs 1..3
-  static_assert(RED_BYTES <= STAGE_BYTES, "reduction reuses the slice buffers");
-  __shared__ __attribute__((aligned(16))) unsigned char smem[V_BYTES + STAGE_BYTES + ST_BYTES];
-  uint16_t* v_lds = reinterpret_cast<uint16_t*>(smem);
-  uint16_t* stage = reinterpret_cast<uint16_t*>(smem + V_BYTES);
-  float* stats = reinterpret_cast<float*>(smem + V_BYTES + STAGE_BYTES);
+  constexpr int STAGE = 4 * 2 * SLICE;               // one buffer: [pair][Q | dO]
+  constexpr int RS = D + 4;                          // fp32 row of a partial tile
+  static_assert(2 * 32 * RS * 4 <= STAGE * 2, "a pair's partial tiles fit one buffer");
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[64 * VT::kRowElems];
+  __shared__ __attribute__((aligned(16))) uint16_t stage0[STAGE], stage1[STAGE];
+  __shared__ __attribute__((aligned(16))) float stat0[4 * 64], stat1[4 * 64];  // [pair][lse | Delta]
 
   const int wg = order ? order[blockIdx.x] : xcd_remap(blockIdx.x, gridDim.x);
   const int bh = wg / Tk, kj = wg % Tk;
   const int key0 = kj * 64;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
   const int h = lane >> 5, l32 = lane & 31;
   const int pair = w >> 1, kb = w & 1;
   const size_t base = (size_t)bh * N * D;
@@ -740,32 +783,22 @@ void dkdv_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ 
   const int total = cnt * SUB;
   const int steps = (total + 3) / 4;
 
-  // Copy slice g = 4s + pair of step s into buffer b: wave kb = 0 copies Q
-  // and the 32 rows' log2-scaled LSE and Delta, wave kb = 1 copies dO.  Lane
-  // l's 16 bytes of copy i land in LDS unit 64i + l, which holds row
-  // r = 4i + l/16 and logical unit (l % 16) ^ swz(r).  Rows past N are read
-  // from row N-1 (their P is zeroed below).
-  const bf16_t* src = (kb == 0 ? q : dout) + base;
-  const float* ssrc = (h == 0 ? lse2 : delta) + (size_t)bh * N;
-  auto copy_step = [&](int s, int b) {
+  // Copy slice g = 4s + pair of step s: wave kb = 0 copies Q and the 32 rows'
+  // statistics (one 256-byte group: log2-scaled LSE, then Delta), wave kb = 1
+  // copies dO.  Rows past N arrive as zeros (their P is zeroed below).
+  const rsrc_t rsrc = make_rsrc((kb == 0 ? q : dout) + base, (uint32_t)N * D * 2);
+  const int G = stat_groups(N);
+  const rsrc_t rstat = make_rsrc(stats + (size_t)bh * G * 64, (uint32_t)G * 256);
+  uint32_t uo[4];
+  unit_offsets(lane, uo);
+  auto slice_row = [&](int s) {
     const int g = 4 * s + pair;
-    if (g >= total) return;
-    const int row0 = lst[g / SUB] * BQ + 32 * (g % SUB);
-    uint16_t* dst = stage + ((b * 4 + pair) * 2 + kb) * SLICE;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = 4 * i + (lane >> 4);
-      const int sw = ((r & 3) << 2) | ((r >> 2) & 3);
-      const int row = min(row0 + r, N - 1);
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(src + row * D + 8 * ((lane & 15) ^ sw)),
-          (__attribute__((address_space(3))) void*)(dst + i * 512), 16, 0, 0);
-    }
-    if (kb == 0) {
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(ssrc + min(row0 + l32, N - 1)),
-          (__attribute__((address_space(3))) void*)(stats + (b * 4 + pair) * 64), 4, 0, 0);
-    }
+    return g < total ? lst[g / SUB] * BQ + 32 * (g % SUB) : 0;
+  };
+  auto copy_step = [&](int s, uint16_t* stg, float* sts, int row0) {
+    if (4 * s + pair >= total) return;
+    copy_groups<2>(rsrc, row0, 0, stg + (pair * 2 + kb) * SLICE, uo);
+    if (kb == 0) buf_lds4<0>(rstat, sts + pair * 64, 4 * lane, (uint32_t)row0 * 8u);
   };
 
   f32x16 accv[ND], acck[ND];
@@ -776,92 +809,107 @@ void dkdv_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ 
   }
   const int krow = 32 * kb + l32;
 
-  if (steps > 0) copy_step(0, 0);
-  for (int s = 0; s < steps; ++s) {
-    const int b = s & 1;
+  // the list is walked with scalar loads, one step ahead of the copies
+  int row_cur = slice_row(0);
+  if (steps > 0) copy_step(0, stage0, stat0, row_cur);
+  int row_nxt = slice_row(1);
+  double_buffered(steps, [&](int s, auto parity) {
+    constexpr bool odd = decltype(parity)::value == 1;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (s + 1 < steps) copy_step(s + 1, b ^ 1);
-    const int g = 4 * s + pair;
-    if (g < total) {
-      const int row0 = lst[g / SUB] * BQ + 32 * (g % SUB);
-      const uint16_t* sq = stage + ((b * 4 + pair) * 2) * SLICE;
-      const uint16_t* sd = sq + SLICE;
-      const float* stl = stats + (b * 4 + pair) * 64;
-      // S = Q K^T and dP = dO V^T for the slice's 32 rows and this wave's keys
-      f32x16 sa = zero16(), dpa = zero16();
+    if (s + 1 < steps) copy_step(s + 1, odd ? stage0 : stage1, odd ? stat0 : stat1, row_nxt);
+    const int row0 = row_cur;
+    row_cur = row_nxt;
+    row_nxt = slice_row(s + 2);
+    if (4 * s + pair >= total) return;
+    const uint16_t* sq = (odd ? stage1 : stage0) + (pair * 2) * SLICE;
+    const uint16_t* sd = sq + SLICE;
+    const float* stl = (odd ? stat1 : stat0) + pair * 64;
+    // S = Q K^T and dP = dO V^T for the slice's 32 rows and this wave's keys
+    f32x16 sa = zero16(), dpa = zero16();
 #pragma unroll
-      for (int kk = 0; kk < NK; ++kk) {
-        const int c = 16 * kk + 8 * h;
-        sa = mfma32(lds_read8(sq + ST::off(l32, c)), kf[kk], sa);
-        dpa = mfma32(lds_read8(sd + ST::off(l32, c)), lds_read8(v_lds + VT::off(krow, c)), dpa);
-      }
-      // P and dS for rows 8g+4h+i, packed into the B operands of the two
-      // 16-row steps (keys past N need no mask: they only feed their own,
-      // unstored, dK and dV rows)
-      if (row0 + 32 > N) {  // the partial last query block: rows past N add nothing
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (row0 + 8 * (e >> 2) + 4 * h + (e & 3) >= N) sa[e] = -INFINITY;
-      }
-      bf16x8 pb[2], sb[2];
-#pragma unroll
-      for (int gg = 0; gg < 4; ++gg) {
-        const f32x4 L = *reinterpret_cast<const f32x4*>(stl + 8 * gg + 4 * h);
-        const f32x4 Dl = *reinterpret_cast<const f32x4*>(stl + 32 + 8 * gg + 4 * h);
-        float pv[4], ds[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int e = 4 * gg + i;
-          pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[e], scale_log2, -L[i]));
-          ds[i] = pv[i] * (dpa[e] - Dl[i]);
-        }
-        // two packed conversions per four values
-        const int t = gg >> 1, o = 4 * (gg & 1);
-        pb[t][o] = (__bf16)pv[0]; pb[t][o + 1] = (__bf16)pv[1];
-        pb[t][o + 2] = (__bf16)pv[2]; pb[t][o + 3] = (__bf16)pv[3];
-        sb[t][o] = (__bf16)ds[0]; sb[t][o + 1] = (__bf16)ds[1];
-        sb[t][o + 2] = (__bf16)ds[2]; sb[t][o + 3] = (__bf16)ds[3];
-      }
-      // dV^T += dO^T P and dK^T += Q^T dS over the slice's rows
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int db = 0; db < ND; ++db) {
-          accv[db] = mfma32(tr_operand<D, kBoth>(sd, 16 * t, 32 * db, lane), pb[t], accv[db]);
-          acck[db] = mfma32(tr_operand<D, kBoth>(sq, 16 * t, 32 * db, lane), sb[t], acck[db]);
-        }
+    for (int kk = 0; kk < NK; ++kk) {
+      const int c = 16 * kk + 8 * h;
+      sa = mfma32(lds_read8(sq + ST::off(l32, c)), kf[kk], sa);
+      dpa = mfma32(lds_read8(sd + ST::off(l32, c)), lds_read8(v_lds + VT::off(krow, c)), dpa);
     }
-  }
+    // P and dS for rows 8g+4h+i, packed into the B operands of the two
+    // 16-row steps (keys past N need no mask: they only feed their own,
+    // unstored, dK and dV rows)
+    if (row0 + 32 > N) {  // the partial last query block: rows past N add nothing
+      const int lim = N - row0 - 4 * h;
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (8 * (e >> 2) + (e & 3) >= lim) sa[e] = -INFINITY;
+    }
+    bf16x8 pb[2], sb[2];
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg) {
+      const f32x4 L = *reinterpret_cast<const f32x4*>(stl + 8 * gg + 4 * h);
+      const f32x4 Dl = *reinterpret_cast<const f32x4*>(stl + 32 + 8 * gg + 4 * h);
+      float pv[4], ds[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = 4 * gg + i;
+        pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[e], scale_log2, -L[i]));
+        ds[i] = pv[i] * (dpa[e] - Dl[i]);
+      }
+      // two packed conversions per four values
+      const int t = gg >> 1, o = 4 * (gg & 1);
+      pb[t][o] = (__bf16)pv[0]; pb[t][o + 1] = (__bf16)pv[1];
+      pb[t][o + 2] = (__bf16)pv[2]; pb[t][o + 3] = (__bf16)pv[3];
+      sb[t][o] = (__bf16)ds[0]; sb[t][o + 1] = (__bf16)ds[1];
+      sb[t][o + 2] = (__bf16)ds[2]; sb[t][o + 3] = (__bf16)ds[3];
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS over the slice's rows
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int db = 0; db < ND; ++db) {
+        accv[db] = mfma32(tr_operand<D, kBoth>(sd, 16 * t, 32 * db, lane), pb[t], accv[db]);
+        acck[db] = mfma32(tr_operand<D, kBoth>(sq, 16 * t, 32 * db, lane), sb[t], acck[db]);
+      }
+  });
 
-  // Sum the four pairs' partial tiles: pairs 1..3 write theirs to LDS, pair 0
-  // adds them in pair order and stores.  Element e of block db is
-  // d = 32db + 8(e/4) + 4h + e%4 at key 32kb + l32.
-  float* red = reinterpret_cast<float*>(stage);
+  // Sum the four pairs' partial tiles in pair order through LDS (a buffer
+  // holds one pair's two 32 x 128 fp32 tiles): pairs 1 and 2 write theirs,
+  // pair 0 adds them; pair 3 writes, pair 0 adds it and stages the total for
+  // row-wise stores.  Element e of block db is d = 32db + 8(e/4) + 4h + e%4
+  // at key 32kb + l32.
+  float* red0 = reinterpret_cast<float*>(stage0) + kb * 32 * RS;
+  float* red1 = reinterpret_cast<float*>(stage1) + kb * 32 * RS;
+  auto put_partial = [&](float* t, const f32x16* acc) {
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) t[l32 * RS + 32 * db + 8 * (e >> 2) + 4 * h + (e & 3)] = acc[db][e];
+  };
   for (int which = 0; which < 2; ++which) {
-    __syncthreads();
-    if (pair > 0) {
-      float* t = red + ((pair - 1) * 2 + kb) * 32 * RS;
-#pragma unroll
-      for (int db = 0; db < ND; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          t[l32 * RS + 32 * db + 8 * (e >> 2) + 4 * h + (e & 3)] =
-              which == 0 ? accv[db][e] : acck[db][e];
-    }
+    f32x16* acc = which == 0 ? accv : acck;
+    __syncthreads();                                  // buffers free (loop or last round done)
+    if (pair == 1) put_partial(red0, acc);
+    if (pair == 2) put_partial(red1, acc);
     __syncthreads();
     if (pair == 0) {
-      const float mul = which == 0 ? 1.f : scale;
-      float* t0 = red + kb * 32 * RS;   // pair 1's tile, overwritten with the sum
 #pragma unroll
       for (int db = 0; db < ND; ++db)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int off = l32 * RS + 32 * db + 8 * (e >> 2) + 4 * h + (e & 3);
-          float sum = which == 0 ? accv[db][e] : acck[db][e];
+          acc[db][e] = acc[db][e] + red0[off] + red1[off];
+        }
+    }
+    __syncthreads();
+    if (pair == 3) put_partial(red0, acc);
+    __syncthreads();
+    if (pair == 0) {
+      const float mul = which == 0 ? 1.f : scale;
 #pragma unroll
-          for (int pp = 0; pp < 3; ++pp) sum += red[(pp * 2 + kb) * 32 * RS + off];
-          t0[off] = sum * mul;
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int off = l32 * RS + 32 * db + 8 * (e >> 2) + 4 * h + (e & 3);
+          red1[off] = (acc[db][e] + red0[off]) * mul;
         }
       wave_lds_sync();
       bf16_t* out = (which == 0 ? dv : dk) + base;
@@ -869,7 +917,7 @@ void dkdv_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ 
         const int r = ch / (D / 4), c4 = (ch % (D / 4)) * 4;
         const int key = key0 + 32 * kb + r;
         if (key < N) {
-          const float* pp = t0 + r * RS + c4;
+          const float* pp = red1 + r * RS + c4;
           store4(out + (size_t)key * D + c4, pp[0], pp[1], pp[2], pp[3]);
         }
       }
@@ -884,8 +932,7 @@ template <typename T, int D, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4 ? 2 : 1, 2)))
 void dq_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                const T* __restrict__ o, const T* __restrict__ dout, const float* __restrict__ lse,
-               float* __restrict__ delta, float* __restrict__ lse2,
-               const int32_t* __restrict__ row_cnt,
+               float* __restrict__ stats, const int32_t* __restrict__ row_cnt,
                const int32_t* __restrict__ row_idx, const int32_t* __restrict__ order, int N,
                int Tq, int Tk, float scale_log2, float scale, T* __restrict__ dq) {
   constexpr int NT = NW * 64;
@@ -926,10 +973,8 @@ void dq_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __rest
   // Delta = 0 give dS = 0 whatever P is.
   const float dl = dpart + __shfl_xor(dpart, 32);
   const float l2 = qvalid ? lse[(size_t)bh * N + qrow] * kLog2e : 0.f;
-  if (qvalid && h == 0) {
-    delta[(size_t)bh * N + qrow] = dl;
-    lse2[(size_t)bh * N + qrow] = l2;
-  }
+  // both statistics of every row of the block, padding rows (zeros) included
+  stats[stat_lse2(bh, stat_groups(N), qrow) + 32 * h] = h ? dl : l2;
 
   f32x16 acc[ND];
 #pragma unroll
@@ -972,9 +1017,10 @@ void dq_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __rest
         sb[e] = pv * (dpb[e] - dl);
       }
       if (tail) {  // keys past N enter the dQ contraction: zero them
+        const int lim = N - key0 - 4 * h;
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-          if (key0 + 32 * b + 8 * (e >> 2) + 4 * h + (e & 3) >= N) sb[e] = 0.f;
+          if (32 * b + 8 * (e >> 2) + (e & 3) >= lim) sb[e] = 0.f;
       }
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
@@ -1055,8 +1101,7 @@ struct BwdArgs {
   int BH, N;
   float sl2, scale;
   void *dq, *dk, *dv;
-  float* delta;
-  float* lse2;
+  float* stats;
   hipStream_t s;
 };
 
@@ -1067,7 +1112,7 @@ static void launch_dq(const BwdArgs& a) {
 #define SA2_DQ_ASYNC_ARGS                                                                     \
   static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k),                            \
       static_cast<const bf16_t*>(a.v), static_cast<const bf16_t*>(a.o),                        \
-      static_cast<const bf16_t*>(a.dout), a.lse, a.delta, a.lse2, m->row_cnt, m->row_idx,      \
+      static_cast<const bf16_t*>(a.dout), a.lse, a.stats, m->row_cnt, m->row_idx,               \
       m->row_order, a.N, m->Tq, m->Tk, a.sl2, a.scale, static_cast<bf16_t*>(a.dq)
     if (m->bq == 128) dq_async_kernel<4><<<a.BH * m->Tq, 256, 0, a.s>>>(SA2_DQ_ASYNC_ARGS);
     else dq_async_kernel<2><<<a.BH * m->Tq, 128, 0, a.s>>>(SA2_DQ_ASYNC_ARGS);
@@ -1076,7 +1121,7 @@ static void launch_dq(const BwdArgs& a) {
   }
 #define SA2_DQ_ARGS                                                                          \
   static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),          \
-      static_cast<const T*>(a.o), static_cast<const T*>(a.dout), a.lse, a.delta, a.lse2,      \
+      static_cast<const T*>(a.o), static_cast<const T*>(a.dout), a.lse, a.stats,              \
       m->row_cnt,                                                                             \
       m->row_idx, m->row_order, a.N, m->Tq, m->Tk, a.sl2, a.scale, static_cast<T*>(a.dq)
   if (m->bq == 128) dq_kernel<T, D, 4><<<a.BH * m->Tq, 256, 0, a.s>>>(SA2_DQ_ARGS);
@@ -1090,7 +1135,7 @@ static void launch_dkdv(const BwdArgs& a) {
   if constexpr (D == 128 && sizeof(T) == 2) {
 #define SA2_DKDV_ASYNC_ARGS                                                                  \
   static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k),                            \
-      static_cast<const bf16_t*>(a.v), static_cast<const bf16_t*>(a.dout), a.lse2, a.delta,    \
+      static_cast<const bf16_t*>(a.v), static_cast<const bf16_t*>(a.dout), a.stats,            \
       m->col_cnt, m->col_idx, m->col_order, a.N, m->Tq, m->Tk, a.sl2, a.scale,                 \
       static_cast<bf16_t*>(a.dk), static_cast<bf16_t*>(a.dv)
     if (m->bq == 128) dkdv_async_kernel<128><<<a.BH * m->Tk, 512, 0, a.s>>>(SA2_DKDV_ASYNC_ARGS);
@@ -1100,7 +1145,7 @@ static void launch_dkdv(const BwdArgs& a) {
   }
 #define SA2_DKDV_ARGS                                                                         \
   static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),          \
-      static_cast<const T*>(a.dout), a.lse2, a.delta, m->col_cnt, m->col_idx, m->col_order, a.N, \
+      static_cast<const T*>(a.dout), a.stats, m->col_cnt, m->col_idx, m->col_order, a.N,      \
       m->Tq, m->Tk, a.sl2, a.scale, static_cast<T*>(a.dk), static_cast<T*>(a.dv)
   if (m->bq == 128) dkdv_kernel<T, D, 128><<<a.BH * m->Tk, 256, 0, a.s>>>(SA2_DKDV_ARGS);
   else dkdv_kernel<T, D, 64><<<a.BH * m->Tk, 256, 0, a.s>>>(SA2_DKDV_ARGS);
@@ -1133,18 +1178,13 @@ static sa2_status check_bwd(const char* fn, const void* q, const void* k, const 
   return SA2_OK;
 }
 
-static size_t bwd_half_bytes(int B, int H, int N) {
-  return ((size_t)B * H * N * 4 + 255) & ~(size_t)255;
-}
 
 static BwdArgs bwd_args(const void* q, const void* k, const void* v, const void* o,
                         const float* lse, const void* dout, int B, int H, int N, int d,
                         const sa2_mask* m, void* dq, void* dk, void* dv, void* ws, void* stream) {
   const double sc = 1.0 / sqrt((double)d);
-  float* delta = static_cast<float*>(ws);
-  float* lse2 = reinterpret_cast<float*>(static_cast<char*>(ws) + bwd_half_bytes(B, H, N));
   return BwdArgs{q, k, v, o, dout, lse, m, B * H, N, (float)(1.4426950408889634 * sc),
-                 (float)sc, dq, dk, dv, delta, lse2, reinterpret_cast<hipStream_t>(stream)};
+                 (float)sc, dq, dk, dv, static_cast<float*>(ws), reinterpret_cast<hipStream_t>(stream)};
 }
 
 }  // namespace sa2
@@ -1174,7 +1214,8 @@ extern "C" sa2_status sa2_attn_fwd(const void* q, const void* k, const void* v, 
 
 extern "C" size_t sa2_bwd_workspace_bytes(int B, int H, int N, int d) {
   if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return 0;
-  return 2 * (((size_t)B * H * N * 4 + 255) & ~(size_t)255);
+  // per head: stat_groups(N) groups of 32 rows x (LSE, Delta) in fp32
+  return ((size_t)B * H * sa2::stat_groups(N) * 256 + 255) & ~(size_t)255;
 }
 
 extern "C" sa2_status sa2_attn_bwd_dq(const void* q, const void* k, const void* v,

@@ -162,4 +162,75 @@ __device__ inline void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
+
+// A value the compiler may keep in a scalar register (it is the same in every
+// lane, e.g. the wave index).
+__device__ inline int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// ---------------------------------------------------------------------------
+// Direct global -> LDS copies through buffer resources.
+//
+// A raw buffer resource covers `bytes` bytes from `base`; a load whose offset
+// (vector + scalar + immediate) is at or past `bytes` returns zeros, so rows
+// past the end of a tensor arrive as zero rows with no clamping.  The
+// buffer_load ... lds form writes lane l's bytes to LDS at M0 + IMM + size*l
+// (M0: the LDS byte address of dst, the same in every lane); the immediate
+// offset IMM moves the global address and the LDS address alike, the scalar
+// offset only the global one.
+//
+// The copies are issued from inline assembly, so the compiler does not track
+// them: it would otherwise make LDS reads that it cannot prove disjoint from
+// a copy in flight wait for it (the transposing reads are such), which
+// serialises the double buffers.  Every kernel therefore waits for its own
+// copies explicitly (s_waitcnt vmcnt(0)) and then passes a workgroup barrier
+// before it reads them, and issues no copy that it does not wait for.
+// ---------------------------------------------------------------------------
+typedef uint32_t rsrc_t __attribute__((ext_vector_type(4)));
+#define SA2_AS3 __attribute__((address_space(3)))
+
+__device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  rsrc_t r;
+  r[0] = (uint32_t)a;
+  r[1] = (uint32_t)(a >> 32);   // stride 0: a raw byte buffer
+  r[2] = bytes;
+  r[3] = 0x00020000u;           // 32-bit data format, no swizzle
+  return r;
+}
+__device__ inline uint32_t lds_addr(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((const SA2_AS3 void*)p);
+}
+template <int IMM>
+__device__ inline void buf_lds16(rsrc_t r, const void* dst, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen offset:%4 lds"
+               :: "s"(lds_addr(dst)), "v"(voff), "s"(r), "s"(soff), "i"(IMM) : "memory", "m0");
+}
+template <int IMM>
+__device__ inline void buf_lds4(rsrc_t r, const void* dst, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen offset:%4 lds"
+               :: "s"(lds_addr(dst)), "v"(voff), "s"(r), "s"(soff), "i"(IMM) : "memory", "m0");
+}
+
+// Unrolls f(integral_constant<int, I>) for I = B .. E-1, so that I can feed
+// an immediate operand.
+template <int I> struct Int { static constexpr int value = I; };
+template <int B, int E, typename F>
+__device__ inline void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(Int<B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Backward row statistics (bwd workspace).  Per head, rows are taken in
+// groups of 32; group g holds [32 x log2-scaled LSE | 32 x Delta] (fp32), so
+// one 256-byte copy brings both statistics of a 32-row slice.  A head has
+// 4 * ceil(N / 128) groups: every row of every query block, padding included.
+// ---------------------------------------------------------------------------
+__host__ __device__ inline int stat_groups(int N) { return 4 * ((N + 127) / 128); }
+__device__ inline size_t stat_lse2(int bh, int G, int row) {
+  return ((size_t)bh * G + (row >> 5)) * 64 + (row & 31);
+}
+__device__ inline size_t stat_delta(int bh, int G, int row) { return stat_lse2(bh, G, row) + 32; }
 }  // namespace sa2

@@ -306,9 +306,12 @@ void columns_kernel(const uint8_t* __restrict__ bitmap, int Tq, int Tk,
 }
 
 // ---------------------------------------------------------------------------
-// Work orders: row (column) indices sorted by decreasing count, so that the
-// attention kernels start the longest lists first.  One workgroup per order
-// (block 0 rows, block 1 columns) counts, scans and places in LDS; the order
+// Work orders.  Workgroup slot i of an attention kernel runs on XCD i % 8.
+// XCD x takes the contiguous share of the natural (b, h, block) order that
+// the fixed XCD-aware mapping (xcd_remap) gives it, so that its L2 sees the
+// inputs of a narrow band of heads; within that share its slots are filled
+// by decreasing list length, so that each XCD starts its longest lists first.
+// One workgroup per (order, XCD) counts, scans and places in LDS; the order
 // among equal counts is whatever the LDS atomics give (it affects scheduling
 // only).
 // ---------------------------------------------------------------------------
@@ -320,14 +323,18 @@ void order_kernel(const int32_t* __restrict__ row_cnt, int nrows, int row_max,
                   int32_t* __restrict__ row_order, int32_t* __restrict__ col_order) {
   __shared__ int hist[kMaxTk + 1];
   __shared__ int scan[kOrderThreads];
-  const int32_t* cnt = blockIdx.x == 0 ? row_cnt : col_cnt;
-  int32_t* order = blockIdx.x == 0 ? row_order : col_order;
-  const int n = blockIdx.x == 0 ? nrows : ncols;
-  const int nb = (blockIdx.x == 0 ? row_max : col_max) + 1;   // counts 0 .. max
+  const int which = blockIdx.x / 8, x = blockIdx.x % 8;
+  const int32_t* cnt = which == 0 ? row_cnt : col_cnt;
+  int32_t* order = which == 0 ? row_order : col_order;
+  const int n = which == 0 ? nrows : ncols;
+  const int nb = (which == 0 ? row_max : col_max) + 1;   // counts 0 .. max
+  // this XCD's share of the natural order (as in xcd_remap)
+  const int qn = n / 8, rn = n % 8;
+  const int c0 = x * qn + min(x, rn), len = qn + (x < rn ? 1 : 0);
   const int tid = threadIdx.x;
   for (int c = tid; c < nb; c += kOrderThreads) hist[c] = 0;
   __syncthreads();
-  for (int i = tid; i < n; i += kOrderThreads) atomicAdd(&hist[cnt[i]], 1);
+  for (int j = tid; j < len; j += kOrderThreads) atomicAdd(&hist[cnt[c0 + j]], 1);
   __syncthreads();
   // first position of each count in descending-count order
   const int per = (nb + kOrderThreads - 1) / kOrderThreads;
@@ -350,7 +357,11 @@ void order_kernel(const int32_t* __restrict__ row_cnt, int nrows, int row_max,
     run += h;
   }
   __syncthreads();
-  for (int i = tid; i < n; i += kOrderThreads) order[atomicAdd(&hist[cnt[i]], 1)] = i;
+  // rank j within the share goes to slot 8j + x (slots i with i % 8 == x)
+  for (int j = tid; j < len; j += kOrderThreads) {
+    const int id = c0 + j;
+    order[8 * atomicAdd(&hist[cnt[id]], 1) + x] = id;
+  }
 }
 
 static int next_pow2(int x) {
@@ -447,7 +458,7 @@ extern "C" sa2_status sa2_build_mask(const void* q, const void* k, int dtype, in
                                                         m->col_idx);
   if (sa2_status st = check_launch("columns_kernel")) return st;
   if (orders) {
-    order_kernel<<<2, kOrderThreads, 0, s>>>(m->row_cnt, BH * Tq, Tk, m->col_cnt, BH * Tk, Tq,
+    order_kernel<<<16, kOrderThreads, 0, s>>>(m->row_cnt, BH * Tq, Tk, m->col_cnt, BH * Tk, Tq,
                                              m->row_order, m->col_order);
     if (sa2_status st = check_launch("order_kernel")) return st;
   }

@@ -68,11 +68,15 @@ typedef enum { SA2_BF16 = 0, SA2_F32 = 1 } sa2_dtype;
  *   col_idx  int32 [B, H, Tk, Tq]: the first col_cnt entries are those query
  *            blocks, ascending (the transposed index the backward walks).
  *   row_order, col_order  optional (may be NULL) int32 [B*H*Tq], [B*H*Tk]:
- *            a work order for the attention kernels, the flat (b*H + h)*Tq + i
- *            (resp. *Tk + j) indices sorted by decreasing row_cnt (col_cnt),
- *            so that the longest lists start first.  The order among equal
- *            counts is unspecified; it changes scheduling only, never results.
- *            When NULL the kernels use a fixed XCD-aware order.
+ *            a work order for the attention kernels: a permutation of the
+ *            flat (b*H + h)*Tq + i (resp. *Tk + j) indices.  Workgroup slot s
+ *            runs on XCD s % 8; the slots of XCD x hold the x-th contiguous
+ *            eighth of the flat indices (the fixed XCD-aware order), sorted
+ *            by decreasing row_cnt (col_cnt), so that each XCD's L2 serves a
+ *            narrow band of heads and each XCD starts its longest lists
+ *            first.  The order among equal counts is unspecified; it changes
+ *            scheduling only, never results.  When NULL the kernels use the
+ *            fixed XCD-aware order itself.
  *
  * sa2_build_mask writes all these arrays; the attention calls read row_cnt /
  * row_idx (forward, dQ) and col_cnt / col_idx (dK, dV), and the orders when
@@ -152,8 +156,10 @@ sa2_status sa2_attn_fwd(const void* q, const void* k, const void* v, int dtype,
 
 /*
  * Bytes of device workspace the backward calls need: two fp32 per token
- * (2*B*H*N floats, each half rounded up to 256 bytes): the row sums
- * Delta_t = sum_c dO_tc * O_tc and the LSE in base 2 (lse_t * log2(e)).
+ * row, the row sums Delta_t = sum_c dO_tc * O_tc and the LSE in base 2
+ * (lse_t * log2(e)), for every row of every 128-row query block (padding
+ * rows past N included): B*H*4*ceil(N/128) groups of 32 rows x 2 x 4 bytes,
+ * rounded up to 256 bytes.
  */
 size_t sa2_bwd_workspace_bytes(int B, int H, int N, int d);
 

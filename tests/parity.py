@@ -85,14 +85,23 @@ def check_lists(bitmap: np.ndarray, row_cnt, row_idx, col_cnt, col_idx):
 
 
 def check_orders(row_cnt: np.ndarray, col_cnt: np.ndarray, row_order, col_order):
-    """Work orders: permutations of the flat row / column indices with
-    non-increasing counts (the order among equal counts is free)."""
+    """Work orders: permutations of the flat row / column indices in which the
+    slots of XCD x (slot % 8 == x) hold the x-th contiguous eighth of the
+    indices (the split of the fixed XCD-aware order) with non-increasing
+    counts; the order among equal counts is free."""
     for cnt, order in ((row_cnt.reshape(-1), row_order), (col_cnt.reshape(-1), col_order)):
         if order is None:
             continue
         order = np.asarray(order)
-        assert np.array_equal(np.sort(order), np.arange(cnt.size)), "order is not a permutation"
-        assert np.all(np.diff(cnt[order]) <= 0), "order is not by decreasing count"
+        n = cnt.size
+        assert np.array_equal(np.sort(order), np.arange(n)), "order is not a permutation"
+        q, r = divmod(n, 8)
+        for x in range(8):
+            c0, ln = x * q + min(x, r), q + (1 if x < r else 0)
+            share = order[x::8]
+            assert share.size == ln, f"XCD {x}: {share.size} slots, expected {ln}"
+            assert np.array_equal(np.sort(share), np.arange(c0, c0 + ln)), f"XCD {x}: wrong share"
+            assert np.all(np.diff(cnt[share]) <= 0), f"XCD {x}: not by decreasing count"
 
 
 def rel_fro(a: np.ndarray, b: np.ndarray) -> float:

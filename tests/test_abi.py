@@ -38,7 +38,7 @@ def test_workspace_sizes():
     want = up(B * H * Tq * d * 8) + up(B * H * Tk * d * 8) + up(B * H * Tq * Tk * 8)
     assert L.sa2_mask_workspace_bytes(B, H, N, d, bq, bk) == want
     assert L.sa2_mask_workspace_bytes(0, H, N, d, bq, bk) == 0
-    assert L.sa2_bwd_workspace_bytes(B, H, N, d) == 2 * up(B * H * N * 4)
+    assert L.sa2_bwd_workspace_bytes(B, H, N, d) == up(B * H * 4 * (-(-N // 128)) * 32 * 2 * 4)
 
 
 def _mask(B=1, H=1, N=256, bq=64, bk=64):
