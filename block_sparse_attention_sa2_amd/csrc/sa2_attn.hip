@@ -724,81 +724,74 @@ void dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
 }
 
 // ---------------------------------------------------------------------------
-// Backward dK, dV for bf16 and d = 128: one workgroup (8 waves) per key block.
+// Backward dK, dV for bf16 and d = 128: one workgroup of two waves per key
+// block.
 //
-// Wave (pair p, kb) owns keys key0 + 32kb .. +31: their K fragments live in
-// registers for the whole kernel, their dK and dV tiles (32 x 128) in
-// accumulators.  Pair p takes the 32-row slices 4j + p of the flattened list
-// of (listed query block, slice) pairs.  Slices (Q, dO) and their LSE / Delta
-// are copied from global memory straight into LDS (buffer loads to LDS, see
-// copy_groups) into a double buffer (see double_buffered), so the copy of
-// the next slice is in flight during the current one and costs no
-// registers.
+// Wave kb owns keys key0 + 32kb .. +31: their K and V fragments (the B
+// operands of S = Q K^T and dP = dO V^T) live in registers for the whole
+// kernel, their dK^T and dV^T tiles (32 x 128 each) in accumulators.  Both
+// waves walk every 32-row slice of the query blocks in the column list; each
+// slice's Q rows and statistics (copied by wave 0) and dO rows (wave 1) go
+// straight to an LDS double buffer (see copy_groups, double_buffered) that
+// the two waves share, so the only barrier is between the two.  Four
+// workgroups share a CU, so the two waves on a SIMD belong to different
+// workgroups and overlap their phases freely.
 // ---------------------------------------------------------------------------
 template <int BQ>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void dkdv_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
-                       const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
-                       const float* __restrict__ stats, const int32_t* __restrict__ col_cnt,
-                       const int32_t* __restrict__ col_idx,
-                       const int32_t* __restrict__ order, int N, int Tq, int Tk,
-                       float scale_log2, float scale, bf16_t* __restrict__ dk,
-                       bf16_t* __restrict__ dv) {
-  constexpr int D = 128, NT = 512;
-  using VT = Tile<D, kRows>;   // V tile: fragment reads
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void dkdv_pair_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                      const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
+                      const float* __restrict__ stats, const int32_t* __restrict__ col_cnt,
+                      const int32_t* __restrict__ col_idx, const int32_t* __restrict__ order,
+                      int N, int Tq, int Tk, float scale_log2, float scale,
+                      bf16_t* __restrict__ dk, bf16_t* __restrict__ dv) {
+  constexpr int D = 128;
   using ST = Tile<D, kBoth>;   // slices: permuted, unpadded rows of 256 bytes
   static_assert(ST::kSwizzled, "slices are copied as whole 256-byte rows");
   constexpr int NK = D / 16, ND = D / 32;
-  constexpr int SUB = BQ / 32;                       // slices per query block
-  constexpr int SLICE = 32 * D;                      // elements of one slice tensor
-  constexpr int STAGE = 4 * 2 * SLICE;               // one buffer: [pair][Q | dO]
-  constexpr int RS = D + 4;                          // fp32 row of a partial tile
-  static_assert(2 * 32 * RS * 4 <= STAGE * 2, "a pair's partial tiles fit one buffer");
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[64 * VT::kRowElems];
-  __shared__ __attribute__((aligned(16))) uint16_t stage0[STAGE], stage1[STAGE];
-  __shared__ __attribute__((aligned(16))) float stat0[4 * 64], stat1[4 * 64];  // [pair][lse | Delta]
+  constexpr int SUB = BQ / 32;   // slices per query block
+  constexpr int SLICE = 32 * D;  // elements of one slice tensor
+  __shared__ __attribute__((aligned(16))) uint16_t sq0[SLICE], sq1[SLICE];   // Q slices
+  __shared__ __attribute__((aligned(16))) uint16_t so0[SLICE], so1[SLICE];   // dO slices
+  __shared__ __attribute__((aligned(16))) float st0[64], st1[64];            // [lse | Delta]
 
   const int wg = order ? order[blockIdx.x] : xcd_remap(blockIdx.x, gridDim.x);
   const int bh = wg / Tk, kj = wg % Tk;
   const int key0 = kj * 64;
-  const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
+  const int tid = threadIdx.x, lane = tid & 63, kb = uniform(tid >> 6);
   const int h = lane >> 5, l32 = lane & 31;
-  const int pair = w >> 1, kb = w & 1;
   const size_t base = (size_t)bh * N * D;
 
-  // K fragments of this wave's keys (B operand of S = Q K^T), zero past N
-  bf16x8 kf[NK];
+  // K and V fragments of this wave's keys, zero past N
+  bf16x8 kf[NK], vf[NK];
   {
     const int key = key0 + 32 * kb + l32;
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk)
-      kf[kk] = key < N ? load8(k + base + (size_t)key * D + 16 * kk + 8 * h) : zero8();
-    bf16x8 r[2];
-    fetch_tile<bf16_t, D, NT>(v + base, key0, N, tid, r);
-    put_tile<D, kRows, NT>(v_lds, tid, r);
+    for (int kk = 0; kk < NK; ++kk) {
+      const size_t off = base + (size_t)key * D + 16 * kk + 8 * h;
+      kf[kk] = key < N ? load8(k + off) : zero8();
+      vf[kk] = key < N ? load8(v + off) : zero8();
+    }
   }
 
   const int cnt = col_cnt[wg];
   const int32_t* lst = col_idx + (size_t)wg * Tq;
-  const int total = cnt * SUB;
-  const int steps = (total + 3) / 4;
-
-  // Copy slice g = 4s + pair of step s: wave kb = 0 copies Q and the 32 rows'
-  // statistics (one 256-byte group: log2-scaled LSE, then Delta), wave kb = 1
-  // copies dO.  Rows past N arrive as zeros (their P is zeroed below).
+  const int steps = cnt * SUB;
+  // wave 0 copies Q and the statistics, wave 1 copies dO; rows past N arrive
+  // as zeros, their statistics as the dQ kernel wrote them (zeros)
   const rsrc_t rsrc = make_rsrc((kb == 0 ? q : dout) + base, (uint32_t)N * D * 2);
   const int G = stat_groups(N);
-  const rsrc_t rstat = make_rsrc(stats + (size_t)bh * G * 64, (uint32_t)G * 256);
+  const rsrc_t rst = make_rsrc(stats + (size_t)bh * G * 64, (uint32_t)G * 256);
   uint32_t uo[4];
   unit_offsets(lane, uo);
-  auto slice_row = [&](int s) {
-    const int g = 4 * s + pair;
-    return g < total ? lst[g / SUB] * BQ + 32 * (g % SUB) : 0;
-  };
-  auto copy_step = [&](int s, uint16_t* stg, float* sts, int row0) {
-    if (4 * s + pair >= total) return;
-    copy_groups<2>(rsrc, row0, 0, stg + (pair * 2 + kb) * SLICE, uo);
-    if (kb == 0) buf_lds4<0>(rstat, sts + pair * 64, 4 * lane, (uint32_t)row0 * 8u);
+  auto slice_row = [&](int s) { return s < steps ? lst[s / SUB] * BQ + 32 * (s % SUB) : 0; };
+  auto copy = [&](int row0, uint16_t* dq_, uint16_t* do_, float* ds_) {
+    if (kb == 0) {
+      copy_groups<2>(rsrc, row0, 0, dq_, uo);
+      buf_lds4<0>(rst, ds_, 4 * lane, (uint32_t)row0 * 8u);
+    } else {
+      copy_groups<2>(rsrc, row0, 0, do_, uo);
+    }
   };
 
   f32x16 accv[ND], acck[ND];
@@ -807,121 +800,107 @@ void dkdv_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ 
     accv[db] = zero16();
     acck[db] = zero16();
   }
-  const int krow = 32 * kb + l32;
 
-  // the list is walked with scalar loads, one step ahead of the copies
+  // Byte offsets in the permuted slice layout (kBoth, rows of 256 bytes).
+  // Row reads (lane: row l32, units 2kk + h): (2kk + h) ^ swz(l32) =
+  // 2kk ^ (h ^ swz(l32)), so the address of step kk is ra ^ 32kk.
+  // Transposed reads (tr_operand, rows 16t + 4h + a (+8), units 4db + cc,
+  // a = (lane % 16) / 4): the unit is 4(db ^ a) + (cc ^ b), b = (h + 2hi) % 4,
+  // so the address is tb[hi] ^ 64db, plus 4096t.  The bases are re-made
+  // opaque each step, so that the per-read addresses are formed by one xor in
+  // the loop instead of occupying registers for the whole kernel.
+  const uint32_t ra0 = 256u * l32 + 16u * (h ^ (((l32 & 3) << 2) | ((l32 >> 2) & 3)));
+  uint32_t tb0[2];
+#pragma unroll
+  for (int hi = 0; hi < 2; ++hi) {
+    const int ar = (lane & 15) >> 2, bs = (h + 2 * hi) & 3;
+    const int cc = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    tb0[hi] = 256u * (4 * h + ar + 8 * hi) + 64u * ar + 16u * (cc ^ bs) + 8u * (lane & 1);
+  }
+  auto rd8 = [](const uint16_t* arr, uint32_t boff) {
+    return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(arr) + boff);
+  };
+  auto rdtr = [](const uint16_t* arr, uint32_t boff) {
+    return lds_read_tr(reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(arr) + boff));
+  };
+
   int row_cur = slice_row(0);
-  if (steps > 0) copy_step(0, stage0, stat0, row_cur);
+  if (steps > 0) copy(row_cur, sq0, so0, st0);
   int row_nxt = slice_row(1);
   double_buffered(steps, [&](int s, auto parity) {
     constexpr bool odd = decltype(parity)::value == 1;
+    const uint16_t* sq = odd ? sq1 : sq0;
+    const uint16_t* so = odd ? so1 : so0;
+    const float* stl = odd ? st1 : st0;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (s + 1 < steps) copy_step(s + 1, odd ? stage0 : stage1, odd ? stat0 : stat1, row_nxt);
+    if (s + 1 < steps) copy(row_nxt, odd ? sq0 : sq1, odd ? so0 : so1, odd ? st0 : st1);
     const int row0 = row_cur;
     row_cur = row_nxt;
     row_nxt = slice_row(s + 2);
-    if (4 * s + pair >= total) return;
-    const uint16_t* sq = (odd ? stage1 : stage0) + (pair * 2) * SLICE;
-    const uint16_t* sd = sq + SLICE;
-    const float* stl = (odd ? stat1 : stat0) + pair * 64;
+    uint32_t ra = ra0, tb[2] = {tb0[0], tb0[1]};
+    asm volatile("" : "+v"(ra), "+v"(tb[0]), "+v"(tb[1]));
+
     // S = Q K^T and dP = dO V^T for the slice's 32 rows and this wave's keys
     f32x16 sa = zero16(), dpa = zero16();
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
-      const int c = 16 * kk + 8 * h;
-      sa = mfma32(lds_read8(sq + ST::off(l32, c)), kf[kk], sa);
-      dpa = mfma32(lds_read8(sd + ST::off(l32, c)), lds_read8(v_lds + VT::off(krow, c)), dpa);
+      const uint32_t off = ra ^ (32u * kk);
+      sa = mfma32(rd8(sq, off), kf[kk], sa);
+      dpa = mfma32(rd8(so, off), vf[kk], dpa);
     }
-    // P and dS for rows 8g+4h+i, packed into the B operands of the two
-    // 16-row steps (keys past N need no mask: they only feed their own,
-    // unstored, dK and dV rows)
     if (row0 + 32 > N) {  // the partial last query block: rows past N add nothing
       const int lim = N - row0 - 4 * h;
 #pragma unroll
       for (int e = 0; e < 16; ++e)
         if (8 * (e >> 2) + (e & 3) >= lim) sa[e] = -INFINITY;
     }
+    // P and dS for rows 8g+4h+i, packed into the B operands of the two
+    // 16-row steps (keys past N need no mask: they only feed their own,
+    // unstored, dK and dV rows)
     bf16x8 pb[2], sb[2];
 #pragma unroll
     for (int gg = 0; gg < 4; ++gg) {
       const f32x4 L = *reinterpret_cast<const f32x4*>(stl + 8 * gg + 4 * h);
       const f32x4 Dl = *reinterpret_cast<const f32x4*>(stl + 32 + 8 * gg + 4 * h);
-      float pv[4], ds[4];
+      const int t = gg >> 1, o = 4 * (gg & 1);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int e = 4 * gg + i;
-        pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[e], scale_log2, -L[i]));
-        ds[i] = pv[i] * (dpa[e] - Dl[i]);
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[e], scale_log2, -L[i]));
+        pb[t][o + i] = (__bf16)pv;
+        sb[t][o + i] = (__bf16)(pv * (dpa[e] - Dl[i]));
       }
-      // two packed conversions per four values
-      const int t = gg >> 1, o = 4 * (gg & 1);
-      pb[t][o] = (__bf16)pv[0]; pb[t][o + 1] = (__bf16)pv[1];
-      pb[t][o + 2] = (__bf16)pv[2]; pb[t][o + 3] = (__bf16)pv[3];
-      sb[t][o] = (__bf16)ds[0]; sb[t][o + 1] = (__bf16)ds[1];
-      sb[t][o + 2] = (__bf16)ds[2]; sb[t][o + 3] = (__bf16)ds[3];
     }
     // dV^T += dO^T P and dK^T += Q^T dS over the slice's rows
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int db = 0; db < ND; ++db) {
+      const uint32_t lo = tb[0] ^ (64u * db), hi = tb[1] ^ (64u * db);
 #pragma unroll
-      for (int db = 0; db < ND; ++db) {
-        accv[db] = mfma32(tr_operand<D, kBoth>(sd, 16 * t, 32 * db, lane), pb[t], accv[db]);
-        acck[db] = mfma32(tr_operand<D, kBoth>(sq, 16 * t, 32 * db, lane), sb[t], acck[db]);
+      for (int t = 0; t < 2; ++t) {
+        const bf16x8 ot = cat(rdtr(so, lo + 4096u * t), rdtr(so, hi + 4096u * t));
+        const bf16x8 qt = cat(rdtr(sq, lo + 4096u * t), rdtr(sq, hi + 4096u * t));
+        accv[db] = mfma32(ot, pb[t], accv[db]);
+        acck[db] = mfma32(qt, sb[t], acck[db]);
       }
+    }
   });
 
-  // Sum the four pairs' partial tiles in pair order through LDS (a buffer
-  // holds one pair's two 32 x 128 fp32 tiles): pairs 1 and 2 write theirs,
-  // pair 0 adds them; pair 3 writes, pair 0 adds it and stages the total for
-  // row-wise stores.  Element e of block db is d = 32db + 8(e/4) + 4h + e%4
-  // at key 32kb + l32.
-  float* red0 = reinterpret_cast<float*>(stage0) + kb * 32 * RS;
-  float* red1 = reinterpret_cast<float*>(stage1) + kb * 32 * RS;
-  auto put_partial = [&](float* t, const f32x16* acc) {
+  // Element e of block db is d = 32db + 8(e/4) + 4h + e%4 at key 32kb + l32:
+  // runs of four consecutive d of one key row.
+  const int key = key0 + 32 * kb + l32;
+  if (key < N) {
+    bf16_t* rv = dv + base + (size_t)key * D;
+    bf16_t* rk = dk + base + (size_t)key * D;
 #pragma unroll
     for (int db = 0; db < ND; ++db)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) t[l32 * RS + 32 * db + 8 * (e >> 2) + 4 * h + (e & 3)] = acc[db][e];
-  };
-  for (int which = 0; which < 2; ++which) {
-    f32x16* acc = which == 0 ? accv : acck;
-    __syncthreads();                                  // buffers free (loop or last round done)
-    if (pair == 1) put_partial(red0, acc);
-    if (pair == 2) put_partial(red1, acc);
-    __syncthreads();
-    if (pair == 0) {
-#pragma unroll
-      for (int db = 0; db < ND; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int off = l32 * RS + 32 * db + 8 * (e >> 2) + 4 * h + (e & 3);
-          acc[db][e] = acc[db][e] + red0[off] + red1[off];
-        }
-    }
-    __syncthreads();
-    if (pair == 3) put_partial(red0, acc);
-    __syncthreads();
-    if (pair == 0) {
-      const float mul = which == 0 ? 1.f : scale;
-#pragma unroll
-      for (int db = 0; db < ND; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int off = l32 * RS + 32 * db + 8 * (e >> 2) + 4 * h + (e & 3);
-          red1[off] = (acc[db][e] + red0[off]) * mul;
-        }
-      wave_lds_sync();
-      bf16_t* out = (which == 0 ? dv : dk) + base;
-      for (int ch = lane; ch < 32 * D / 4; ch += 64) {
-        const int r = ch / (D / 4), c4 = (ch % (D / 4)) * 4;
-        const int key = key0 + 32 * kb + r;
-        if (key < N) {
-          const float* pp = red1 + r * RS + c4;
-          store4(out + (size_t)key * D + c4, pp[0], pp[1], pp[2], pp[3]);
-        }
+      for (int g = 0; g < 4; ++g) {
+        const int c = 32 * db + 8 * g + 4 * h, e = 4 * g;
+        store4(rv + c, accv[db][e], accv[db][e + 1], accv[db][e + 2], accv[db][e + 3]);
+        store4(rk + c, acck[db][e] * scale, acck[db][e + 1] * scale, acck[db][e + 2] * scale,
+               acck[db][e + 3] * scale);
       }
-    }
   }
 }
 
@@ -1133,14 +1112,14 @@ template <typename T, int D>
 static void launch_dkdv(const BwdArgs& a) {
   const sa2_mask* m = a.m;
   if constexpr (D == 128 && sizeof(T) == 2) {
-#define SA2_DKDV_ASYNC_ARGS                                                                  \
+#define SA2_DKDV_PAIR_ARGS                                                                  \
   static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k),                            \
       static_cast<const bf16_t*>(a.v), static_cast<const bf16_t*>(a.dout), a.stats,            \
       m->col_cnt, m->col_idx, m->col_order, a.N, m->Tq, m->Tk, a.sl2, a.scale,                 \
       static_cast<bf16_t*>(a.dk), static_cast<bf16_t*>(a.dv)
-    if (m->bq == 128) dkdv_async_kernel<128><<<a.BH * m->Tk, 512, 0, a.s>>>(SA2_DKDV_ASYNC_ARGS);
-    else dkdv_async_kernel<64><<<a.BH * m->Tk, 512, 0, a.s>>>(SA2_DKDV_ASYNC_ARGS);
-#undef SA2_DKDV_ASYNC_ARGS
+    if (m->bq == 128) dkdv_pair_kernel<128><<<a.BH * m->Tk, 128, 0, a.s>>>(SA2_DKDV_PAIR_ARGS);
+    else dkdv_pair_kernel<64><<<a.BH * m->Tk, 128, 0, a.s>>>(SA2_DKDV_PAIR_ARGS);
+#undef SA2_DKDV_PAIR_ARGS
     return;
   }
 #define SA2_DKDV_ARGS                                                                         \
