@@ -113,6 +113,52 @@ __device__ inline bf16x8 pack8(const f32x16& a, int e0) {
 }
 
 // ---------------------------------------------------------------------------
+// Byte offsets into a permuted tile (kBoth layout, d = 128: rows of 256
+// bytes, 16-byte unit u of row r stored at u ^ swz(r)), for the two access
+// patterns of the MFMA operands, each formed with one xor per read.
+//   Row reads (A operand rows r = 32blk + l32, units 2kk + h):
+//     (2kk + h) ^ swz(l32) = 2kk ^ (h ^ swz(l32)) -> ra ^ 32kk, + 8192blk.
+//   Transposed reads (tr_operand: rows 16t + 4h + a (+8 for the high half),
+//   a = (lane % 16) / 4, units 4db + c, c = 2((lane / 16) % 2) + (lane % 4) / 2):
+//     the unit is 4(db ^ a) + (c ^ b), b = (h + 2hi) % 4 -> tb[hi] ^ 64db,
+//     + 4096t.
+// A kernel re-makes the bases opaque once per step (fresh()), so that the
+// compiler forms each address in the loop instead of keeping one register
+// per distinct address for the whole kernel.
+// ---------------------------------------------------------------------------
+struct SwzAddr {
+  uint32_t ra, tb[2];
+  __device__ explicit SwzAddr(int lane) {
+    const int h = lane >> 5, l32 = lane & 31;
+    ra = 256u * l32 + 16u * (h ^ (((l32 & 3) << 2) | ((l32 >> 2) & 3)));
+    const int a = (lane & 15) >> 2;
+    const int c = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi)
+      tb[hi] = 256u * (4 * h + a + 8 * hi) + 64u * a + 16u * (c ^ ((h + 2 * hi) & 3)) +
+               8u * (lane & 1);
+  }
+  __device__ SwzAddr fresh() const {
+    SwzAddr r = *this;
+    asm volatile("" : "+v"(r.ra), "+v"(r.tb[0]), "+v"(r.tb[1]));
+    return r;
+  }
+  __device__ uint32_t row(int blk, int kk) const { return 8192u * blk + (ra ^ (32u * kk)); }
+  __device__ uint32_t tr(int t, int db, int hi) const {
+    return (tb[hi] ^ (64u * db)) + 4096u * t;
+  }
+};
+__device__ inline bf16x8 rd_row(const uint16_t* tile, uint32_t boff) {
+  return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(tile) + boff);
+}
+// tr_operand<128, kBoth>(tile, 16t, 32db, lane) through the bases above
+__device__ inline bf16x8 rd_tr(const uint16_t* tile, const SwzAddr& A, int t, int db) {
+  const char* b = reinterpret_cast<const char*>(tile);
+  return cat(lds_read_tr(reinterpret_cast<const uint16_t*>(b + A.tr(t, db, 0))),
+             lds_read_tr(reinterpret_cast<const uint16_t*>(b + A.tr(t, db, 1))));
+}
+
+// ---------------------------------------------------------------------------
 // Forward
 // ---------------------------------------------------------------------------
 template <typename T, int D, int NW>
@@ -275,24 +321,36 @@ __device__ inline void copy_kv_tile(rsrc_t rk, rsrc_t rv, int key0, uint16_t* kd
   copy_groups<PER / 4>(rv, key0, w * PER, vdst, uo);
 }
 
-// Double buffering of asynchronous copies.  The two buffers are separate LDS
-// arrays and the tile loop is unrolled by two, so that each step names its
-// buffers statically: the compiler then sees that the copy in flight (into
-// the other array) cannot alias this step's LDS reads and does not wait for
-// it.  With one array indexed by the step parity it would wait for the copy
-// before the first read, which serialises copy and compute.  One workgroup
-// barrier per step: after it, every wave's copy for this step has landed
-// (each waits for its own first) and every wave is done with the other
-// buffer, which then receives the next copy.
+// Step loops over LDS rings.  The buffers of a ring are separate LDS arrays
+// and the loop is unrolled by a multiple of the ring sizes, so that each step
+// names its buffers statically and every LDS address is a register plus an
+// immediate offset.
+template <int P, typename F>
+__device__ inline void unrolled_steps(int cnt, F&& step) {
+  for (int t = 0; t < cnt; t += P)
+    static_for<0, P>([&](auto j) {
+      if (t + decltype(j)::value < cnt) step(t + decltype(j)::value, j);
+    });
+}
+// Double buffering: one workgroup barrier per step; after it, every wave's
+// copy for this step has landed (each waits for its own first) and every
+// wave is done with the other buffer, which then receives the next copy.
 template <typename F>
 __device__ inline void double_buffered(int cnt, F&& step) {
-  for (int t = 0; t < cnt; t += 2) {
-    step(t, Int<0>{});
-    if (t + 1 < cnt) step(t + 1, Int<1>{});
-  }
+  unrolled_steps<2>(cnt, step);
 }
 
-// Forward for bf16 and d = 128 with double-buffered asynchronous K/V tiles.
+// s_waitcnt with vmcnt(VM) and lgkmcnt(0) (expcnt not waited).
+template <int VM>
+__device__ inline void wait_vm_lgkm0() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4));
+}
+
+// Forward for bf16 and d = 128 with double-buffered asynchronous K/V tiles
+// (see double_buffered).  The LDS operands of each MFMA group are read well
+// ahead of their MFMAs (sched_group_barrier fixes the issue order), so that
+// LDS latency overlaps the matrix work instead of stalling it.
 template <int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4 ? 2 : 1, 2)))
 void fwd_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
@@ -301,11 +359,11 @@ void fwd_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
                       int N, int Tq, int Tk, float scale_log2, bf16_t* __restrict__ o,
                       float* __restrict__ lse) {
   constexpr int D = 128;
-  using KT = Tile<D, kBoth>;
   constexpr int NK = D / 16, ND = D / 32;
   constexpr int TILE = 64 * D;
-  __shared__ __attribute__((aligned(16))) uint16_t kbuf0[TILE], kbuf1[TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t vbuf0[TILE], vbuf1[TILE];
+  constexpr int KCOPIES = 16 / NW;   // copy instructions per wave per tile tensor
+  __shared__ __attribute__((aligned(16))) uint16_t kb0[TILE], kb1[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t vb0[TILE], vb1[TILE];
 
   const int wg = order ? order[blockIdx.x] : xcd_remap(blockIdx.x, gridDim.x);
   const int bh = wg / Tq, qi = wg % Tq;
@@ -316,6 +374,7 @@ void fwd_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
   const rsrc_t rv = make_rsrc(v + base, (uint32_t)N * D * 2);
   uint32_t uo[4];
   unit_offsets(lane, uo);
+  const SwzAddr addr0(lane);
   const int qrow = qi * (NW * 32) + w * 32 + l32;
   const bool qvalid = qrow < N;
 
@@ -332,28 +391,44 @@ void fwd_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
   // the list is walked with scalar loads, one entry ahead of its copy
   const int cnt = row_cnt[wg];
   const int32_t* lst = row_idx + (size_t)wg * Tk;
-  int key_cur = cnt > 0 ? lst[0] * 64 : 0;
-  if (cnt > 0) copy_kv_tile<NW>(rk, rv, key_cur, kbuf0, vbuf0, w, uo);
-  int key_nxt = cnt > 1 ? lst[1] * 64 : 0;
+  auto key_at = [&](int t) { return t < cnt ? lst[t] * 64 : 0; };
+  int key_cur = key_at(0);
+  if (cnt > 0) copy_kv_tile<NW>(rk, rv, key_cur, kb0, vb0, w, uo);
+  int key_nxt = key_at(1);
 
   double_buffered(cnt, [&](int t, auto parity) {
     constexpr bool odd = decltype(parity)::value == 1;
-    const uint16_t* kt = odd ? kbuf1 : kbuf0;
-    const uint16_t* vt = odd ? vbuf1 : vbuf0;
+    const uint16_t* kt = odd ? kb1 : kb0;
+    const uint16_t* vt = odd ? vb1 : vb0;
     const int key0 = key_cur;
-    __builtin_amdgcn_s_waitcnt(0);
+    wait_vm_lgkm0<0>();
     __syncthreads();
-    if (t + 1 < cnt) copy_kv_tile<NW>(rk, rv, key_nxt, odd ? kbuf0 : kbuf1, odd ? vbuf0 : vbuf1, w, uo);
+    if (t + 1 < cnt) copy_kv_tile<NW>(rk, rv, key_nxt, odd ? kb0 : kb1, odd ? vb0 : vb1, w, uo);
     key_cur = key_nxt;
-    if (t + 2 < cnt) key_nxt = lst[t + 2] * 64;
+    key_nxt = key_at(t + 2);
+    const SwzAddr A = addr0.fresh();
 
-    f32x16 s[2];
+    // S = K Q^T: the first half's eight K fragments are read first, the
+    // second half's are read while the first half's MFMAs run
+    f32x16 s[2] = {zero16(), zero16()};
+    {
+      bf16x8 ka[NK], kc[NK];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      s[b] = zero16();
+      for (int kk = 0; kk < NK; ++kk) ka[kk] = rd_row(kt, A.row(0, kk));
 #pragma unroll
-      for (int kk = 0; kk < NK; ++kk)
-        s[b] = mfma32(lds_read8(kt + KT::off(32 * b + l32, 16 * kk + 8 * h)), qf[kk], s[b]);
+      for (int kk = 0; kk < NK; ++kk) {
+        s[0] = mfma32(ka[kk], qf[kk], s[0]);
+        kc[kk] = rd_row(kt, A.row(1, kk));
+      }
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) s[1] = mfma32(kc[kk], qf[kk], s[1]);
+      __builtin_amdgcn_sched_group_barrier(0x100, NK, 0);   // DS reads
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, NK, 0);
     }
     if (key0 + 64 > N) {  // the partial last key block (a uniform branch)
       const int lim = N - key0 - 4 * h;   // keys of this lane at offsets >= lim are past N
@@ -377,22 +452,33 @@ void fwd_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
 #pragma unroll
       for (int db = 0; db < ND; ++db) acc[db] *= alpha;
     }
+    // the first V fragments are read while P is formed
+    bf16x8 va[ND];
+#pragma unroll
+    for (int db = 0; db < ND; ++db) va[db] = rd_tr(vt, A, 0, db);
     float ps = 0.f;
+    bf16x8 pf[4];
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][e], scale_log2, -m));
-        s[b][e] = pv;
+        pf[2 * b + (e >> 3)][e & 7] = (__bf16)pv;
         ps += pv;
       }
     lsum += ps;
+    // O^T += V^T P^T, the next 16-key step's V fragments read during this one's
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
-      const bf16x8 pf = pack8(s[tt >> 1], 8 * (tt & 1));
+      bf16x8 vn[ND];
 #pragma unroll
-      for (int db = 0; db < ND; ++db)
-        acc[db] = mfma32(tr_operand<D, kBoth>(vt, 16 * tt, 32 * db, lane), pf, acc[db]);
+      for (int db = 0; db < ND; ++db) {
+        acc[db] = mfma32(va[db], pf[tt], acc[db]);
+        if (tt < 3) vn[db] = rd_tr(vt, A, tt + 1, db);
+      }
+      if (tt < 3)
+#pragma unroll
+        for (int db = 0; db < ND; ++db) va[db] = vn[db];
     }
   });
 
@@ -411,7 +497,7 @@ void fwd_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
   }
 }
 
-// dQ for bf16 and d = 128 with the same double-buffered asynchronous tiles.
+// dQ for bf16 and d = 128 with the same K and V rings as the forward.
 template <int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4 ? 2 : 1, 2)))
 void dq_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
@@ -422,11 +508,11 @@ void dq_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                      const int32_t* __restrict__ order, int N, int Tq, int Tk, float scale_log2,
                      float scale, bf16_t* __restrict__ dq) {
   constexpr int D = 128;
-  using KT = Tile<D, kBoth>;
   constexpr int NK = D / 16, ND = D / 32;
   constexpr int TILE = 64 * D;
-  __shared__ __attribute__((aligned(16))) uint16_t kbuf0[TILE], kbuf1[TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t vbuf0[TILE], vbuf1[TILE];
+  constexpr int KCOPIES = 16 / NW;   // copy instructions per wave per tile tensor
+  __shared__ __attribute__((aligned(16))) uint16_t kb0[TILE], kb1[TILE], kb2[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t vb0[TILE], vb1[TILE];
 
   const int wg = order ? order[blockIdx.x] : xcd_remap(blockIdx.x, gridDim.x);
   const int bh = wg / Tq, qi = wg % Tq;
@@ -437,8 +523,20 @@ void dq_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   const rsrc_t rv = make_rsrc(v + base, (uint32_t)N * D * 2);
   uint32_t uo[4];
   unit_offsets(lane, uo);
+  const SwzAddr addr0(lane);
   const int qrow = qi * (NW * 32) + w * 32 + l32;
   const bool qvalid = qrow < N;
+
+  // the first tiles' copies go out before the row loads below
+  const int cnt = row_cnt[wg];
+  const int32_t* lst = row_idx + (size_t)wg * Tk;
+  auto key_at = [&](int t) { return t < cnt ? lst[t] * 64 : 0; };
+  int key_t = key_at(0), key_t1 = key_at(1), key_t2 = key_at(2);
+  if (cnt > 0) {
+    copy_groups<KCOPIES / 4>(rk, key_t, w * KCOPIES, kb0, uo);
+    copy_groups<KCOPIES / 4>(rv, key_t, w * KCOPIES, vb0, uo);
+  }
+  if (cnt > 1) copy_groups<KCOPIES / 4>(rk, key_t1, w * KCOPIES, kb1, uo);
 
   bf16x8 qf[NK], df[NK];
   float dpart = 0.f;
@@ -466,22 +564,21 @@ void dq_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
 #pragma unroll
   for (int db = 0; db < ND; ++db) acc[db] = zero16();
 
-  const int cnt = row_cnt[wg];
-  const int32_t* lst = row_idx + (size_t)wg * Tk;
-  int key_cur = cnt > 0 ? lst[0] * 64 : 0;
-  if (cnt > 0) copy_kv_tile<NW>(rk, rv, key_cur, kbuf0, vbuf0, w, uo);
-  int key_nxt = cnt > 1 ? lst[1] * 64 : 0;
-
-  double_buffered(cnt, [&](int t, auto parity) {
-    constexpr bool odd = decltype(parity)::value == 1;
-    const uint16_t* kt = odd ? kbuf1 : kbuf0;
-    const uint16_t* vt = odd ? vbuf1 : vbuf0;
-    const int key0 = key_cur;
-    __builtin_amdgcn_s_waitcnt(0);
+  unrolled_steps<6>(cnt, [&](int t, auto j) {
+    constexpr int J = decltype(j)::value;
+    const uint16_t* kt = J % 3 == 0 ? kb0 : J % 3 == 1 ? kb1 : kb2;
+    const uint16_t* vt = J % 2 == 0 ? vb0 : vb1;
+    uint16_t* vn = J % 2 == 0 ? vb1 : vb0;                            // V(t+1)
+    uint16_t* kn = J % 3 == 0 ? kb2 : J % 3 == 1 ? kb0 : kb1;         // K(t+2)
+    const int key0 = key_t;
+    if (t + 1 < cnt) wait_vm_lgkm0<KCOPIES>(); else wait_vm_lgkm0<0>();
     __syncthreads();
-    if (t + 1 < cnt) copy_kv_tile<NW>(rk, rv, key_nxt, odd ? kbuf0 : kbuf1, odd ? vbuf0 : vbuf1, w, uo);
-    key_cur = key_nxt;
-    if (t + 2 < cnt) key_nxt = lst[t + 2] * 64;
+    if (t + 1 < cnt) copy_groups<KCOPIES / 4>(rv, key_t1, w * KCOPIES, vn, uo);
+    if (t + 2 < cnt) copy_groups<KCOPIES / 4>(rk, key_t2, w * KCOPIES, kn, uo);
+    key_t = key_t1;
+    key_t1 = key_t2;
+    key_t2 = key_at(t + 3);
+    const SwzAddr A = addr0.fresh();
 
     // the two 32-key halves one after the other, so that only one half's S
     // and dP are live at a time
@@ -491,9 +588,8 @@ void dq_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       f32x16 sb = zero16(), dpb = zero16();
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
-        const int c = 16 * kk + 8 * h;
-        sb = mfma32(lds_read8(kt + KT::off(32 * b + l32, c)), qf[kk], sb);
-        dpb = mfma32(lds_read8(vt + KT::off(32 * b + l32, c)), df[kk], dpb);
+        sb = mfma32(rd_row(kt, A.row(b, kk)), qf[kk], sb);
+        dpb = mfma32(rd_row(vt, A.row(b, kk)), df[kk], dpb);
       }
       // dS = P * (dP - Delta)
 #pragma unroll
@@ -512,8 +608,7 @@ void dq_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         const bf16x8 sf = pack8(sb, 8 * t2);
 #pragma unroll
         for (int db = 0; db < ND; ++db)
-          acc[db] = mfma32(tr_operand<D, kBoth>(kt, 32 * b + 16 * t2, 32 * db, lane), sf,
-                           acc[db]);
+          acc[db] = mfma32(rd_tr(kt, A, 2 * b + t2, db), sf, acc[db]);
       }
     }
   });
@@ -801,28 +896,7 @@ void dkdv_pair_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
     acck[db] = zero16();
   }
 
-  // Byte offsets in the permuted slice layout (kBoth, rows of 256 bytes).
-  // Row reads (lane: row l32, units 2kk + h): (2kk + h) ^ swz(l32) =
-  // 2kk ^ (h ^ swz(l32)), so the address of step kk is ra ^ 32kk.
-  // Transposed reads (tr_operand, rows 16t + 4h + a (+8), units 4db + cc,
-  // a = (lane % 16) / 4): the unit is 4(db ^ a) + (cc ^ b), b = (h + 2hi) % 4,
-  // so the address is tb[hi] ^ 64db, plus 4096t.  The bases are re-made
-  // opaque each step, so that the per-read addresses are formed by one xor in
-  // the loop instead of occupying registers for the whole kernel.
-  const uint32_t ra0 = 256u * l32 + 16u * (h ^ (((l32 & 3) << 2) | ((l32 >> 2) & 3)));
-  uint32_t tb0[2];
-#pragma unroll
-  for (int hi = 0; hi < 2; ++hi) {
-    const int ar = (lane & 15) >> 2, bs = (h + 2 * hi) & 3;
-    const int cc = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-    tb0[hi] = 256u * (4 * h + ar + 8 * hi) + 64u * ar + 16u * (cc ^ bs) + 8u * (lane & 1);
-  }
-  auto rd8 = [](const uint16_t* arr, uint32_t boff) {
-    return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(arr) + boff);
-  };
-  auto rdtr = [](const uint16_t* arr, uint32_t boff) {
-    return lds_read_tr(reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(arr) + boff));
-  };
+  const SwzAddr addr0(lane);
 
   int row_cur = slice_row(0);
   if (steps > 0) copy(row_cur, sq0, so0, st0);
@@ -838,16 +912,14 @@ void dkdv_pair_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
     const int row0 = row_cur;
     row_cur = row_nxt;
     row_nxt = slice_row(s + 2);
-    uint32_t ra = ra0, tb[2] = {tb0[0], tb0[1]};
-    asm volatile("" : "+v"(ra), "+v"(tb[0]), "+v"(tb[1]));
+    const SwzAddr A = addr0.fresh();
 
     // S = Q K^T and dP = dO V^T for the slice's 32 rows and this wave's keys
     f32x16 sa = zero16(), dpa = zero16();
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
-      const uint32_t off = ra ^ (32u * kk);
-      sa = mfma32(rd8(sq, off), kf[kk], sa);
-      dpa = mfma32(rd8(so, off), vf[kk], dpa);
+      sa = mfma32(rd_row(sq, A.row(0, kk)), kf[kk], sa);
+      dpa = mfma32(rd_row(so, A.row(0, kk)), vf[kk], dpa);
     }
     if (row0 + 32 > N) {  // the partial last query block: rows past N add nothing
       const int lim = N - row0 - 4 * h;
@@ -874,16 +946,12 @@ void dkdv_pair_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
     }
     // dV^T += dO^T P and dK^T += Q^T dS over the slice's rows
 #pragma unroll
-    for (int db = 0; db < ND; ++db) {
-      const uint32_t lo = tb[0] ^ (64u * db), hi = tb[1] ^ (64u * db);
+    for (int db = 0; db < ND; ++db)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const bf16x8 ot = cat(rdtr(so, lo + 4096u * t), rdtr(so, hi + 4096u * t));
-        const bf16x8 qt = cat(rdtr(sq, lo + 4096u * t), rdtr(sq, hi + 4096u * t));
-        accv[db] = mfma32(ot, pb[t], accv[db]);
-        acck[db] = mfma32(qt, sb[t], acck[db]);
+        accv[db] = mfma32(rd_tr(so, A, t, db), pb[t], accv[db]);
+        acck[db] = mfma32(rd_tr(sq, A, t, db), sb[t], acck[db]);
       }
-    }
   });
 
   // Element e of block db is d = 32db + 8(e/4) + 4h + e%4 at key 32kb + l32:
