@@ -17,6 +17,7 @@ convention: forward 4 N^2 d H density, forward+backward 3.5x that.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import platform
@@ -28,6 +29,37 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+
+# HBM bytes per launch of the attention kernels, from rocprofv3 FETCH_SIZE /
+# WRITE_SIZE runs (scaled by a copy of known size), recorded with a digest of
+# the kernel sources they were taken on; used only while the sources match.
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "wan13_layer_hbm_traffic.md")
+KERNEL_SOURCES = ("block_sparse_attention_sa2_amd/csrc/sa2_attn.hip",
+                  "block_sparse_attention_sa2_amd/csrc/sa2_common.h")
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel: str, workload: str):
+    """Measured HBM bytes per launch of `kernel` on `workload`, or None if the
+    record is missing or was taken on another workload or other sources."""
+    try:
+        with open(TRAFFIC_SUMMARY) as fh:
+            line = next(l for l in fh if l.startswith("traffic-record "))
+        rec = json.loads(line[len("traffic-record "):])
+    except (OSError, StopIteration, ValueError):
+        return None
+    if (rec.get("source_digest") != kernel_source_digest() or rec.get("workload") != workload
+            or kernel not in rec.get("kernels", {})):
+        return None
+    k = rec["kernels"][kernel]
+    return float(k["fetch_bytes"] + k["write_bytes"])
 
 
 def log(*a):
@@ -41,7 +73,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c2", help="workload key (default: 1.3B layer fwd+bwd)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=3, help="heads the oracle times")
+    ap.add_argument("--cpu-heads", type=int, default=12, help="heads the oracle times (default: the whole layer)")
     ap.add_argument("--no-work-order", action="store_true",
                     help="schedule the attention kernels in their fixed order")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -161,16 +193,17 @@ def main():
 
     # per-kernel algorithmic work (each attention stage is exactly one kernel)
     unit = 2.0 * N * N * d * H * B * density          # one GEMM over the kept pairs
-    kernels = {"fwd": ("fwd_kernel", 2 * unit, 2 * unit)}
+    # (the bf16, d = 128 kernels each stage launches)
+    kernels = {"fwd": ("fwd_async_kernel", 2 * unit, 2 * unit)}
     if backward:
-        kernels["bwd_dq"] = ("dq_kernel", 1 * unit, 3 * unit)       # S, dP recomputed
-        kernels["bwd_dkdv"] = ("dkdv_kernel", 4 * unit, 4 * unit)
+        kernels["bwd_dq"] = ("dq_async_kernel", 1 * unit, 3 * unit)     # S, dP recomputed
+        kernels["bwd_dkdv"] = ("dkdv_pair_kernel", 4 * unit, 4 * unit)
     dom = max(kernels, key=lambda st: per[st])
     name, alg, exe = kernels[dom]
     achieved = alg / (per[dom] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": name, "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": None,
+                "traffic": recorded_traffic(name, args.workload),
                 "per_launch": {"algorithmic_flop": alg, "executed_flop": exe, "ms": round(per[dom], 4)}}
     qk_bytes = 2.0 * B * H * N * d * q.element_size()
     mask_gbps = qk_bytes / (per["mask"] * 1e-3) / 1e9
