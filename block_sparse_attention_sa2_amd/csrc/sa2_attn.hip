@@ -263,7 +263,7 @@ void fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
         acc[db] = mfma32(tr_operand<D, kCols>(v_lds, 16 * tt, 32 * db, lane), pf, acc[db]);
     }
   }
-  const float ltot = lsum + __shfl_xor(lsum, 32);
+  const float ltot = wave_sum32(lsum);
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
   if (qvalid) {
     T* orow = o + base + (size_t)qrow * D;
@@ -482,7 +482,7 @@ void fwd_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
     }
   });
 
-  const float ltot = lsum + __shfl_xor(lsum, 32);
+  const float ltot = wave_sum32(lsum);
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
   if (qvalid) {
     bf16_t* orow = o + base + (size_t)qrow * D;
@@ -556,7 +556,7 @@ void dq_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   // Delta = rowsum(dO * O): the two half-waves hold alternate 8-wide pieces
   // of the row.  Both statistics of every row of the block, padding rows
   // (zeros) included, are kept for the dK/dV kernel.
-  const float dl = dpart + __shfl_xor(dpart, 32);
+  const float dl = wave_sum32(dpart);
   const float l2 = qvalid ? lse[(size_t)bh * N + qrow] * kLog2e : 0.f;
   stats[stat_lse2(bh, stat_groups(N), qrow) + 32 * h] = h ? dl : l2;
 
@@ -1018,7 +1018,7 @@ void dq_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __rest
   // Delta = rowsum(dO * O): the two half-waves hold alternate 8-wide pieces
   // of the row.  It is kept for the dK/dV kernel.  Padding rows: dO = 0 and
   // Delta = 0 give dS = 0 whatever P is.
-  const float dl = dpart + __shfl_xor(dpart, 32);
+  const float dl = wave_sum32(dpart);
   const float l2 = qvalid ? lse[(size_t)bh * N + qrow] * kLog2e : 0.f;
   // both statistics of every row of the block, padding rows (zeros) included
   stats[stat_lse2(bh, stat_groups(N), qrow) + 32 * h] = h ? dl : l2;

@@ -110,8 +110,26 @@ __device__ inline int xcd_remap(int id, int n) {
   return x * q + min(x, r) + local;
 }
 
+// v and the value of the lane 32 apart, in lane-dependent order, through
+// v_permlane32_swap (a VALU exchange of the two half-waves; no LDS trip).
+// Swapping the upper half of one copy with the lower half of another leaves
+// each lane holding its own value in one result and its partner's in the
+// other, so symmetric combinations need no select.
+__device__ inline void cross_half(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
 __device__ inline float wave_max32(float v) {  // max with the lane 32 apart
-  return fmaxf(v, __shfl_xor(v, 32));
+  float a, b;
+  cross_half(v, a, b);
+  return fmaxf(a, b);
+}
+__device__ inline float wave_sum32(float v) {  // sum with the lane 32 apart (same in both)
+  float a, b;
+  cross_half(v, a, b);
+  return a + b;
 }
 
 }  // namespace sa2
