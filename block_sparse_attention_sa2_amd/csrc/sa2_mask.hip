@@ -5,8 +5,8 @@
 // Kernels on the caller's stream:
 //   pool       q-bar / k-bar: fp64 means of each block's tokens (HBM stream)
 //   score      S-bar = q-bar k-bar^T / sqrt(d), fp64, 64x64 tiles
-//   select     one workgroup per query-block row: softmax, rank, cut, emit
-//              the bitmap row, row count and ascending row list
+//   select     one wave per query-block row: softmax, rank, cut, emit the
+//              bitmap row, row count and ascending row list
 //   columns    transposed lists (query blocks per key block), ascending
 //   order      optional work orders (longest lists first)
 // fp64 throughout keeps the ranking and the Top-p cut equal to an exact
@@ -140,101 +140,104 @@ __device__ inline double key_value(uint64_t k) {
   return __longlong_as_double((long long)b);
 }
 
-// Deterministic workgroup reductions (fixed combination order).
-__device__ inline double wg_max(double v, double* red) {
-  for (int off = 32; off > 0; off >>= 1) v = fmax(v, __shfl_xor(v, off));
-  const int w = threadIdx.x / 64;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[w] = v;
-  __syncthreads();
-  double r = red[0];
-  for (int i = 1; i < kMaskThreads / 64; ++i) r = fmax(r, red[i]);
-  return r;
-}
-__device__ inline double wg_sum(double v, double* red) {
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  const int w = threadIdx.x / 64;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[w] = v;
-  __syncthreads();
-  double r = red[0];
-  for (int i = 1; i < kMaskThreads / 64; ++i) r += red[i];
-  return r;
-}
-// Exclusive prefix over threads in thread order (values are small counts or
-// fp64 masses); returns this thread's exclusive prefix, total in *total.
-template <typename V>
-__device__ inline V wg_exclusive_scan(V v, V* buf, V* total) {
-  __syncthreads();
-  buf[threadIdx.x] = v;
-  __syncthreads();
-  // Hillis-Steele over kMaskThreads entries, in LDS
-  for (int off = 1; off < kMaskThreads; off <<= 1) {
-    V add = (threadIdx.x >= off) ? buf[threadIdx.x - off] : V(0);
-    __syncthreads();
-    buf[threadIdx.x] += add;
-    __syncthreads();
-  }
-  *total = buf[kMaskThreads - 1];
-  return buf[threadIdx.x] - v;
-}
-
 // "a is ranked before b": higher score, lower index on ties.
 __device__ inline bool ranks_before(uint64_t ka, uint32_t ia, uint64_t kb, uint32_t ib) {
   return ka > kb || (ka == kb && ia < ib);
 }
 
-// One workgroup per (b*h, query block) row.  Dynamic LDS: P2 keys (u64),
-// P2 indices (u32), Tk flags (u8), P2 = next power of two >= Tk.
-__global__ __launch_bounds__(kMaskThreads)
-void select_kernel(const double* __restrict__ sbar, int Tk, int P2, int kc, double p, int all,
-                   uint8_t* __restrict__ bitmap, int32_t* __restrict__ row_cnt,
-                   int32_t* __restrict__ row_idx) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  uint64_t* key = reinterpret_cast<uint64_t*>(smem);
-  uint32_t* idx = reinterpret_cast<uint32_t*>(key + P2);
-  uint8_t* flag = reinterpret_cast<uint8_t*>(idx + P2);
-  __shared__ double red[kMaskThreads / 64];
-  __shared__ double fscan[kMaskThreads];
-  __shared__ int iscan[kMaskThreads];
-  const int row = blockIdx.x;
-  const int tid = threadIdx.x;
+// ---------------------------------------------------------------------------
+// select, one wave per (b*h, query block) row.  The row's P2 = 64E ranking
+// entries (P2 = max(64, next power of two >= Tk)) live in registers: entry
+// i = E*lane + e in register e of lane i / E.  The bitonic network's strides
+// below E exchange registers within a lane; larger strides exchange lanes
+// (ds_bpermute), so the sort needs no LDS array and no barrier.  The wave's
+// row flags live in LDS (private to the wave).
+// ---------------------------------------------------------------------------
+constexpr int kSelectWaves = 4;
+
+__device__ inline uint32_t xor_lane(uint32_t v, int d) {
+  return (uint32_t)__shfl_xor((int)v, d);
+}
+
+// One compare-exchange of entries at network positions a < b = a + stride:
+// position a ends with the entry ranked first if `fwd`, else the other.
+__device__ inline void cx(uint64_t& ka, uint32_t& ia, uint64_t& kb, uint32_t& ib, bool fwd) {
+  if (fwd != ranks_before(ka, ia, kb, ib)) {
+    const uint64_t tk = ka; ka = kb; kb = tk;
+    const uint32_t ti = ia; ia = ib; ib = ti;
+  }
+}
+
+template <int E, int J>
+__device__ inline void in_lane_stage(uint64_t* key, uint32_t* idx, int lane, int kk) {
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if ((e & J) == 0) cx(key[e], idx[e], key[e + J], idx[e + J], ((lane * E + e) & kk) == 0);
+}
+
+template <int E>
+__global__ __launch_bounds__(64 * kSelectWaves)
+void select_wave_kernel(const double* __restrict__ sbar, int nrows, int Tk, int kc, double p,
+                        int all, uint8_t* __restrict__ bitmap, int32_t* __restrict__ row_cnt,
+                        int32_t* __restrict__ row_idx) {
+  constexpr int P2 = 64 * E;
+  __shared__ uint8_t flags_all[kSelectWaves][P2];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int row = blockIdx.x * kSelectWaves + wv;
+  if (row >= nrows) return;
+  uint8_t* flag = flags_all[wv];
   const double* s = sbar + (size_t)row * Tk;
 
   int c;
+  uint32_t idx[E];
   if (all) {
     c = Tk;
-    for (int j = tid; j < Tk; j += kMaskThreads) flag[j] = 1;
   } else {
-    // softmax statistics of the row
+    // this lane's entries E*lane .. E*lane+E-1 (padding past Tk ranks last)
+    uint64_t key[E];
     double mx = -INFINITY;
-    for (int j = tid; j < Tk; j += kMaskThreads) mx = fmax(mx, s[j]);
-    mx = wg_max(mx, red);
-    double z = 0.0;
-    for (int j = tid; j < Tk; j += kMaskThreads) z += exp(s[j] - mx);
-    z = wg_sum(z, red);
-    // rank: bitonic sort of (key, index) pairs, padding last
-    for (int j = tid; j < P2; j += kMaskThreads) {
-      key[j] = (j < Tk) ? order_key(s[j]) : 0ull;
-      idx[j] = (uint32_t)j;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int j = lane * E + e;
+      const double v = j < Tk ? s[j] : -INFINITY;
+      key[e] = j < Tk ? order_key(v) : 0ull;
+      idx[e] = (uint32_t)j;
+      mx = fmax(mx, v);
     }
-    for (int j = tid; j < Tk; j += kMaskThreads) flag[j] = 0;
-    __syncthreads();
+    for (int off = 32; off > 0; off >>= 1) mx = fmax(mx, __shfl_xor(mx, off));
+    double z = 0.0;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (lane * E + e < Tk) z += exp(key_value(key[e]) - mx);
+    for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off);
+
+    // bitonic sort into ranking order (descending score, ascending index)
     for (int kk = 2; kk <= P2; kk <<= 1) {
       for (int jj = kk >> 1; jj > 0; jj >>= 1) {
-        for (int t = tid; t < P2 / 2; t += kMaskThreads) {
-          const int a = (t / jj) * 2 * jj + (t % jj);
-          const int b = a + jj;
-          const uint64_t ka = key[a], kb = key[b];
-          const uint32_t ia = idx[a], ib = idx[b];
-          const bool fwd = (a & kk) == 0;
-          const bool a_first = ranks_before(ka, ia, kb, ib);
-          if (fwd != a_first) {
-            key[a] = kb; key[b] = ka;
-            idx[a] = ib; idx[b] = ia;
+        if (jj >= E) {
+          const int d = jj / E;                   // lane distance
+          const bool lower = (lane & d) == 0;
+          const bool fwd = ((lane * E) & kk) == 0;
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            const uint32_t plo = xor_lane((uint32_t)key[e], d);
+            const uint32_t phi = xor_lane((uint32_t)(key[e] >> 32), d);
+            const uint32_t pi = xor_lane(idx[e], d);
+            const uint64_t pk = ((uint64_t)phi << 32) | plo;
+            const bool mine_first = ranks_before(key[e], idx[e], pk, pi);
+            if (lower != (fwd == mine_first)) {
+              key[e] = pk;
+              idx[e] = pi;
+            }
           }
+        } else {
+          if constexpr (E >= 2) if (jj == 1) in_lane_stage<E, 1>(key, idx, lane, kk);
+          if constexpr (E >= 4) if (jj == 2) in_lane_stage<E, 2>(key, idx, lane, kk);
+          if constexpr (E >= 8) if (jj == 4) in_lane_stage<E, 4>(key, idx, lane, kk);
+          if constexpr (E >= 16) if (jj == 8) in_lane_stage<E, 8>(key, idx, lane, kk);
+          if constexpr (E >= 32) if (jj == 16) in_lane_stage<E, 16>(key, idx, lane, kk);
+          if constexpr (E >= 64) if (jj == 32) in_lane_stage<E, 32>(key, idx, lane, kk);
         }
-        __syncthreads();
       }
     }
     // Top-p count: ranks r whose running mass (through r) is still below p
@@ -242,39 +245,57 @@ void select_kernel(const double* __restrict__ sbar, int Tk, int P2, int kc, doub
     if (p >= 1.0) {
       pc = Tk;
     } else if (p > 0.0) {
-      const int per = (P2 + kMaskThreads - 1) / kMaskThreads;
-      const int r_lo = tid * per, r_hi = min(Tk, r_lo + per);
+      double mass[E];
       double local = 0.0;
-      for (int r = r_lo; r < r_hi; ++r) local += exp(key_value(key[r]) - mx) / z;
-      double tot;
-      double run = wg_exclusive_scan(local, fscan, &tot);
-      int below = 0;
-      for (int r = r_lo; r < r_hi; ++r) {
-        run += exp(key_value(key[r]) - mx) / z;
-        below += (run < p) ? 1 : 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int r = lane * E + e;
+        mass[e] = r < Tk ? exp(key_value(key[e]) - mx) / z : 0.0;
+        local += mass[e];
       }
-      int btot;
-      (void)wg_exclusive_scan(below, iscan, &btot);
-      pc = (btot < Tk) ? btot + 1 : Tk;
+      // exclusive scan of the lane totals over the wave
+      double incl = local;
+      for (int off = 1; off < 64; off <<= 1) {
+        const double up = __shfl_up(incl, off);
+        if (lane >= off) incl += up;
+      }
+      double run = incl - local;
+      int below = 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        run += mass[e];
+        below += (lane * E + e < Tk && run < p) ? 1 : 0;
+      }
+      for (int off = 32; off > 0; off >>= 1) below += __shfl_xor(below, off);
+      pc = below < Tk ? below + 1 : Tk;
     }
     c = max(kc, pc);
-    __syncthreads();
-    for (int r = tid; r < c; r += kMaskThreads) flag[idx[r]] = 1;
   }
-  __syncthreads();
-  // emit the bitmap row and the ascending row list
+  // flags by key block, then the bitmap row and the ascending row list
+  for (int j = lane; j < P2; j += 64) flag[j] = all && j < Tk ? 1 : 0;
+  wave_lds_sync();
+  if (!all) {
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (lane * E + e < c) flag[idx[e]] = 1;
+    wave_lds_sync();
+  }
   uint8_t* bm = bitmap + (size_t)row * Tk;
-  for (int j = tid; j < Tk; j += kMaskThreads) bm[j] = flag[j];
-  const int per = (Tk + kMaskThreads - 1) / kMaskThreads;
-  const int j_lo = tid * per, j_hi = min(Tk, j_lo + per);
+  for (int j = lane; j < Tk; j += 64) bm[j] = flag[j];
   int mine = 0;
-  for (int j = j_lo; j < j_hi; ++j) mine += flag[j];
-  int tot;
-  int pos = wg_exclusive_scan(mine, iscan, &tot);
+#pragma unroll
+  for (int e = 0; e < E; ++e) mine += flag[lane * E + e];
+  int pos = mine;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int up = __shfl_up(pos, off);
+    if (lane >= off) pos += up;
+  }
+  pos -= mine;
   int32_t* out = row_idx + (size_t)row * Tk;
-  for (int j = j_lo; j < j_hi; ++j)
-    if (flag[j]) out[pos++] = j;
-  if (tid == 0) row_cnt[row] = c;
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (flag[lane * E + e]) out[pos++] = lane * E + e;
+  if (lane == 0) row_cnt[row] = c;
 }
 
 // ---------------------------------------------------------------------------
@@ -448,11 +469,22 @@ extern "C" sa2_status sa2_build_mask(const void* q, const void* k, int dtype, in
 
   const int kc = topk_count(k_frac, Tk);
   const int all = (kc >= Tk || p >= 1.0) ? 1 : 0;
-  const int P2 = next_pow2(Tk);
-  const size_t lds = (size_t)P2 * (8 + 4) + ((Tk + 15) & ~15);
-  select_kernel<<<BH * Tq, kMaskThreads, lds, s>>>(sbar, Tk, P2, kc, p, all, m->bitmap,
-                                                   m->row_cnt, m->row_idx);
-  if (sa2_status st = check_launch("select_kernel")) return st;
+  const int P2 = max(64, next_pow2(Tk));
+  const int rows = BH * Tq, sgrid = cdiv(rows, kSelectWaves), sthreads = 64 * kSelectWaves;
+#define SA2_SELECT(E_)                                                                         \
+  select_wave_kernel<E_><<<sgrid, sthreads, 0, s>>>(sbar, rows, Tk, kc, p, all, m->bitmap,       \
+                                                   m->row_cnt, m->row_idx)
+  switch (P2 / 64) {
+    case 1: SA2_SELECT(1); break;
+    case 2: SA2_SELECT(2); break;
+    case 4: SA2_SELECT(4); break;
+    case 8: SA2_SELECT(8); break;
+    case 16: SA2_SELECT(16); break;
+    case 32: SA2_SELECT(32); break;
+    default: SA2_SELECT(64); break;
+  }
+#undef SA2_SELECT
+  if (sa2_status st = check_launch("select_wave_kernel")) return st;
 
   columns_kernel<<<dim3(cdiv(Tk, 64), BH), 256, 0, s>>>(m->bitmap, Tq, Tk, m->col_cnt,
                                                         m->col_idx);
