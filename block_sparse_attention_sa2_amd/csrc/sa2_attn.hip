@@ -914,22 +914,34 @@ void dkdv_pair_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
     row_nxt = slice_row(s + 2);
     const SwzAddr A = addr0.fresh();
 
-    // S = Q K^T and dP = dO V^T for the slice's 32 rows and this wave's keys
+    // S = Q K^T and dP = dO V^T for the slice's 32 rows and this wave's keys,
+    // the row fragments of step kk read two steps ahead
     f32x16 sa = zero16(), dpa = zero16();
+    {
+      bf16x8 qa[NK], oa[NK];
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-      sa = mfma32(rd_row(sq, A.row(0, kk)), kf[kk], sa);
-      dpa = mfma32(rd_row(so, A.row(0, kk)), vf[kk], dpa);
-    }
-    if (row0 + 32 > N) {  // the partial last query block: rows past N add nothing
-      const int lim = N - row0 - 4 * h;
+      for (int kk = 0; kk < NK; ++kk) {
+        qa[kk] = rd_row(sq, A.row(0, kk));
+        oa[kk] = rd_row(so, A.row(0, kk));
+      }
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        if (8 * (e >> 2) + (e & 3) >= lim) sa[e] = -INFINITY;
+      for (int kk = 0; kk < NK; ++kk) {
+        sa = mfma32(qa[kk], kf[kk], sa);
+        dpa = mfma32(oa[kk], vf[kk], dpa);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);    // reads of steps 0, 1
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMAs of step kk
+        if (kk + 2 < NK) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // reads of kk + 2
+      }
     }
+    __builtin_amdgcn_sched_barrier(0);
     // P and dS for rows 8g+4h+i, packed into the B operands of the two
-    // 16-row steps (keys past N need no mask: they only feed their own,
-    // unstored, dK and dV rows)
+    // 16-row steps.  No mask is needed: keys past N only feed their own,
+    // unstored, dK and dV rows; query rows past N arrive as zero Q and dO
+    // rows with zero statistics, so their P is exactly 1, their dS exactly 0,
+    // and both meet zero rows in the dV and dK products.
     bf16x8 pb[2], sb[2];
 #pragma unroll
     for (int gg = 0; gg < 4; ++gg) {
@@ -944,14 +956,30 @@ void dkdv_pair_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
         sb[t][o + i] = (__bf16)(pv * (dpa[e] - Dl[i]));
       }
     }
-    // dV^T += dO^T P and dK^T += Q^T dS over the slice's rows
+    // dV^T += dO^T P and dK^T += Q^T dS over the slice's rows; the
+    // transposed operands of a (t, db) step are read two steps ahead (in a
+    // scheduling region of their own, so that the reads are not hoisted into
+    // the S and dP phase, where their registers are taken)
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      bf16x8 ot[2 * ND], qt[2 * ND];
 #pragma unroll
-    for (int db = 0; db < ND; ++db)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        accv[db] = mfma32(rd_tr(so, A, t, db), pb[t], accv[db]);
-        acck[db] = mfma32(rd_tr(sq, A, t, db), sb[t], acck[db]);
+      for (int g = 0; g < 2 * ND; ++g) {
+        ot[g] = rd_tr(so, A, g / ND, g % ND);
+        qt[g] = rd_tr(sq, A, g / ND, g % ND);
       }
+#pragma unroll
+      for (int g = 0; g < 2 * ND; ++g) {
+        accv[g % ND] = mfma32(ot[g], pb[g / ND], accv[g % ND]);
+        acck[g % ND] = mfma32(qt[g], sb[g / ND], acck[g % ND]);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);    // DS reads of steps 0, 1
+#pragma unroll
+      for (int g = 0; g < 2 * ND; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMAs of step g
+        if (g + 2 < 2 * ND) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // reads of g + 2
+      }
+    }
   });
 
   // Element e of block db is d = 32db + 8(e/4) + 4h + e%4 at key 32kb + l32:
