@@ -72,12 +72,16 @@ void pool_kernel(const T* __restrict__ q, const T* __restrict__ k, int BH, int N
 }
 
 // ---------------------------------------------------------------------------
-// score: S-bar tile of 64 query blocks x 64 key blocks per workgroup.
+// score: S-bar tile of 64 query blocks x 64 key blocks per workgroup.  The d
+// dimension is walked in chunks of 32 staged in LDS; the next chunk's global
+// loads are issued before the current chunk's products, so their latency
+// overlaps the arithmetic.  Each product is one fp64 sum over d in order.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256)
 void score_kernel(const double* __restrict__ qbar, const double* __restrict__ kbar, int Tq,
                   int Tk, int d, double sqrt_d, double* __restrict__ sbar) {
-  constexpr int TK = 32;  // d chunk
+  constexpr int TK = 32;                 // d chunk
+  constexpr int PER = 64 * TK / 256;     // elements of each operand a thread stages per chunk
   __shared__ double qs[64][TK + 1];
   __shared__ double ks[64][TK + 1];
   const int bh = blockIdx.z;
@@ -90,14 +94,27 @@ void score_kernel(const double* __restrict__ qbar, const double* __restrict__ kb
   for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[a][c] = 0.0;
-  for (int c0 = 0; c0 < d; c0 += TK) {
-    for (int e = tid; e < 64 * TK; e += 256) {
-      const int r = e / TK, c = e % TK;
+  double qn[PER], kn[PER];
+  auto fetch = [&](int c0) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = tid + 256 * u, r = e / TK, c = e % TK;
       const int ii = i0 + r, jj = j0 + r, cc = c0 + c;
-      qs[r][c] = (ii < Tq && cc < d) ? qb[(size_t)ii * d + cc] : 0.0;
-      ks[r][c] = (jj < Tk && cc < d) ? kb[(size_t)jj * d + cc] : 0.0;
+      qn[u] = (ii < Tq && cc < d) ? qb[(size_t)ii * d + cc] : 0.0;
+      kn[u] = (jj < Tk && cc < d) ? kb[(size_t)jj * d + cc] : 0.0;
+    }
+  };
+  fetch(0);
+  for (int c0 = 0; c0 < d; c0 += TK) {
+    __syncthreads();   // the previous chunk's reads of qs / ks are done
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = tid + 256 * u, r = e / TK, c = e % TK;
+      qs[r][c] = qn[u];
+      ks[r][c] = kn[u];
     }
     __syncthreads();
+    if (c0 + TK < d) fetch(c0 + TK);
     const int kk_end = min(TK, d - c0);
     for (int kk = 0; kk < kk_end; ++kk) {
       double av[4], bv[4];
@@ -110,7 +127,6 @@ void score_kernel(const double* __restrict__ qbar, const double* __restrict__ kb
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[a][c] = fma(av[a], bv[c], acc[a][c]);
     }
-    __syncthreads();
   }
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
@@ -299,17 +315,20 @@ void select_wave_kernel(const double* __restrict__ sbar, int nrows, int Tk, int 
 }
 
 // ---------------------------------------------------------------------------
-// columns: workgroup per (b*h, 64 key blocks); thread (part, column) counts
-// its quarter of the query-block rows, then writes its entries at the prefix.
+// columns: workgroup per (b*h, 16 key blocks); thread (part, column) counts
+// its sixteenth of the query-block rows, then writes its entries at the
+// prefix of the parts before it, so each list comes out ascending.
 // ---------------------------------------------------------------------------
+constexpr int kColsPerGroup = 16, kColParts = 256 / kColsPerGroup;
+
 __global__ __launch_bounds__(256)
 void columns_kernel(const uint8_t* __restrict__ bitmap, int Tq, int Tk,
                     int32_t* __restrict__ col_cnt, int32_t* __restrict__ col_idx) {
-  __shared__ int cnt[4][64];
+  __shared__ int cnt[kColParts][kColsPerGroup];
   const int bh = blockIdx.y;
-  const int tid = threadIdx.x, c = tid % 64, part = tid / 64;
-  const int j = blockIdx.x * 64 + c;
-  const int per = (Tq + 3) / 4;
+  const int tid = threadIdx.x, c = tid % kColsPerGroup, part = tid / kColsPerGroup;
+  const int j = blockIdx.x * kColsPerGroup + c;
+  const int per = (Tq + kColParts - 1) / kColParts;
   const int i_lo = part * per, i_hi = min(Tq, i_lo + per);
   const uint8_t* bm = bitmap + (size_t)bh * Tq * Tk;
   int n = 0;
@@ -323,7 +342,7 @@ void columns_kernel(const uint8_t* __restrict__ bitmap, int Tq, int Tk,
   int32_t* out = col_idx + ((size_t)bh * Tk + j) * Tq;
   for (int i = i_lo; i < i_hi; ++i)
     if (bm[(size_t)i * Tk + j]) out[off++] = i;
-  if (part == 3) col_cnt[(size_t)bh * Tk + j] = off;
+  if (part == kColParts - 1) col_cnt[(size_t)bh * Tk + j] = off;
 }
 
 // ---------------------------------------------------------------------------
@@ -486,8 +505,8 @@ extern "C" sa2_status sa2_build_mask(const void* q, const void* k, int dtype, in
 #undef SA2_SELECT
   if (sa2_status st = check_launch("select_wave_kernel")) return st;
 
-  columns_kernel<<<dim3(cdiv(Tk, 64), BH), 256, 0, s>>>(m->bitmap, Tq, Tk, m->col_cnt,
-                                                        m->col_idx);
+  columns_kernel<<<dim3(cdiv(Tk, kColsPerGroup), BH), 256, 0, s>>>(m->bitmap, Tq, Tk,
+                                                                    m->col_cnt, m->col_idx);
   if (sa2_status st = check_launch("columns_kernel")) return st;
   if (orders) {
     order_kernel<<<16, kOrderThreads, 0, s>>>(m->row_cnt, BH * Tq, Tk, m->col_cnt, BH * Tk, Tq,
