@@ -236,3 +236,40 @@ class SparseAttention(torch.autograd.Function):
 
 def sparse_attention(q, k, v, mask: BlockMask):
     return SparseAttention.apply(q, k, v, mask)
+
+
+def distill_workspace_bytes(B, H, N, d) -> int:
+    return int(_lib.lib().sa2_distill_workspace_bytes(B, H, N, d))
+
+
+def distill_loss_grad(o_student, o_teacher, dout=None, loss=None, workspace=None):
+    """Layer-level velocity-distillation loss mean((o_s - o_t)^2) and its
+    gradient 2 (o_s - o_t) / numel (sa2_distill_loss_grad) -> (loss, dout);
+    loss is a one-element float64 device tensor."""
+    dt = _dtype_code(o_student, o_teacher)
+    B, H, N, d = _shape(o_student)
+    if _shape(o_teacher) != (B, H, N, d):
+        raise ValueError("o_student and o_teacher must have the same shape")
+    dout = torch.empty_like(o_student) if dout is None else dout
+    if loss is None:
+        loss = torch.empty((1,), dtype=torch.float64, device=o_student.device)
+    if workspace is None:
+        workspace = torch.empty(max(distill_workspace_bytes(B, H, N, d), 1), dtype=torch.uint8,
+                                device=o_student.device)
+    st = _lib.lib().sa2_distill_loss_grad(_ptr(o_student), _ptr(o_teacher), dt, B, H, N, d,
+                                          _ptr(dout), _ptr(loss), _ptr(workspace),
+                                          workspace.numel(), _stream(o_student.device))
+    check("sa2_distill_loss_grad", st)
+    return loss, dout
+
+
+def distill_step(q, k, v, mask: BlockMask, dense_mask: BlockMask):
+    """One layer-level velocity-distillation step: the teacher is the same
+    attention with every block kept (dense_mask), the student the sparse one
+    (mask).  Returns (loss, dq, dk, dv, o_student, o_teacher); the gradients
+    are those of the loss through the student, the teacher held fixed."""
+    o_t, _ = attn_fwd(q, k, v, dense_mask)
+    o_s, lse = attn_fwd(q, k, v, mask)
+    loss, dout = distill_loss_grad(o_s, o_t)
+    dq, dk, dv = attn_bwd(q, k, v, o_s, lse, dout, mask)
+    return loss, dq, dk, dv, o_s, o_t

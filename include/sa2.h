@@ -210,6 +210,28 @@ sa2_status sa2_attn_bwd_dkdv(const void* q, const void* k, const void* v,
                              const sa2_mask* mask, void* dk, void* dv,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Layer-level velocity distillation (gist.science, section 2B: the student,
+ * with sparse attention, is fitted to the frozen full-attention teacher by
+ * the squared difference of their outputs).  At the level of one attention
+ * layer the student output is o_student (sa2_attn_fwd with the hybrid mask)
+ * and the teacher output o_teacher (the same call with every block kept):
+ *
+ *   loss = sum over all B*H*N*d elements of (o_student - o_teacher)^2 / (B*H*N*d)
+ *   dout = d loss / d o_student = 2 (o_student - o_teacher) / (B*H*N*d)
+ *
+ * dout (written, [B, H, N, d] in `dtype`) is the upstream gradient for
+ * sa2_attn_bwd on the student's mask; loss is one fp64 value written to device
+ * memory.  The sum is taken in fp64 in a fixed order (per-chunk partial sums
+ * in the workspace, then one ordered sum), so it is bitwise reproducible.
+ * o_student, o_teacher, dout: 16-byte aligned; workspace: at least
+ * sa2_distill_workspace_bytes() bytes, 256-byte aligned.
+ */
+size_t sa2_distill_workspace_bytes(int B, int H, int N, int d);
+sa2_status sa2_distill_loss_grad(const void* o_student, const void* o_teacher, int dtype,
+                                 int B, int H, int N, int d, void* dout, double* loss,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

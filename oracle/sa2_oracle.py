@@ -357,3 +357,36 @@ def dkdv_key_block(Q, K, V, dO, row_lists, bq, bk, j):
         dV += P[:, sel].T @ dO[lo:hi]
         dK += dS[:, sel].T @ Q[lo:hi] / math.sqrt(d)
     return dK, dV
+
+
+# ---------------------------------------------------------------------------
+# Layer-level velocity distillation (gist.science, section 2B): the sparse
+# student is fitted to the frozen full-attention teacher by the squared
+# difference of their outputs.  At one attention layer the student output is
+# the block-sparse attention and the teacher output the dense attention of the
+# same Q, K, V; the expectation of the squared norm is taken as the mean over
+# all output elements (a reading: the pages state the objective over a whole
+# model's velocity prediction).
+# ---------------------------------------------------------------------------
+def distill_loss_grad(O_student: np.ndarray, O_teacher: np.ndarray):
+    """loss = mean((O_s - O_t)^2); dO = d loss / d O_s = 2 (O_s - O_t) / numel."""
+    diff = np.asarray(O_student, dtype=np.float64) - np.asarray(O_teacher, dtype=np.float64)
+    n = diff.size
+    return float((diff * diff).sum() / n), 2.0 * diff / n
+
+
+def distill_step(Q, K, V, row_lists, bq, bk, O_teacher=None):
+    """One layer-level distillation step on one head: the teacher output (dense
+    attention unless given), the student forward over ``row_lists``, the loss,
+    its gradient dO and the student's dQ, dK, dV for that dO (teacher fixed).
+
+    Returns loss, dQ, dK, dV, O_student, O_teacher.
+    """
+    N, d = Q.shape
+    if O_teacher is None:
+        Tq, Tk = n_blocks(N, bq), n_blocks(N, bk)
+        O_teacher, _ = attention_gathered(Q, K, V, [np.arange(Tk)] * Tq, bq, bk)
+    O_s, _ = attention_gathered(Q, K, V, row_lists, bq, bk)
+    loss, dO = distill_loss_grad(O_s, O_teacher)
+    _, _, dQ, dK, dV = attention_gathered(Q, K, V, row_lists, bq, bk, dO=dO)
+    return loss, dQ, dK, dV, O_s, O_teacher

@@ -106,3 +106,27 @@ def test_python_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 1, 64, 64)
     with pytest.raises(ValueError):
         sa2.build_mask(q, q, 64, 64, 0.5, 0.5)
+
+
+def test_distill_validation():
+    L = _lib.lib()
+    assert L.sa2_distill_workspace_bytes(1, 2, 64, 64) >= 8
+    assert L.sa2_distill_workspace_bytes(0, 2, 64, 64) == 0
+    ws = ctypes.c_void_p(1 << 20)
+    loss = ctypes.c_void_p(1 << 20)
+    call = lambda **kw: L.sa2_distill_loss_grad(
+        kw.get("s", FAKE), kw.get("t", FAKE), kw.get("dt", 0), 1, 2, kw.get("N", 64),
+        kw.get("d", 64), kw.get("o", FAKE), loss, kw.get("ws", ws), kw.get("wsb", 1 << 20), None)
+    cases = [
+        (dict(s=None), _lib.SA2_EINVAL),
+        (dict(dt=5), _lib.SA2_EINVAL),
+        (dict(d=12), _lib.SA2_EUNSUPPORTED),
+        (dict(N=0), _lib.SA2_EINVAL),
+        (dict(o=ctypes.c_void_p((1 << 20) + 8)), _lib.SA2_EINVAL),
+        (dict(ws=ctypes.c_void_p((1 << 20) + 16)), _lib.SA2_EINVAL),
+        (dict(wsb=8), _lib.SA2_EINVAL),
+    ]
+    for kw, want in cases:
+        st, msg = _status_and_msg(call(**kw))
+        assert st == want, (kw, st, msg)
+        assert msg.startswith("sa2_distill_loss_grad"), msg

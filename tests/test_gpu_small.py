@@ -203,3 +203,37 @@ def test_autograd_wrapper():
     for g, want, name in zip((q.grad, k.grad, v.grad), O.attention_dense_bwd(Q, K, V, dO, P),
                              ("dq", "dk", "dv")):
         check_grad(f64(g[0, 0]), want, name)
+
+
+@pytest.mark.parametrize("wname,k_frac,p", [("c0", 0.25, 0.0), ("c0c", 0.125, 0.3)])
+def test_distillation_step(wname, k_frac, p):
+    """Layer-level velocity distillation (gist.science 2B): the sparse student
+    fitted to the dense teacher.  Loss within 2e-2 relative and the gradients
+    within the backward bar of the oracle's step on the same masks."""
+    w = W.WORKLOADS[wname]
+    _say(f"[case] distill {w.name} k{k_frac} p{p}")
+    dev, ref = device_inputs(w)
+    q, k, v = dev["q"], dev["k"], dev["v"]
+    mask = sa2.build_mask(q, k, w.bq, w.bk, k_frac, p)
+    dense = sa2.build_mask(q, k, w.bq, w.bk, 1.0, 0.0)
+    loss, dq, dk, dv, o_s, o_t = sa2.distill_step(q, k, v, mask, dense)
+    torch.cuda.synchronize()
+    assert dense.density() == 1.0
+    rc, ri = mask.row_cnt.cpu().numpy(), mask.row_idx.cpu().numpy()
+    total = 0.0
+    grads = []
+    for h in range(w.H):
+        rows = [ri[0, h, i, :rc[0, h, i]] for i in range(rc.shape[2])]
+        Q, K, V = (ref[t][0, h] for t in ("q", "k", "v"))
+        lh, gq, gk, gv, _, _ = O.distill_step(Q, K, V, rows, w.bq, w.bk)
+        total += lh
+        grads.append((gq, gk, gv))
+    want = total / w.H                     # the mean over every element of every head
+    got = float(loss.item())
+    assert abs(got - want) <= 2e-2 * want, (got, want)
+    # the oracle's per-head gradients are of its per-head mean; the step's loss
+    # is the mean over all H heads, so its gradients are 1/H of those
+    for h in range(w.H):
+        for name, mine, g in (("dq", dq, grads[h][0]), ("dk", dk, grads[h][1]),
+                              ("dv", dv, grads[h][2])):
+            check_grad(f64(mine[0, h]), g / w.H, f"distill {w.name} h{h} {name}")

@@ -362,3 +362,62 @@ def test_per_block_functions_match_the_whole_head():
         lo, hi = O.block_range(j, bk, N)
         k_j, v_j = O.dkdv_key_block(Q, K, V, dO, rows, bq, bk, j)
         assert np.abs(k_j - dK[lo:hi]).max() < 1e-12 and np.abs(v_j - dV[lo:hi]).max() < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# Layer-level velocity distillation (gist.science, section 2B)
+# ---------------------------------------------------------------------------
+def _rows_from_bitmap(bm):
+    return [np.flatnonzero(r) for r in bm]
+
+
+def test_distill_gradient_is_derivative_of_loss():
+    """dO = 2 (O_s - O_t) / numel is d loss / d O_s (central differences)."""
+    Os, Ot = _rand((40, 8), 50), _rand((40, 8), 51)
+    loss, dO = O.distill_loss_grad(Os, Ot)
+    assert loss == pytest.approx(float(((Os - Ot) ** 2).mean()), rel=1e-15)
+    h = 1e-6
+    for t, c in ((0, 0), (7, 3), (39, 7)):
+        up, dn = Os.copy(), Os.copy()
+        up[t, c] += h
+        dn[t, c] -= h
+        fd = (O.distill_loss_grad(up, Ot)[0] - O.distill_loss_grad(dn, Ot)[0]) / (2 * h)
+        assert abs(fd - dO[t, c]) <= 1e-9
+
+
+def test_distill_step_finite_differences():
+    """Gradients of the whole distillation step (student through the sparse
+    attention, teacher held fixed) against central differences of its loss."""
+    N, d, b = 128, 16, 32
+    Q, K, V = (_rand((N, d), s) for s in (60, 61, 62))
+    bm = np.zeros((4, 4), np.uint8)
+    bm[np.arange(4), np.arange(4)] = 1
+    bm[np.arange(4), (np.arange(4) + 2) % 4] = 1
+    rows = _rows_from_bitmap(bm)
+    loss, dQ, dK, dV, Os, Ot = O.distill_step(Q, K, V, rows, b, b)
+    assert loss > 1e-3                                   # the sparse student differs
+    def loss_of(q, k, v):
+        return O.distill_step(q, k, v, rows, b, b, O_teacher=Ot)[0]
+    rng = np.random.default_rng(3)
+    h = 1e-6
+    for which, g in zip(range(3), (dQ, dK, dV)):
+        for _ in range(5):
+            t, c = int(rng.integers(N)), int(rng.integers(d))
+            args = [Q.copy(), K.copy(), V.copy()]
+            args[which][t, c] += h
+            up = loss_of(*args)
+            args[which][t, c] -= 2 * h
+            dn = loss_of(*args)
+            fd = (up - dn) / (2 * h)
+            assert abs(fd - g[t, c]) <= 1e-7 * max(1.0, abs(g[t, c])) + 1e-10, (which, t, c)
+
+
+def test_distill_with_every_block_kept_is_zero():
+    """Student = teacher when the mask keeps every block: loss and gradients 0."""
+    N, d, b = 96, 8, 32
+    Q, K, V = (_rand((N, d), s) for s in (70, 71, 72))
+    rows = [np.arange(3)] * 3
+    loss, dQ, dK, dV, Os, Ot = O.distill_step(Q, K, V, rows, b, b)
+    assert loss <= 1e-28
+    for g in (dQ, dK, dV):
+        assert np.abs(g).max() <= 1e-14
