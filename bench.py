@@ -10,15 +10,20 @@ N=32760 (21x30x52 latent grid), d=128, bf16, q-block 128, k-block 64,
 k = 3% plus Top-p tuned to 5% density (95% sparsity), forward + backward.
 
 Prints one JSON line (stdout).  Effective FLOPs follow the FlashAttention
-convention: forward 4 N^2 d H density, forward+backward 3.5x that.
+convention: forward 4 N^2 d H density, forward+backward 3.5x that.  Beside
+the headline figures the line carries the dense baseline (the same kernels
+with every block kept), the same layer with 64 x 64 blocks, and the fp64
+oracle timed on the host.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+    python bench.py --sweep variants   # mask rules at equal density, one line per case
 """
 from __future__ import annotations
 
 import argparse
 import hashlib
 import json
+import math
 import os
 import platform
 import sys
@@ -76,6 +81,13 @@ def parse():
     ap.add_argument("--cpu-heads", type=int, default=12, help="heads the oracle times (default: the whole layer)")
     ap.add_argument("--no-work-order", action="store_true",
                     help="schedule the attention kernels in their fixed order")
+    ap.add_argument("--sweep", choices=["variants"], default=None,
+                    help="instead of the benchmark line: the mask-rule sweep (one JSON line "
+                         "per regime, density and Top-k share; --steps timed steps each)")
+    ap.add_argument("--regimes", default=None, help="comma-separated subset of the sweep's "
+                    "score regimes (sink, uniform, smooth)")
+    ap.add_argument("--no-second-geometry", action="store_true",
+                    help="skip the 64 x 64-block run of the same layer")
     ap.add_argument("--no-dense-baseline", action="store_true",
                     help="skip the dense (all blocks kept) run of the same kernels")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -154,6 +166,153 @@ def dense_baseline(sa2, q, k, v, do, w, sparse_attn_ms, args):
                     "attention time (forward + backward, mask excluded)"}
 
 
+def second_geometry(sa2, W, q, k, v, do, name="c2_b64", warmup=3, steps=10):
+    """The same layer and inputs with square 64 x 64 blocks (its own tuned p for
+    the same 5% density): mask + forward + backward, per-stage times."""
+    import numpy as np
+    import torch
+    w = W.WORKLOADS[name]
+    k_frac, p = W.tuned_params(name)
+    B, H, N, d = q.shape
+    dev = q.device
+    mask = sa2.BlockMask(B, H, N, w.bq, w.bk, dev, work_order=True)
+    mws = torch.empty(sa2.mask_workspace_bytes(B, H, N, d, w.bq, w.bk), dtype=torch.uint8, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    bws = torch.empty(sa2.bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    times = []
+    for it in range(warmup + steps):
+        ev[0].record()
+        sa2.build_mask(q, k, w.bq, w.bk, k_frac, p, mask=mask, workspace=mws)
+        ev[1].record()
+        sa2.attn_fwd(q, k, v, mask, o=o, lse=lse)
+        ev[2].record()
+        sa2.attn_bwd_dq(q, k, v, o, lse, do, mask, bws, dq=dq)
+        ev[3].record()
+        sa2.attn_bwd_dkdv(q, k, v, lse, do, mask, bws, dk=dk, dv=dv)
+        ev[4].record()
+        torch.cuda.synchronize()
+        if it >= warmup:
+            times.append([ev[i].elapsed_time(ev[i + 1]) for i in range(4)])
+    t = np.mean(np.array(times), axis=0)
+    density = mask.density()
+    ms = float(t.sum())
+    eff = 14.0 * N * N * d * H * B * density
+    return {"bq": w.bq, "bk": w.bk, "k_frac": k_frac, "p": p, "density": round(density, 5),
+            "ms_per_step": round(ms, 4), "effective_tflops": round(eff / (ms * 1e-3) / 1e12, 1),
+            "stages_ms": {st: round(float(x), 4) for st, x in
+                          zip(("mask", "fwd", "bwd_dq", "bwd_dkdv"), t)},
+            "note": "same inputs, 64 x 64 blocks, p tuned for the same density; "
+                    "sum of per-stage event times"}
+
+
+def _density_for(sa2, q, k, bq, bk, k_frac, target, mask, mws, steps=30):
+    """p for which the hybrid mask with this k_frac has `target` density (the
+    library's own masks, bisected on the host); (p, density, reached)."""
+    def dens(p):
+        sa2.build_mask(q, k, bq, bk, k_frac, p, mask=mask, workspace=mws)
+        return mask.density()
+    if k_frac > 0 and dens(0.0) >= target:
+        return 0.0, dens(0.0), True
+    top = dens(0.999)
+    if top < target:
+        return 0.999, top, False
+    lo, hi, best = 0.0, 0.999, (0.999, top)
+    for _ in range(steps):
+        mid = 0.5 * (lo + hi)
+        dm = dens(mid)
+        if abs(dm - target) < abs(best[1] - target):
+            best = (mid, dm)
+        if abs(dm - target) <= 0.02 * target:
+            break
+        lo, hi = (mid, hi) if dm < target else (lo, mid)
+    return best[0], best[1], True
+
+
+def variant_sweep(args):
+    """Mask rules at equal density over the three score regimes of the
+    mask-rule stress workloads (H=8, N=16384, d=128, bf16; attention sink,
+    near-uniform, smooth): Top-k only, Top-p only and hybrids whose Top-k
+    share r = k_frac / density runs from 0 (Top-p only) to 1 (Top-k only),
+    p tuned on the library's own masks to the target density.  Per case: the
+    density reached, mask + forward + backward time, effective TFLOPS, and how
+    far the sparse output is from the dense one (the layer-level distillation
+    loss, mean squared difference, and the relative Frobenius error).
+    One JSON line per case on stdout."""
+    import numpy as np
+    import torch
+
+    import block_sparse_attention_sa2_amd as sa2
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    ratios = (0.0, 0.25, 0.5, 0.6, 0.75, 1.0)
+    for regime in (args.regimes.split(",") if args.regimes else W.C4_REGIMES):
+        w = W.WORKLOADS[f"c4_{regime}_05"]
+        log(f"[sweep] generating {regime} inputs")
+        x = W.make_inputs(w)
+        q, k, v, do = (W.to_device_dtype(x[t], w.dtype).to(dev) for t in ("q", "k", "v", "do"))
+        del x
+        B, H, N, d = q.shape
+        mask = sa2.BlockMask(B, H, N, w.bq, w.bk, dev, work_order=True)
+        mws = torch.empty(sa2.mask_workspace_bytes(B, H, N, d, w.bq, w.bk), dtype=torch.uint8,
+                          device=dev)
+        bws = torch.empty(sa2.bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
+        o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        dense = sa2.BlockMask(B, H, N, w.bq, w.bk, dev, work_order=True)
+        sa2.build_mask(q, k, w.bq, w.bk, 1.0, 0.0, mask=dense, workspace=mws)
+        o_dense, _ = sa2.attn_fwd(q, k, v, dense)
+        ref_norm = float(o_dense.float().norm())
+        for D in W.C4_DENSITIES:
+            for r in ratios:
+                k_frac = round(r * D, 6)
+                if r >= 1.0:
+                    p, dens, reached = 0.0, None, True
+                else:
+                    p, dens, reached = _density_for(sa2, q, k, w.bq, w.bk, k_frac, D, mask, mws)
+                # steps queued back to back, one synchronisation at the end; the
+                # median per stage is robust to a stalled host thread
+                evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)]
+                       for _ in range(2 + args.steps)]
+                for ev in evs:
+                    ev[0].record()
+                    sa2.build_mask(q, k, w.bq, w.bk, k_frac, p, mask=mask, workspace=mws)
+                    ev[1].record()
+                    sa2.attn_fwd(q, k, v, mask, o=o, lse=lse)
+                    ev[2].record()
+                    sa2.attn_bwd_dq(q, k, v, o, lse, do, mask, bws, dq=dq)
+                    ev[3].record()
+                    sa2.attn_bwd_dkdv(q, k, v, lse, do, mask, bws, dk=dk, dv=dv)
+                    ev[4].record()
+                torch.cuda.synchronize()
+                times = [[ev[i].elapsed_time(ev[i + 1]) for i in range(4)] for ev in evs[2:]]
+                stage = np.median(np.array(times), axis=0)
+                ms = float(stage.sum())
+                ccnt = mask.col_cnt.reshape(-1).float()
+                rcnt = mask.row_cnt.reshape(-1).float()
+                dens = mask.density()
+                loss, _ = sa2.distill_loss_grad(o, o_dense)
+                loss = float(loss.item())
+                rule = "top-p only" if r == 0 else "top-k only" if r >= 1 else "hybrid"
+                print(json.dumps({
+                    "regime": regime, "target_density": D, "rule": rule, "topk_share": r,
+                    "k_frac": k_frac, "p": round(p, 6), "density": round(dens, 5),
+                    "target_reached": reached and abs(dens - D) <= 0.05 * D,
+                    "ms_mask_fwd_bwd": round(ms, 4),
+                    "stages_ms": {st: round(float(x), 4) for st, x in
+                                  zip(("mask", "fwd", "bwd_dq", "bwd_dkdv"), stage)},
+                    "row_cnt_max": int(rcnt.max()), "col_cnt_max": int(ccnt.max()),
+                    "pairs_per_block_mean": round(float(rcnt.mean()), 2),
+                    "effective_tflops": round(14.0 * N * N * d * H * B * dens / (ms * 1e-3) / 1e12, 1),
+                    "distill_loss": loss,
+                    "rel_err_vs_dense": math.sqrt(loss * o.numel()) / ref_norm}), flush=True)
+        del q, k, v, do, o, dq, dk, dv, o_dense
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.copy_probe:
@@ -163,6 +322,9 @@ def main():
         print("bench.py runs on one GPU only: the hot path is measured per GPU (heads shard "
               "with no exchange); run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.sweep == "variants":
+        variant_sweep(args)
+        return
 
     import numpy as np
     import torch
@@ -253,7 +415,9 @@ def main():
     attn_ms = sum(per[st] for st in kernels)
 
     out = {
-        "metric": "effective TFLOPS + ms/layer fwd+bwd, 95% sparse, H=12 N=32760 d=128 bf16",
+        "metric": (f"effective TFLOPS + ms/layer {'fwd+bwd' if backward else 'fwd'}, "
+                   f"{round(100 * (1 - (w.target_density or density)))}% sparse, "
+                   f"H={H} N={N} d={d} {w.dtype}"),
         "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
@@ -270,6 +434,8 @@ def main():
     }
     if not args.no_dense_baseline and backward:
         out["dense_baseline"] = dense_baseline(sa2, q, k, v, do, w, attn_ms, args)
+    if args.workload == "c2" and not args.no_second_geometry:
+        out["second_geometry"] = second_geometry(sa2, W, q, k, v, do)
     if not args.no_cpu_baseline:
         log(f"[bench] timing the oracle on {args.cpu_heads} head(s)")
         ref1 = {k_: v_ for k_, v_ in ref.items()}

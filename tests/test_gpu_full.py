@@ -2,7 +2,8 @@
 benchmark times (one call per step over all heads).
 
 * Wan2.1-1.3B-shaped layer (H=12, N=32760 = 21x30x52, d=128, bf16, q-block
-  128, k-block 64, k = 3%, p tuned for 5% density), forward and backward:
+  128, k-block 64, k = 3%, p tuned for 5% density), forward and backward,
+  and the same layer in a second block geometry (64 x 64 blocks):
   the whole mask of every head against the oracle; O, LSE, dQ, dK, dV on
   sampled blocks of every head (first, a random interior one, the ragged
   last one); closed-form invariants of the gradients on every head.
@@ -91,11 +92,11 @@ def _invariants(q, k, dq, dk, dv, do, h):
 # Wan2.1-1.3B-shaped layer, forward + backward
 # ---------------------------------------------------------------------------
 
-@pytest.fixture(scope="module")
-def wan13():
-    w = W.WORKLOADS["c2"]
-    k_frac, p = W.tuned_params("c2")
-    _say(f"[wan1.3B] generating inputs H{w.H} N{w.N} d{w.d}")
+@pytest.fixture(scope="module", params=["c2", "c2_b64"], ids=["bq128_bk64", "bq64_bk64"])
+def wan13(request):
+    w = W.WORKLOADS[request.param]
+    k_frac, p = W.tuned_params(request.param)
+    _say(f"[wan1.3B] generating inputs H{w.H} N{w.N} d{w.d} bq{w.bq} bk{w.bk}")
     dev, ref = device_inputs(w)
     q, k, v, do = (dev[t] for t in ("q", "k", "v", "do"))
     mask = sa2.build_mask(q, k, w.bq, w.bk, k_frac, p)
@@ -221,6 +222,11 @@ def test_stress_union_and_oracle(name, stress_inputs):
     bm = hy_bm.cpu().numpy()
     hm = O.build_mask_head(ref["q"][0, 0], ref["k"][0, 0], w.bq, w.bk, k_frac, p)
     compare_mask(hm, bm[0, 0], p)
+    # each rule on its own, as a mode of its own, against the oracle
+    ko_h = O.build_mask_head(ref["q"][0, 0], ref["k"][0, 0], w.bq, w.bk, k_frac, 0.0)
+    compare_mask(ko_h, ko.cpu().numpy()[0, 0], 0.0)
+    po_h = O.build_mask_head(ref["q"][0, 0], ref["k"][0, 0], w.bq, w.bk, 0.0, p)
+    compare_mask(po_h, po.cpu().numpy()[0, 0], p)
     _spot_check(w, ref, 0, bm[0, 0], o, lse, grads, np.random.default_rng(2))
     dens = hy.density()
     want = W.tuned_record(name)["density"]

@@ -85,6 +85,9 @@ WORKLOADS: dict[str, Workload] = {
                    target_density=0.05, grid=(21, 30, 52), backward=False),
     "c2": Workload("c2", 1, 12, 32760, 128, 128, 64, "smooth", 1, "bf16", 0.03, None,
                    target_density=0.05, grid=(21, 30, 52), backward=True),
+    # the 1.3B layer with square 64 x 64 blocks (a second block geometry)
+    "c2_b64": Workload("c2_b64", 1, 12, 32760, 128, 64, 64, "smooth", 1, "bf16", 0.03, None,
+                       target_density=0.05, grid=(21, 30, 52), backward=True),
     "c3": Workload("c3", 1, 40, 75600, 128, 128, 64, "smooth", 3, "bf16", 0.03, None,
                    target_density=0.05, grid=(21, 45, 80), backward=True),
 }
