@@ -279,6 +279,143 @@ void fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
 }
 
 // ---------------------------------------------------------------------------
+// dK/dV work plan.  A key block's column list is walked by one workgroup, so
+// a long list (an attention sink is kept by every query block) would set the
+// kernel's time by itself.  The plan cuts every list longer than L into
+// nearly equal segments; a segment's workgroup writes fp32 partial dK, dV to
+// a slot of the workspace and counts itself done on the block's completion
+// counter; the workgroup that finds itself last adds the block's partials in
+// segment order and writes dK, dV.  Values are never accumulated atomically
+// and the order of the sum is fixed, so results are reproducible bit for bit;
+// no workgroup waits for another.
+//
+// L is the larger of kMinSegment and twice the mean load of the kernel's
+// resident workgroups (kDkdvSlots), so that only lists that would set the
+// kernel's time are cut (each cut costs a partial write, a device-scope
+// release and the final sum), and per XCD share at least
+// total / kShareExtra, which bounds a share's extra segments by kShareExtra
+// and its partial slots by 2 kShareExtra.
+//
+// Items, in the workspace as int4 {block, first list entry, entries, -1 or
+// split entry * 1024 + segment}; item j of XCD x sits at 8j + x (the
+// workgroup slots that run on XCD x), longest first; unused items have block
+// -1.  Each XCD takes the contiguous share of blocks that xcd_remap gives it,
+// so its L2 sees a narrow band of heads.  Split entries: int4 {block, first
+// partial slot, segments}, kShareExtra per XCD share, with one completion
+// counter each, which the plan zeroes.
+// ---------------------------------------------------------------------------
+constexpr int kDkdvSlots = 1024;     // 256 CUs x 4 resident dK/dV workgroups
+constexpr int kMinSegment = 8;
+constexpr int kFairShares = 2;       // lists up to this many mean loads stay whole
+constexpr int kShareExtra = 128;     // extra segments (and split blocks) per XCD share
+constexpr int kPlanBuckets = 4096;   // list lengths are ranked by min(length, 4095)
+constexpr int kPlanWorkgroups = 8;   // one per XCD share
+constexpr size_t kPartialFloats = 2 * 64 * 128;   // dV and dK of one key block
+
+__host__ __device__ inline int plan_items_per_xcd(int ncols) {
+  return (ncols + 7) / 8 + kShareExtra;
+}
+
+// The plan of XCD share x, by one workgroup of nt threads (a multiple of 64).
+// LDS: hist[kPlanBuckets] ints, scan[nt] ints, red[nt / 64] 64-bit sums,
+// ctr[2] ints.
+__device__ void dkdv_plan_share(int x, const int32_t* __restrict__ col_cnt, int ncols,
+                                int4* __restrict__ items, int4* __restrict__ splits,
+                                int* __restrict__ done, int* hist, int* scan, long long* red,
+                                int* ctr) {
+  const int tid = threadIdx.x, nt = blockDim.x, nw = nt / 64;
+  const int qn = ncols / 8, rn = ncols % 8;
+  const int c0 = x * qn + min(x, rn), len = qn + (x < rn ? 1 : 0);
+
+  // totals over all blocks and over this share
+  long long all = 0, mine = 0;
+  for (int c = tid; c < ncols; c += nt) {
+    const int n = col_cnt[c];
+    all += n;
+    if (c >= c0 && c < c0 + len) mine += n;
+  }
+  for (int off = 32; off > 0; off >>= 1) {
+    all += __shfl_xor(all, off);
+    mine += __shfl_xor(mine, off);
+  }
+  if ((tid & 63) == 0) red[tid >> 6] = all;
+  __syncthreads();
+  long long total = 0;
+  for (int w = 0; w < nw; ++w) total += red[w];
+  __syncthreads();
+  if ((tid & 63) == 0) red[tid >> 6] = mine;
+  for (int c = tid; c < kPlanBuckets; c += nt) hist[c] = 0;
+  if (tid == 0) ctr[0] = ctr[1] = 0;
+  __syncthreads();
+  long long share = 0;
+  for (int w = 0; w < nw; ++w) share += red[w];
+  const long long Lg =
+      max((long long)kMinSegment, kFairShares * ((total + kDkdvSlots - 1) / kDkdvSlots));
+  const int L = (int)max(Lg, (share + kShareExtra - 1) / kShareExtra);
+  auto nseg = [&](int n) { return n > L ? (n + L - 1) / L : 1; };
+  auto seg = [&](int n, int ns, int s, int& start) {
+    const int base = n / ns, rem = n % ns;
+    start = s * base + min(s, rem);
+    return base + (s < rem ? 1 : 0);
+  };
+  auto bucket = [](int ln) { return min(ln, kPlanBuckets - 1); };
+
+  // histogram of segment lengths, then first position of each bucket in
+  // descending order (as in the mask's work orders)
+  for (int j = tid; j < len; j += nt) {
+    const int n = col_cnt[c0 + j], ns = nseg(n);
+    for (int s2 = 0; s2 < ns; ++s2) {
+      int st;
+      atomicAdd(&hist[bucket(seg(n, ns, s2, st))], 1);
+    }
+  }
+  __syncthreads();
+  const int per = kPlanBuckets / nt;   // nt divides kPlanBuckets
+  const int lo = tid * per, hi = lo + per;
+  int local = 0;
+  for (int r = lo; r < hi; ++r) local += hist[kPlanBuckets - 1 - r];
+  scan[tid] = local;
+  __syncthreads();
+  for (int off = 1; off < nt; off <<= 1) {
+    const int add = tid >= off ? scan[tid - off] : 0;
+    __syncthreads();
+    scan[tid] += add;
+    __syncthreads();
+  }
+  const int nitems = scan[nt - 1];
+  int run = scan[tid] - local;
+  for (int r = lo; r < hi; ++r) {
+    const int c = kPlanBuckets - 1 - r;
+    const int h = hist[c];
+    hist[c] = run;
+    run += h;
+  }
+  __syncthreads();
+  for (int j = tid; j < len; j += nt) {
+    const int col = c0 + j, n = col_cnt[col], ns = nseg(n);
+    int entry = -1;
+    if (ns > 1) {
+      const int p0 = 2 * kShareExtra * x + atomicAdd(&ctr[1], ns);
+      entry = kShareExtra * x + atomicAdd(&ctr[0], 1);
+      splits[entry] = make_int4(col, p0, ns, 0);
+    }
+    for (int s2 = 0; s2 < ns; ++s2) {
+      int st;
+      const int ln = seg(n, ns, s2, st);
+      items[8 * atomicAdd(&hist[bucket(ln)], 1) + x] =
+          make_int4(col, st, ln, ns > 1 ? entry * 1024 + s2 : -1);
+    }
+  }
+  __syncthreads();
+  const int J = plan_items_per_xcd(ncols);
+  for (int j = nitems + tid; j < J; j += nt) items[8 * j + x] = make_int4(-1, 0, 0, -1);
+  for (int j = ctr[0] + tid; j < kShareExtra; j += nt)
+    splits[kShareExtra * x + j] = make_int4(-1, 0, 0, 0);
+  for (int j = tid; j < kShareExtra; j += nt) done[kShareExtra * x + j] = 0;
+}
+
+
+// ---------------------------------------------------------------------------
 // Asynchronous tile copies (bf16, d = 128), global -> LDS through buffer
 // resources.  Rows of 256 bytes are copied in groups of four: lane l's 16
 // bytes of group i land in LDS unit 64i + l, i.e. row 4i + l/16 and unit
@@ -506,15 +643,28 @@ void dq_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                      float* __restrict__ stats, const int32_t* __restrict__ row_cnt,
                      const int32_t* __restrict__ row_idx,
                      const int32_t* __restrict__ order, int N, int Tq, int Tk, float scale_log2,
-                     float scale, bf16_t* __restrict__ dq) {
+                     float scale, bf16_t* __restrict__ dq, const int32_t* __restrict__ col_cnt,
+                     int ncols, int4* __restrict__ plan_items, int4* __restrict__ plan_splits,
+                     int* __restrict__ plan_done) {
   constexpr int D = 128;
   constexpr int NK = D / 16, ND = D / 32;
   constexpr int TILE = 64 * D;
   constexpr int KCOPIES = 16 / NW;   // copy instructions per wave per tile tensor
   __shared__ __attribute__((aligned(16))) uint16_t kb0[TILE], kb1[TILE], kb2[TILE];
   __shared__ __attribute__((aligned(16))) uint16_t vb0[TILE], vb1[TILE];
+  static_assert(TILE * 2 == kPlanBuckets * 4, "the plan's histogram fills one tile buffer");
 
-  const int wg = order ? order[blockIdx.x] : xcd_remap(blockIdx.x, gridDim.x);
+  // The first workgroups write the dK/dV plan of one XCD share each (it
+  // depends on the column counts only), in the tile buffers' LDS.
+  if (blockIdx.x < kPlanWorkgroups) {
+    dkdv_plan_share(blockIdx.x, col_cnt, ncols, plan_items, plan_splits, plan_done,
+                    reinterpret_cast<int*>(kb0), reinterpret_cast<int*>(kb1),
+                    reinterpret_cast<long long*>(kb2), reinterpret_cast<int*>(vb0));
+    return;
+  }
+  const int slot = blockIdx.x - kPlanWorkgroups;
+  const int nslots = gridDim.x - kPlanWorkgroups;
+  const int wg = order ? order[slot] : xcd_remap(slot, nslots);
   const int bh = wg / Tq, qi = wg % Tq;
   const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
   const int h = lane >> 5, l32 = lane & 31;
@@ -836,10 +986,11 @@ template <int BQ>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void dkdv_pair_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                       const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
-                      const float* __restrict__ stats, const int32_t* __restrict__ col_cnt,
-                      const int32_t* __restrict__ col_idx, const int32_t* __restrict__ order,
-                      int N, int Tq, int Tk, float scale_log2, float scale,
-                      bf16_t* __restrict__ dk, bf16_t* __restrict__ dv) {
+                      const float* __restrict__ stats, const int4* __restrict__ items,
+                      const int32_t* __restrict__ col_idx, int N, int Tq, int Tk,
+                      float scale_log2, float scale, bf16_t* __restrict__ dk,
+                      bf16_t* __restrict__ dv, const int4* __restrict__ splits,
+                      int* __restrict__ done, float* __restrict__ partials) {
   constexpr int D = 128;
   using ST = Tile<D, kBoth>;   // slices: permuted, unpadded rows of 256 bytes
   static_assert(ST::kSwizzled, "slices are copied as whole 256-byte rows");
@@ -849,8 +1000,11 @@ void dkdv_pair_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
   __shared__ __attribute__((aligned(16))) uint16_t sq0[SLICE], sq1[SLICE];   // Q slices
   __shared__ __attribute__((aligned(16))) uint16_t so0[SLICE], so1[SLICE];   // dO slices
   __shared__ __attribute__((aligned(16))) float st0[64], st1[64];            // [lse | Delta]
+  __shared__ int last_segment;
 
-  const int wg = order ? order[blockIdx.x] : xcd_remap(blockIdx.x, gridDim.x);
+  const int4 item = items[blockIdx.x];   // {block, first entry, entries, partial slot}
+  if (item.x < 0) return;
+  const int wg = item.x;
   const int bh = wg / Tk, kj = wg % Tk;
   const int key0 = kj * 64;
   const int tid = threadIdx.x, lane = tid & 63, kb = uniform(tid >> 6);
@@ -869,8 +1023,8 @@ void dkdv_pair_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
     }
   }
 
-  const int cnt = col_cnt[wg];
-  const int32_t* lst = col_idx + (size_t)wg * Tq;
+  const int cnt = item.z;
+  const int32_t* lst = col_idx + (size_t)wg * Tq + item.y;
   const int steps = cnt * SUB;
   // wave 0 copies Q and the statistics, wave 1 copies dO; rows past N arrive
   // as zeros, their statistics as the dQ kernel wrote them (zeros)
@@ -985,7 +1139,55 @@ void dkdv_pair_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
   // Element e of block db is d = 32db + 8(e/4) + 4h + e%4 at key 32kb + l32:
   // runs of four consecutive d of one key row.
   const int key = key0 + 32 * kb + l32;
-  if (key < N) {
+  if (item.w >= 0) {
+    // one segment of a split list: fp32 partial [dV | dK] rows of all 64 keys
+    const int entry = item.w >> 10;
+    const int4 sp = splits[entry];   // {block, first partial slot, segments}
+    float* pv = partials + (size_t)(sp.y + (item.w & 1023)) * kPartialFloats +
+                (size_t)(32 * kb + l32) * D;
+    float* pk = pv + 64 * D;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = 32 * db + 8 * g + 4 * h, e = 4 * g;
+        store4(pv + c, accv[db][e], accv[db][e + 1], accv[db][e + 2], accv[db][e + 3]);
+        store4(pk + c, acck[db][e] * scale, acck[db][e + 1] * scale, acck[db][e + 2] * scale,
+               acck[db][e + 3] * scale);
+      }
+    // release the partial, count this segment done; the last one sums
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) last_segment = atomicAdd(&done[entry], 1) == sp.z - 1;
+    __syncthreads();
+    if (last_segment) {
+      __threadfence();
+      // thread t sums 16-byte groups t + 128j of the partials, all 32 of a
+      // segment loaded at once, the segments in order
+      constexpr int PER = (int)kPartialFloats / 4 / 128;
+      const float* part = partials + (size_t)sp.y * kPartialFloats + 4 * tid;
+      f32x4 acc[PER];
+#pragma unroll
+      for (int j = 0; j < PER; ++j) acc[j] = *reinterpret_cast<const f32x4*>(part + 512 * j);
+      for (int s2 = 1; s2 < sp.z; ++s2) {
+        const float* ps = part + (size_t)s2 * kPartialFloats;
+        f32x4 t[PER];
+#pragma unroll
+        for (int j = 0; j < PER; ++j) t[j] = *reinterpret_cast<const f32x4*>(ps + 512 * j);
+#pragma unroll
+        for (int j = 0; j < PER; ++j) acc[j] += t[j];
+      }
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int g = tid + 128 * j;
+        const int r = (g / (D / 4)) % 64, c4 = (g % (D / 4)) * 4;   // dV rows, then dK rows
+        if (key0 + r < N)
+          store4((g < (int)kPartialFloats / 8 ? dv : dk) + base + (size_t)(key0 + r) * D + c4,
+                 acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+      }
+      if (tid == 0) done[entry] = 0;   // ready for the next call
+    }
+  } else if (key < N) {
     bf16_t* rv = dv + base + (size_t)key * D;
     bf16_t* rk = dk + base + (size_t)key * D;
 #pragma unroll
@@ -1177,6 +1379,9 @@ struct BwdArgs {
   float sl2, scale;
   void *dq, *dk, *dv;
   float* stats;
+  int4 *items, *splits;   // dK/dV plan (bf16, d = 128)
+  int* done;
+  float* partials;
   hipStream_t s;
 };
 
@@ -1188,9 +1393,11 @@ static void launch_dq(const BwdArgs& a) {
   static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k),                            \
       static_cast<const bf16_t*>(a.v), static_cast<const bf16_t*>(a.o),                        \
       static_cast<const bf16_t*>(a.dout), a.lse, a.stats, m->row_cnt, m->row_idx,               \
-      m->row_order, a.N, m->Tq, m->Tk, a.sl2, a.scale, static_cast<bf16_t*>(a.dq)
-    if (m->bq == 128) dq_async_kernel<4><<<a.BH * m->Tq, 256, 0, a.s>>>(SA2_DQ_ASYNC_ARGS);
-    else dq_async_kernel<2><<<a.BH * m->Tq, 128, 0, a.s>>>(SA2_DQ_ASYNC_ARGS);
+      m->row_order, a.N, m->Tq, m->Tk, a.sl2, a.scale, static_cast<bf16_t*>(a.dq), m->col_cnt, \
+      a.BH * m->Tk, a.items, a.splits, a.done
+    const int grid = kPlanWorkgroups + a.BH * m->Tq;
+    if (m->bq == 128) dq_async_kernel<4><<<grid, 256, 0, a.s>>>(SA2_DQ_ASYNC_ARGS);
+    else dq_async_kernel<2><<<grid, 128, 0, a.s>>>(SA2_DQ_ASYNC_ARGS);
 #undef SA2_DQ_ASYNC_ARGS
     return;
   }
@@ -1208,13 +1415,15 @@ template <typename T, int D>
 static void launch_dkdv(const BwdArgs& a) {
   const sa2_mask* m = a.m;
   if constexpr (D == 128 && sizeof(T) == 2) {
+    const int ncols = a.BH * m->Tk;
 #define SA2_DKDV_PAIR_ARGS                                                                  \
   static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k),                            \
-      static_cast<const bf16_t*>(a.v), static_cast<const bf16_t*>(a.dout), a.stats,            \
-      m->col_cnt, m->col_idx, m->col_order, a.N, m->Tq, m->Tk, a.sl2, a.scale,                 \
-      static_cast<bf16_t*>(a.dk), static_cast<bf16_t*>(a.dv)
-    if (m->bq == 128) dkdv_pair_kernel<128><<<a.BH * m->Tk, 128, 0, a.s>>>(SA2_DKDV_PAIR_ARGS);
-    else dkdv_pair_kernel<64><<<a.BH * m->Tk, 128, 0, a.s>>>(SA2_DKDV_PAIR_ARGS);
+      static_cast<const bf16_t*>(a.v), static_cast<const bf16_t*>(a.dout), a.stats, a.items,   \
+      m->col_idx, a.N, m->Tq, m->Tk, a.sl2, a.scale, static_cast<bf16_t*>(a.dk),               \
+      static_cast<bf16_t*>(a.dv), a.splits, a.done, a.partials
+    const int grid = 8 * plan_items_per_xcd(ncols);
+    if (m->bq == 128) dkdv_pair_kernel<128><<<grid, 128, 0, a.s>>>(SA2_DKDV_PAIR_ARGS);
+    else dkdv_pair_kernel<64><<<grid, 128, 0, a.s>>>(SA2_DKDV_PAIR_ARGS);
 #undef SA2_DKDV_PAIR_ARGS
     return;
   }
@@ -1239,6 +1448,32 @@ static void by_type(int dtype, int d, const BwdArgs& a) {
   }
 }
 
+// Workspace regions of the backward, each 256-byte aligned: the row
+// statistics; for d = 128 also the dK/dV plan (items, split blocks) and the
+// partial-sum slots of split key blocks.
+struct BwdWorkspace {
+  size_t stats, items, splits, done, partials, total;
+};
+static BwdWorkspace bwd_workspace(int B, int H, int N, int d) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  BwdWorkspace w{};
+  w.stats = 0;
+  size_t off = up((size_t)B * H * stat_groups(N) * 256);
+  if (d == 128) {
+    const int ncols = (int)std::min<size_t>((size_t)B * H * cdiv(N, 64), 0x7fffffff);
+    w.items = off;
+    off = up(off + (size_t)8 * plan_items_per_xcd(ncols) * sizeof(int4));
+    w.splits = off;
+    off = up(off + (size_t)8 * kShareExtra * sizeof(int4));
+    w.done = off;
+    off = up(off + (size_t)8 * kShareExtra * sizeof(int));
+    w.partials = off;
+    off = up(off + (size_t)8 * 2 * kShareExtra * kPartialFloats * sizeof(float));
+  }
+  w.total = off;
+  return w;
+}
+
 static sa2_status check_bwd(const char* fn, const void* q, const void* k, const void* v,
                             const float* lse, const void* dout, int dtype, int B, int H, int N,
                             int d, const sa2_mask* m, void* ws, size_t ws_bytes) {
@@ -1258,8 +1493,15 @@ static BwdArgs bwd_args(const void* q, const void* k, const void* v, const void*
                         const float* lse, const void* dout, int B, int H, int N, int d,
                         const sa2_mask* m, void* dq, void* dk, void* dv, void* ws, void* stream) {
   const double sc = 1.0 / sqrt((double)d);
+  const BwdWorkspace w = bwd_workspace(B, H, N, d);
+  char* base = static_cast<char*>(ws);
   return BwdArgs{q, k, v, o, dout, lse, m, B * H, N, (float)(1.4426950408889634 * sc),
-                 (float)sc, dq, dk, dv, static_cast<float*>(ws), reinterpret_cast<hipStream_t>(stream)};
+                 (float)sc, dq, dk, dv, reinterpret_cast<float*>(base + w.stats),
+                 d == 128 ? reinterpret_cast<int4*>(base + w.items) : nullptr,
+                 d == 128 ? reinterpret_cast<int4*>(base + w.splits) : nullptr,
+                 d == 128 ? reinterpret_cast<int*>(base + w.done) : nullptr,
+                 d == 128 ? reinterpret_cast<float*>(base + w.partials) : nullptr,
+                 reinterpret_cast<hipStream_t>(stream)};
 }
 
 }  // namespace sa2
@@ -1287,10 +1529,10 @@ extern "C" sa2_status sa2_attn_fwd(const void* q, const void* k, const void* v, 
   return check_launch("fwd_kernel");
 }
 
+
 extern "C" size_t sa2_bwd_workspace_bytes(int B, int H, int N, int d) {
   if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return 0;
-  // per head: stat_groups(N) groups of 32 rows x (LSE, Delta) in fp32
-  return ((size_t)B * H * sa2::stat_groups(N) * 256 + 255) & ~(size_t)255;
+  return sa2::bwd_workspace(B, H, N, d).total;
 }
 
 extern "C" sa2_status sa2_attn_bwd_dq(const void* q, const void* k, const void* v,

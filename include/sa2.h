@@ -159,7 +159,12 @@ sa2_status sa2_attn_fwd(const void* q, const void* k, const void* v, int dtype,
  * row, the row sums Delta_t = sum_c dO_tc * O_tc and the LSE in base 2
  * (lse_t * log2(e)), for every row of every 128-row query block (padding
  * rows past N included): B*H*4*ceil(N/128) groups of 32 rows x 2 x 4 bytes,
- * rounded up to 256 bytes.
+ * rounded up to 256 bytes.  For d = 128 it also holds the dK/dV work plan:
+ * column lists longer than a fair share of the kernel's resident workgroups
+ * are cut into segments, each segment's fp32 partial dK, dV goes to one of
+ * 2048 slots of 64 KB, and the partials are added in segment order (128 MB
+ * plus 16 bytes per key block and about 16 KB).  The contents need no
+ * initialisation and are scratch between calls.
  */
 size_t sa2_bwd_workspace_bytes(int B, int H, int N, int d);
 
@@ -171,7 +176,8 @@ size_t sa2_bwd_workspace_bytes(int B, int H, int N, int d);
  *   dS = P * (dP - Delta);  dQ = dS K / sqrt(d);  dK = dS^T Q / sqrt(d).
  * P is recomputed from q, k and lse.  dK and dV of a key block are summed over
  * the query blocks in its col_idx list, dQ of a query block over its row_idx
- * list; no atomics are used, so results are bitwise reproducible.  Key
+ * list (a long column list is summed in segments, then across segments in
+ * a fixed order); no atomics are used, so results are bitwise reproducible.  Key
  * blocks that no query block keeps get dK = dV = 0.
  *
  * q, k, v, o, dout: device [B, H, N, d] (o and lse from sa2_attn_fwd on the

@@ -38,7 +38,15 @@ def test_workspace_sizes():
     want = up(B * H * Tq * d * 8) + up(B * H * Tk * d * 8) + up(B * H * Tq * Tk * 8)
     assert L.sa2_mask_workspace_bytes(B, H, N, d, bq, bk) == want
     assert L.sa2_mask_workspace_bytes(0, H, N, d, bq, bk) == 0
-    assert L.sa2_bwd_workspace_bytes(B, H, N, d) == up(B * H * 4 * (-(-N // 128)) * 32 * 2 * 4)
+    stats = up(B * H * 4 * (-(-N // 128)) * 32 * 2 * 4)
+    # d = 128 adds the dK/dV plan: items, split entries, their completion
+    # counters, partial-sum slots
+    items = up(8 * ((B * H * Tk + 7) // 8 + 128) * 16)
+    splits = up(8 * 128 * 16)
+    done = up(8 * 128 * 4)
+    partials = up(8 * 2 * 128 * 2 * 64 * 128 * 4)
+    assert L.sa2_bwd_workspace_bytes(B, H, N, d) == stats + items + splits + done + partials
+    assert L.sa2_bwd_workspace_bytes(B, H, N, 64) == stats
 
 
 def _mask(B=1, H=1, N=256, bq=64, bk=64):

@@ -152,9 +152,22 @@ def test_both_rules_off_is_an_error():
         sa2.build_mask(q, q, 64, 64, 0.0, 0.0)
 
 
-def test_reproducible_and_fully_written():
-    """Two runs agree bit for bit; outputs pre-filled with NaN are fully overwritten."""
-    w = W.Workload("repro", 1, 2, 1500, 128, 128, 64, "normal", 23, "bf16", 0.1, 0.5)
+@pytest.mark.parametrize("N,bq", [(2000, 128), (1100, 64)])
+def test_long_column_lists_are_split(N, bq):
+    """Dense masks: every key block's column list is longer than the dK/dV
+    plan's shortest segment, so each list is cut into segments whose fp32
+    partial sums the reduce kernel adds; all of dK, dV against the oracle."""
+    w = W.Workload(f"split{bq}", 1, 2, N, 128, bq, 64, "normal", 26, "bf16", 1.0, 0.0)
+    mask, _ = run_case(w, 1.0, 0.0)
+    assert int(mask.col_cnt.min().item()) > 8
+
+
+@pytest.mark.parametrize("k_frac,p", [(0.1, 0.5), (1.0, 0.0)], ids=["hybrid", "dense_split"])
+def test_reproducible_and_fully_written(k_frac, p):
+    """Two runs agree bit for bit; outputs pre-filled with NaN are fully
+    overwritten (with every block kept, every dK/dV column list is split and
+    summed by its last segment)."""
+    w = W.Workload("repro", 1, 2, 1500, 128, 128, 64, "normal", 23, "bf16", k_frac, p)
     dev, _ = device_inputs(w)
     q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
     outs = []
