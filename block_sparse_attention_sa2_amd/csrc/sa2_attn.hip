@@ -70,7 +70,7 @@ __device__ inline void fetch_tile(const T* __restrict__ x, int key0, int N, int 
   for (int c = 0; c < CPT; ++c) {
     const int ch = tid + c * NT, row = ch / CPR, c8 = ch % CPR;
     const int key = key0 + row;
-    r[c] = key < N ? load8(x + (size_t)key * D + c8 * 8) : zero8();
+    r[c] = (unsigned)key < (unsigned)N ? load8(x + (size_t)key * D + c8 * 8) : zero8();
   }
 }
 
@@ -98,6 +98,10 @@ __device__ inline bf16x8 tr_operand(const uint16_t* lds, int kbase, int nbase, i
   const bf16x4 hi = lds_read_tr(lds + Tile<D, L>::off(r + 8, c));
   return cat(lo, hi);
 }
+
+// A list length read from a mask, clamped to [0, cap]: a malformed mask
+// then gives wrong values but no access past the lists and no unbounded loop.
+__device__ inline int list_len(int n, int cap) { return min(max(n, 0), cap); }
 
 // Rows of the running max only move when the tile maximum exceeds them by
 // more than this (log2 units): P then stays below 2^8, and the rescale of the
@@ -176,6 +180,7 @@ void fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[64 * VT::kRowElems];
 
   const int wg = order ? order[blockIdx.x] : xcd_remap(blockIdx.x, gridDim.x);
+  if ((unsigned)wg >= gridDim.x) return;   // a malformed work order
   const int bh = wg / Tq, qi = wg % Tq;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
@@ -195,7 +200,7 @@ void fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
   for (int db = 0; db < ND; ++db) acc[db] = zero16();
   float m = -INFINITY, lsum = 0.f;
 
-  const int cnt = row_cnt[wg];
+  const int cnt = list_len(row_cnt[wg], Tk);
   const int32_t* lst = row_idx + (size_t)wg * Tk;
   bf16x8 kr[CPT], vr[CPT];
   if (cnt > 0) {
@@ -319,7 +324,7 @@ __host__ __device__ inline int plan_items_per_xcd(int ncols) {
 // The plan of XCD share x, by one workgroup of nt threads (a multiple of 64).
 // LDS: hist[kPlanBuckets] ints, scan[nt] ints, red[nt / 64] 64-bit sums,
 // ctr[2] ints.
-__device__ void dkdv_plan_share(int x, const int32_t* __restrict__ col_cnt, int ncols,
+__device__ void dkdv_plan_share(int x, const int32_t* __restrict__ col_cnt, int ncols, int Tq,
                                 int4* __restrict__ items, int4* __restrict__ splits,
                                 int* __restrict__ done, int* hist, int* scan, long long* red,
                                 int* ctr) {
@@ -330,7 +335,7 @@ __device__ void dkdv_plan_share(int x, const int32_t* __restrict__ col_cnt, int 
   // totals over all blocks and over this share
   long long all = 0, mine = 0;
   for (int c = tid; c < ncols; c += nt) {
-    const int n = col_cnt[c];
+    const int n = list_len(col_cnt[c], Tq);
     all += n;
     if (c >= c0 && c < c0 + len) mine += n;
   }
@@ -363,7 +368,7 @@ __device__ void dkdv_plan_share(int x, const int32_t* __restrict__ col_cnt, int 
   // histogram of segment lengths, then first position of each bucket in
   // descending order (as in the mask's work orders)
   for (int j = tid; j < len; j += nt) {
-    const int n = col_cnt[c0 + j], ns = nseg(n);
+    const int n = list_len(col_cnt[c0 + j], Tq), ns = nseg(n);
     for (int s2 = 0; s2 < ns; ++s2) {
       int st;
       atomicAdd(&hist[bucket(seg(n, ns, s2, st))], 1);
@@ -392,7 +397,7 @@ __device__ void dkdv_plan_share(int x, const int32_t* __restrict__ col_cnt, int 
   }
   __syncthreads();
   for (int j = tid; j < len; j += nt) {
-    const int col = c0 + j, n = col_cnt[col], ns = nseg(n);
+    const int col = c0 + j, n = list_len(col_cnt[col], Tq), ns = nseg(n);
     int entry = -1;
     if (ns > 1) {
       const int p0 = 2 * kShareExtra * x + atomicAdd(&ctr[1], ns);
@@ -503,6 +508,7 @@ void fwd_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
   __shared__ __attribute__((aligned(16))) uint16_t vb0[TILE], vb1[TILE];
 
   const int wg = order ? order[blockIdx.x] : xcd_remap(blockIdx.x, gridDim.x);
+  if ((unsigned)wg >= gridDim.x) return;   // a malformed work order
   const int bh = wg / Tq, qi = wg % Tq;
   const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
   const int h = lane >> 5, l32 = lane & 31;
@@ -526,7 +532,7 @@ void fwd_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
   float m = -INFINITY, lsum = 0.f;
 
   // the list is walked with scalar loads, one entry ahead of its copy
-  const int cnt = row_cnt[wg];
+  const int cnt = list_len(row_cnt[wg], Tk);
   const int32_t* lst = row_idx + (size_t)wg * Tk;
   auto key_at = [&](int t) { return t < cnt ? lst[t] * 64 : 0; };
   int key_cur = key_at(0);
@@ -657,7 +663,7 @@ void dq_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   // The first workgroups write the dK/dV plan of one XCD share each (it
   // depends on the column counts only), in the tile buffers' LDS.
   if (blockIdx.x < kPlanWorkgroups) {
-    dkdv_plan_share(blockIdx.x, col_cnt, ncols, plan_items, plan_splits, plan_done,
+    dkdv_plan_share(blockIdx.x, col_cnt, ncols, Tq, plan_items, plan_splits, plan_done,
                     reinterpret_cast<int*>(kb0), reinterpret_cast<int*>(kb1),
                     reinterpret_cast<long long*>(kb2), reinterpret_cast<int*>(vb0));
     return;
@@ -665,6 +671,7 @@ void dq_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   const int slot = blockIdx.x - kPlanWorkgroups;
   const int nslots = gridDim.x - kPlanWorkgroups;
   const int wg = order ? order[slot] : xcd_remap(slot, nslots);
+  if ((unsigned)wg >= (unsigned)nslots) return;   // a malformed work order
   const int bh = wg / Tq, qi = wg % Tq;
   const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
   const int h = lane >> 5, l32 = lane & 31;
@@ -678,7 +685,7 @@ void dq_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   const bool qvalid = qrow < N;
 
   // the first tiles' copies go out before the row loads below
-  const int cnt = row_cnt[wg];
+  const int cnt = list_len(row_cnt[wg], Tk);
   const int32_t* lst = row_idx + (size_t)wg * Tk;
   auto key_at = [&](int t) { return t < cnt ? lst[t] * 64 : 0; };
   int key_t = key_at(0), key_t1 = key_at(1), key_t2 = key_at(2);
@@ -815,6 +822,7 @@ void dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
   uint16_t* slices = v_lds + 64 * KT::kRowElems;               // [pair][Q | dO][32 rows]
 
   const int wg = order ? order[blockIdx.x] : xcd_remap(blockIdx.x, gridDim.x);
+  if ((unsigned)wg >= gridDim.x) return;   // a malformed work order
   const int bh = wg / Tk, kj = wg % Tk;
   const int key0 = kj * 64;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -847,7 +855,7 @@ void dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
     acck[db] = zero16();
   }
 
-  const int cnt = col_cnt[wg];
+  const int cnt = list_len(col_cnt[wg], Tq);
   const int32_t* lst = col_idx + (size_t)wg * Tq;
   const int steps = cnt * SPP;
 
@@ -856,7 +864,7 @@ void dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
   float stat = 0.f;
   auto fetch = [&](int s) {
     const int row = lst[s / SPP] * BQ + 32 * (2 * (s % SPP) + pair) + l32;
-    const bool ok = row < N;
+    const bool ok = (unsigned)row < (unsigned)N;
     const T* p = src + base + (size_t)row * D + 8 * h;
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) own[kk] = ok ? load8(p + 16 * kk) : zero8();
@@ -990,7 +998,7 @@ void dkdv_pair_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
                       const int32_t* __restrict__ col_idx, int N, int Tq, int Tk,
                       float scale_log2, float scale, bf16_t* __restrict__ dk,
                       bf16_t* __restrict__ dv, const int4* __restrict__ splits,
-                      int* __restrict__ done, float* __restrict__ partials) {
+                      int* __restrict__ done, float* __restrict__ partials, int ncols) {
   constexpr int D = 128;
   using ST = Tile<D, kBoth>;   // slices: permuted, unpadded rows of 256 bytes
   static_assert(ST::kSwizzled, "slices are copied as whole 256-byte rows");
@@ -1002,8 +1010,20 @@ void dkdv_pair_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
   __shared__ __attribute__((aligned(16))) float st0[64], st1[64];            // [lse | Delta]
   __shared__ int last_segment;
 
-  const int4 item = items[blockIdx.x];   // {block, first entry, entries, partial slot}
-  if (item.x < 0) return;
+  // {block, first list entry, entries, -1 or split entry * 1024 + segment};
+  // an entry that does not fit this call (a plan written for another mask,
+  // or never written) is skipped, so nothing is read or written out of range
+  const int4 item = items[blockIdx.x];
+  if (item.x < 0 || item.x >= ncols || item.y < 0 || item.z < 0 || item.y + item.z > Tq) return;
+  int4 sp = make_int4(0, 0, 0, 0);   // {block, first partial slot, segments}
+  if (item.w >= 0) {
+    const int entry = item.w >> 10, seg = item.w & 1023;
+    if (entry >= 8 * kShareExtra) return;
+    sp = splits[entry];
+    if (sp.x != item.x || sp.y < 0 || sp.z < 2 || seg >= sp.z ||
+        sp.y + sp.z > 16 * kShareExtra)
+      return;
+  }
   const int wg = item.x;
   const int bh = wg / Tk, kj = wg % Tk;
   const int key0 = kj * 64;
@@ -1142,7 +1162,6 @@ void dkdv_pair_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
   if (item.w >= 0) {
     // one segment of a split list: fp32 partial [dV | dK] rows of all 64 keys
     const int entry = item.w >> 10;
-    const int4 sp = splits[entry];   // {block, first partial slot, segments}
     float* pv = partials + (size_t)(sp.y + (item.w & 1023)) * kPartialFloats +
                 (size_t)(32 * kb + l32) * D;
     float* pk = pv + 64 * D;
@@ -1221,6 +1240,7 @@ void dq_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __rest
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[64 * VT::kRowElems];
 
   const int wg = order ? order[blockIdx.x] : xcd_remap(blockIdx.x, gridDim.x);
+  if ((unsigned)wg >= gridDim.x) return;   // a malformed work order
   const int bh = wg / Tq, qi = wg % Tq;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
@@ -1257,7 +1277,7 @@ void dq_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __rest
 #pragma unroll
   for (int db = 0; db < ND; ++db) acc[db] = zero16();
 
-  const int cnt = row_cnt[wg];
+  const int cnt = list_len(row_cnt[wg], Tk);
   const int32_t* lst = row_idx + (size_t)wg * Tk;
   bf16x8 kr[CPT], vr[CPT];
   if (cnt > 0) {
@@ -1420,7 +1440,7 @@ static void launch_dkdv(const BwdArgs& a) {
   static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k),                            \
       static_cast<const bf16_t*>(a.v), static_cast<const bf16_t*>(a.dout), a.stats, a.items,   \
       m->col_idx, a.N, m->Tq, m->Tk, a.sl2, a.scale, static_cast<bf16_t*>(a.dk),               \
-      static_cast<bf16_t*>(a.dv), a.splits, a.done, a.partials
+      static_cast<bf16_t*>(a.dv), a.splits, a.done, a.partials, ncols
     const int grid = 8 * plan_items_per_xcd(ncols);
     if (m->bq == 128) dkdv_pair_kernel<128><<<grid, 128, 0, a.s>>>(SA2_DKDV_PAIR_ARGS);
     else dkdv_pair_kernel<64><<<grid, 128, 0, a.s>>>(SA2_DKDV_PAIR_ARGS);

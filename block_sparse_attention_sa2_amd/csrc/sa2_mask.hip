@@ -165,14 +165,51 @@ __device__ inline bool ranks_before(uint64_t ka, uint32_t ia, uint64_t kb, uint3
 // select, one wave per (b*h, query block) row.  The row's P2 = 64E ranking
 // entries (P2 = max(64, next power of two >= Tk)) live in registers: entry
 // i = E*lane + e in register e of lane i / E.  The bitonic network's strides
-// below E exchange registers within a lane; larger strides exchange lanes
-// (ds_bpermute), so the sort needs no LDS array and no barrier.  The wave's
-// row flags live in LDS (private to the wave).
+// below E exchange registers within a lane; larger strides exchange lanes at
+// xor distance 1 .. 32 without going through LDS memory (see xor_lane), so
+// the sort needs no LDS array and no barrier.  The wave's row flags live in
+// LDS (private to the wave).
 // ---------------------------------------------------------------------------
 constexpr int kSelectWaves = 4;
 
-__device__ inline uint32_t xor_lane(uint32_t v, int d) {
-  return (uint32_t)__shfl_xor((int)v, d);
+// The value of lane (lane ^ d), d in {1, 2, 4, 8, 16, 32}: DPP quad
+// permutations for 1 and 2, a swizzle (xor mask 4 within 32 lanes) for 4, a
+// rotation of each 16-lane row by 8 for 8, and the row and half-wave swaps
+// for 16 and 32 (each swap returns both partners; the lane picks the other's).
+template <int D>
+__device__ inline uint32_t xor_lane(uint32_t v, int lane) {
+  if constexpr (D == 1) return __builtin_amdgcn_update_dpp(0u, v, 0xB1, 0xf, 0xf, false);
+  if constexpr (D == 2) return __builtin_amdgcn_update_dpp(0u, v, 0x4E, 0xf, 0xf, false);
+  if constexpr (D == 4) return __builtin_amdgcn_ds_swizzle(v, 0x101f);
+  if constexpr (D == 8) return __builtin_amdgcn_update_dpp(0u, v, 0x128, 0xf, 0xf, false);
+  if constexpr (D == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (lane & 16) ? r[0] : r[1];
+  }
+  if constexpr (D == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (lane & 32) ? r[0] : r[1];
+  }
+}
+
+// One network stage whose partners are D lanes apart: every register of a
+// lane meets the same register of its partner lane.
+template <int E, int D>
+__device__ inline void cross_lane_stage(uint64_t* key, uint32_t* idx, int lane, int kk) {
+  const bool lower = (lane & D) == 0;
+  const bool fwd = ((lane * E) & kk) == 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint32_t plo = xor_lane<D>((uint32_t)key[e], lane);
+    const uint32_t phi = xor_lane<D>((uint32_t)(key[e] >> 32), lane);
+    const uint32_t pi = xor_lane<D>(idx[e], lane);
+    const uint64_t pk = ((uint64_t)phi << 32) | plo;
+    const bool mine_first = ranks_before(key[e], idx[e], pk, pi);
+    if (lower != (fwd == mine_first)) {
+      key[e] = pk;
+      idx[e] = pi;
+    }
+  }
 }
 
 // One compare-exchange of entries at network positions a < b = a + stride:
@@ -211,40 +248,24 @@ void select_wave_kernel(const double* __restrict__ sbar, int nrows, int Tk, int 
   } else {
     // this lane's entries E*lane .. E*lane+E-1 (padding past Tk ranks last)
     uint64_t key[E];
-    double mx = -INFINITY;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int j = lane * E + e;
-      const double v = j < Tk ? s[j] : -INFINITY;
-      key[e] = j < Tk ? order_key(v) : 0ull;
+      key[e] = j < Tk ? order_key(s[j]) : 0ull;
       idx[e] = (uint32_t)j;
-      mx = fmax(mx, v);
     }
-    for (int off = 32; off > 0; off >>= 1) mx = fmax(mx, __shfl_xor(mx, off));
-    double z = 0.0;
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (lane * E + e < Tk) z += exp(key_value(key[e]) - mx);
-    for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off);
 
     // bitonic sort into ranking order (descending score, ascending index)
     for (int kk = 2; kk <= P2; kk <<= 1) {
       for (int jj = kk >> 1; jj > 0; jj >>= 1) {
         if (jj >= E) {
-          const int d = jj / E;                   // lane distance
-          const bool lower = (lane & d) == 0;
-          const bool fwd = ((lane * E) & kk) == 0;
-#pragma unroll
-          for (int e = 0; e < E; ++e) {
-            const uint32_t plo = xor_lane((uint32_t)key[e], d);
-            const uint32_t phi = xor_lane((uint32_t)(key[e] >> 32), d);
-            const uint32_t pi = xor_lane(idx[e], d);
-            const uint64_t pk = ((uint64_t)phi << 32) | plo;
-            const bool mine_first = ranks_before(key[e], idx[e], pk, pi);
-            if (lower != (fwd == mine_first)) {
-              key[e] = pk;
-              idx[e] = pi;
-            }
+          switch (jj / E) {   // lane distance
+            case 1: cross_lane_stage<E, 1>(key, idx, lane, kk); break;
+            case 2: cross_lane_stage<E, 2>(key, idx, lane, kk); break;
+            case 4: cross_lane_stage<E, 4>(key, idx, lane, kk); break;
+            case 8: cross_lane_stage<E, 8>(key, idx, lane, kk); break;
+            case 16: cross_lane_stage<E, 16>(key, idx, lane, kk); break;
+            default: cross_lane_stage<E, 32>(key, idx, lane, kk); break;
           }
         } else {
           if constexpr (E >= 2) if (jj == 1) in_lane_stage<E, 1>(key, idx, lane, kk);
@@ -256,17 +277,29 @@ void select_wave_kernel(const double* __restrict__ sbar, int nrows, int Tk, int 
         }
       }
     }
-    // Top-p count: ranks r whose running mass (through r) is still below p
+    // Top-p count: ranks r whose running mass (through r) is still below p.
+    // The row maximum is rank 0's score; each exponential is taken once, in
+    // ranking order.
     int pc = 0;
     if (p >= 1.0) {
       pc = Tk;
     } else if (p > 0.0) {
+      const uint64_t k0 = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(
+                               (int)(uint32_t)(key[0] >> 32)) << 32) |
+                          (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)key[0]);
+      const double mx = key_value(k0);
       double mass[E];
+      double z = 0.0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        mass[e] = lane * E + e < Tk ? exp(key_value(key[e]) - mx) : 0.0;
+        z += mass[e];
+      }
+      for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off);
       double local = 0.0;
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        const int r = lane * E + e;
-        mass[e] = r < Tk ? exp(key_value(key[e]) - mx) / z : 0.0;
+        mass[e] /= z;
         local += mass[e];
       }
       // exclusive scan of the lane totals over the wave

@@ -82,7 +82,10 @@ typedef enum { SA2_BF16 = 0, SA2_F32 = 1 } sa2_dtype;
  * row_idx (forward, dQ) and col_cnt / col_idx (dK, dV), and the orders when
  * present.  A caller may supply its own mask to the attention calls as long as
  * the lists are ascending, duplicate-free and in range, every row_cnt is at
- * least 1, and the orders (if given) are permutations.
+ * least 1, and the orders (if given) are permutations.  A mask that breaks
+ * these rules gives undefined outputs but no access out of range: counts are
+ * clamped to [0, Tk] (rows) and [0, Tq] (columns), list entries outside the
+ * tensors read as zero rows, and order entries out of range are skipped.
  */
 typedef struct sa2_mask {
   int32_t B, H, N, bq, bk, Tq, Tk;
@@ -195,7 +198,9 @@ sa2_status sa2_attn_bwd(const void* q, const void* k, const void* v,
 /*
  * First half of sa2_attn_bwd: dQ = dS K / sqrt(d) over each query block's
  * row list, and Delta_t = sum_c dO_tc O_tc and lse_t * log2(e), which it
- * leaves in `workspace` for sa2_attn_bwd_dkdv.  Arguments as for sa2_attn_bwd.
+ * leaves in `workspace` for sa2_attn_bwd_dkdv, together with (bf16, d = 128)
+ * the dK/dV work plan made from the mask's column counts.  Arguments as for
+ * sa2_attn_bwd.
  */
 sa2_status sa2_attn_bwd_dq(const void* q, const void* k, const void* v,
                            const void* o, const float* lse, const void* dout,
@@ -205,10 +210,12 @@ sa2_status sa2_attn_bwd_dq(const void* q, const void* k, const void* v,
 
 /*
  * Second half of sa2_attn_bwd: dV = P^T dO and dK = dS^T Q / sqrt(d) over
- * each key block's column list.  Reads Delta and the base-2 LSE from
- * `workspace` (lse itself is still checked), so it must
- * follow sa2_attn_bwd_dq on the same inputs, mask and workspace, on the same
- * stream (or after it completes).  Arguments as for sa2_attn_bwd.
+ * each key block's column list.  Reads Delta, the base-2 LSE and the work
+ * plan from `workspace` (lse itself is still checked), so it must follow
+ * sa2_attn_bwd_dq on the same inputs, mask and workspace, on the same stream
+ * (or after it completes).  Called otherwise, dK and dV are undefined, but
+ * plan entries that do not fit the call are skipped, so nothing is read or
+ * written out of range.  Arguments as for sa2_attn_bwd.
  */
 sa2_status sa2_attn_bwd_dkdv(const void* q, const void* k, const void* v,
                              const float* lse, const void* dout,
