@@ -228,107 +228,248 @@ __device__ inline void in_lane_stage(uint64_t* key, uint32_t* idx, int lane, int
     if ((e & J) == 0) cx(key[e], idx[e], key[e + J], idx[e + J], ((lane * E + e) & kk) == 0);
 }
 
+// Bitonic network over a wave's 64E entries (entry E*lane + e in register e)
+// into ranking order.
 template <int E>
+__device__ inline void sort_wave(uint64_t* key, uint32_t* idx, int lane) {
+  for (int kk = 2; kk <= 64 * E; kk <<= 1) {
+    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+      if (jj >= E) {
+        switch (jj / E) {   // lane distance
+          case 1: cross_lane_stage<E, 1>(key, idx, lane, kk); break;
+          case 2: cross_lane_stage<E, 2>(key, idx, lane, kk); break;
+          case 4: cross_lane_stage<E, 4>(key, idx, lane, kk); break;
+          case 8: cross_lane_stage<E, 8>(key, idx, lane, kk); break;
+          case 16: cross_lane_stage<E, 16>(key, idx, lane, kk); break;
+          default: cross_lane_stage<E, 32>(key, idx, lane, kk); break;
+        }
+      } else {
+        if constexpr (E >= 2) if (jj == 1) in_lane_stage<E, 1>(key, idx, lane, kk);
+        if constexpr (E >= 4) if (jj == 2) in_lane_stage<E, 2>(key, idx, lane, kk);
+        if constexpr (E >= 8) if (jj == 4) in_lane_stage<E, 4>(key, idx, lane, kk);
+        if constexpr (E >= 16) if (jj == 8) in_lane_stage<E, 8>(key, idx, lane, kk);
+        if constexpr (E >= 32) if (jj == 16) in_lane_stage<E, 16>(key, idx, lane, kk);
+        if constexpr (E >= 64) if (jj == 32) in_lane_stage<E, 32>(key, idx, lane, kk);
+      }
+    }
+  }
+}
+
+// A lane's E entries among themselves into ranking order.
+template <int E>
+__device__ inline void sort_lane(uint64_t* key, uint32_t* idx) {
+  for (int kk = 2; kk <= E; kk <<= 1) {
+    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+      if constexpr (E >= 2) if (jj == 1) in_lane_stage<E, 1>(key, idx, 0, kk);
+      if constexpr (E >= 4) if (jj == 2) in_lane_stage<E, 2>(key, idx, 0, kk);
+      if constexpr (E >= 8) if (jj == 4) in_lane_stage<E, 4>(key, idx, 0, kk);
+      if constexpr (E >= 16) if (jj == 8) in_lane_stage<E, 8>(key, idx, 0, kk);
+      if constexpr (E >= 32) if (jj == 16) in_lane_stage<E, 16>(key, idx, 0, kk);
+      if constexpr (E >= 64) if (jj == 32) in_lane_stage<E, 32>(key, idx, 0, kk);
+    }
+  }
+}
+
+// Lane 0's entry of a wave-uniform 64-bit value's first register.
+__device__ inline uint64_t first_lane_u64(uint64_t v) {
+  return ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32)) << 32) |
+         (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+}
+
+// Top-p count over entries in ranking order (rank E*lane + e), the first n
+// of them real, given w[e] = exp(S - mx) (0 for the others) and the row total
+// z: the smallest prefix whose mass w / z, summed in ranking order in fp64,
+// reaches p; -1 if the n entries do not reach it.
+template <int E>
+__device__ inline int topp_prefix(const double* w, int lane, int n, double z, double p) {
+  double mass[E];
+  double local = 0.0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    mass[e] = w[e] / z;
+    local += mass[e];
+  }
+  // exclusive scan of the lane totals over the wave
+  double incl = local;
+  for (int off = 1; off < 64; off <<= 1) {
+    const double up = __shfl_up(incl, off);
+    if (lane >= off) incl += up;
+  }
+  double run = incl - local;
+  int below = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    run += mass[e];
+    below += (lane * E + e < n && run < p) ? 1 : 0;
+  }
+  for (int off = 32; off > 0; off >>= 1) below += __shfl_xor(below, off);
+  return below < n ? below + 1 : -1;
+}
+
+// topp_prefix with the masses recomputed from the sorted keys (mass
+// exp(S - mx) / z), so that no array of them is held.
+template <int E>
+__device__ inline int topp_prefix_chunked(const uint64_t* key, int lane, int n, double mx,
+                                          double z, double p) {
+  auto mass = [&](int e) { return lane * E + e < n ? exp(key_value(key[e]) - mx) / z : 0.0; };
+  double local = 0.0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) local += mass(e);
+  double incl = local;
+  for (int off = 1; off < 64; off <<= 1) {
+    const double up = __shfl_up(incl, off);
+    if (lane >= off) incl += up;
+  }
+  double run = incl - local;
+  int below = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    run += mass(e);
+    below += (lane * E + e < n && run < p) ? 1 : 0;
+  }
+  for (int off = 32; off > 0; off >>= 1) below += __shfl_xor(below, off);
+  return below < n ? below + 1 : -1;
+}
+
+__device__ inline double wave_sum_f64(double v) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// Rows of up to 512 key blocks are sorted whole (E <= 8).  Longer rows keep
+// only c = max(kc, pc) of their Tk blocks, so they first take candidates
+// (CAND): the row's entries are spread over the lanes (entry j in lane j % 64,
+// so neighbouring key blocks land in different lanes), each lane ranks its
+// own E entries and offers its best 8, and the 512 candidates are sorted.
+// The candidates' first c are the row's first c exactly when every lane's
+// best entry left out (its 9th) ranks after candidate c - 1.  Otherwise, or
+// when c exceeds 512 or the candidates' mass does not reach p, the row is
+// marked (row_cnt = -1) and a second launch of the whole-row sort (with
+// `marked`) finishes just the marked rows.  Either way the kept set is the
+// one the full ranking gives.
+template <int E, bool CAND>
 __global__ __launch_bounds__(64 * kSelectWaves)
 void select_wave_kernel(const double* __restrict__ sbar, int nrows, int Tk, int kc, double p,
-                        int all, uint8_t* __restrict__ bitmap, int32_t* __restrict__ row_cnt,
-                        int32_t* __restrict__ row_idx) {
+                        int all, int marked, uint8_t* __restrict__ bitmap,
+                        int32_t* __restrict__ row_cnt, int32_t* __restrict__ row_idx) {
   constexpr int P2 = 64 * E;
   __shared__ uint8_t flags_all[kSelectWaves][P2];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int row = blockIdx.x * kSelectWaves + wv;
   if (row >= nrows) return;
+  if (marked && row_cnt[row] != -1) return;   // settled by the candidate launch
   uint8_t* flag = flags_all[wv];
   const double* s = sbar + (size_t)row * Tk;
 
-  int c;
-  uint32_t idx[E];
-  if (all) {
-    c = Tk;
-  } else {
-    // this lane's entries E*lane .. E*lane+E-1 (padding past Tk ranks last)
-    uint64_t key[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int j = lane * E + e;
-      key[e] = j < Tk ? order_key(s[j]) : 0ull;
-      idx[e] = (uint32_t)j;
-    }
-
-    // bitonic sort into ranking order (descending score, ascending index)
-    for (int kk = 2; kk <= P2; kk <<= 1) {
-      for (int jj = kk >> 1; jj > 0; jj >>= 1) {
-        if (jj >= E) {
-          switch (jj / E) {   // lane distance
-            case 1: cross_lane_stage<E, 1>(key, idx, lane, kk); break;
-            case 2: cross_lane_stage<E, 2>(key, idx, lane, kk); break;
-            case 4: cross_lane_stage<E, 4>(key, idx, lane, kk); break;
-            case 8: cross_lane_stage<E, 8>(key, idx, lane, kk); break;
-            case 16: cross_lane_stage<E, 16>(key, idx, lane, kk); break;
-            default: cross_lane_stage<E, 32>(key, idx, lane, kk); break;
-          }
-        } else {
-          if constexpr (E >= 2) if (jj == 1) in_lane_stage<E, 1>(key, idx, lane, kk);
-          if constexpr (E >= 4) if (jj == 2) in_lane_stage<E, 2>(key, idx, lane, kk);
-          if constexpr (E >= 8) if (jj == 4) in_lane_stage<E, 4>(key, idx, lane, kk);
-          if constexpr (E >= 16) if (jj == 8) in_lane_stage<E, 8>(key, idx, lane, kk);
-          if constexpr (E >= 32) if (jj == 16) in_lane_stage<E, 16>(key, idx, lane, kk);
-          if constexpr (E >= 64) if (jj == 32) in_lane_stage<E, 32>(key, idx, lane, kk);
-        }
-      }
-    }
-    // Top-p count: ranks r whose running mass (through r) is still below p.
-    // The row maximum is rank 0's score; each exponential is taken once, in
-    // ranking order.
-    int pc = 0;
-    if (p >= 1.0) {
-      pc = Tk;
-    } else if (p > 0.0) {
-      const uint64_t k0 = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(
-                               (int)(uint32_t)(key[0] >> 32)) << 32) |
-                          (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)key[0]);
-      const double mx = key_value(k0);
-      double mass[E];
-      double z = 0.0;
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        mass[e] = lane * E + e < Tk ? exp(key_value(key[e]) - mx) : 0.0;
-        z += mass[e];
-      }
-      for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off);
-      double local = 0.0;
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        mass[e] /= z;
-        local += mass[e];
-      }
-      // exclusive scan of the lane totals over the wave
-      double incl = local;
-      for (int off = 1; off < 64; off <<= 1) {
-        const double up = __shfl_up(incl, off);
-        if (lane >= off) incl += up;
-      }
-      double run = incl - local;
-      int below = 0;
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        run += mass[e];
-        below += (lane * E + e < Tk && run < p) ? 1 : 0;
-      }
-      for (int off = 32; off > 0; off >>= 1) below += __shfl_xor(below, off);
-      pc = below < Tk ? below + 1 : Tk;
-    }
-    c = max(kc, pc);
-  }
-  // flags by key block, then the bitmap row and the ascending row list
   for (int j = lane; j < P2; j += 64) flag[j] = all && j < Tk ? 1 : 0;
   wave_lds_sync();
+  int c = Tk;
   if (!all) {
+    uint64_t key[E];
+    uint32_t idx[E];
+    bool whole = true;   // sort the whole row
+    if constexpr (CAND) {
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (lane * E + e < c) flag[idx[e]] = 1;
+      for (int e = 0; e < E; ++e) {
+        const int j = lane + 64 * e;
+        key[e] = j < Tk ? order_key(s[j]) : 0ull;   // padding ranks last
+        idx[e] = (uint32_t)j;
+      }
+      sort_lane<E>(key, idx);
+      uint64_t ck[8];
+      uint32_t ci[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        ck[e] = key[e];
+        ci[e] = idx[e];
+      }
+      sort_wave<8>(ck, ci, lane);
+      const double mx = key_value(first_lane_u64(ck[0]));
+      int pcc = 0;
+      if (p > 0.0) {
+        double z = 0.0;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          if ((int)idx[e] < Tk) z += exp(key_value(key[e]) - mx);
+        z = wave_sum_f64(z);
+        double w[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] = exp(key_value(ck[e]) - mx);
+        pcc = topp_prefix<8>(w, lane, 512, z, p);
+      }
+      const int cc = max(kc, pcc);
+      if (pcc >= 0 && cc <= 512) {
+        // candidate cc - 1 against every lane's 9th entry
+        const int r = cc - 1, src = r >> 3, er = r & 7;
+        uint64_t kv = ck[0];
+        uint32_t iv = ci[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e)
+          if (e == er) {
+            kv = ck[e];
+            iv = ci[e];
+          }
+        const uint64_t kr =
+            ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(kv >> 32), src) << 32) |
+            (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)kv, src);
+        const uint32_t ir = (uint32_t)__builtin_amdgcn_readlane((int)iv, src);
+        if (!__any(ranks_before(key[8], idx[8], kr, ir))) {
+          whole = false;
+          c = cc;
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (lane * 8 + e < c) flag[ci[e]] = 1;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int j = lane * E + e;
+        key[e] = j < Tk ? order_key(s[j]) : 0ull;   // padding ranks last
+        idx[e] = (uint32_t)j;
+      }
+    }
+    if constexpr (CAND) {
+      if (whole) {   // left to the whole-row launch
+        if (lane == 0) row_cnt[row] = -1;
+        return;
+      }
+    } else {
+      sort_wave<E>(key, idx, lane);
+      int pc = 0;
+      if (p >= 1.0) {
+        pc = Tk;
+      } else if (p > 0.0) {
+        // the row maximum is rank 0's score
+        const double mx = key_value(first_lane_u64(key[0]));
+        int r;
+        if constexpr (E <= 8) {   // each exponential once
+          double w[E];
+          double z = 0.0;
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            w[e] = lane * E + e < Tk ? exp(key_value(key[e]) - mx) : 0.0;
+            z += w[e];
+          }
+          r = topp_prefix<E>(w, lane, Tk, wave_sum_f64(z), p);
+        } else {   // long rows: in 8-entry chunks, taken twice (registers)
+          double z = 0.0;
+#pragma unroll
+          for (int e = 0; e < E; ++e)
+            if (lane * E + e < Tk) z += exp(key_value(key[e]) - mx);
+          z = wave_sum_f64(z);
+          r = topp_prefix_chunked<E>(key, lane, Tk, mx, z, p);
+        }
+        pc = r < 0 ? Tk : r;
+      }
+      c = max(kc, pc);
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (lane * E + e < c) flag[idx[e]] = 1;
+    }
     wave_lds_sync();
   }
+  // the bitmap row and the ascending row list from the flags
   uint8_t* bm = bitmap + (size_t)row * Tk;
   for (int j = lane; j < Tk; j += 64) bm[j] = flag[j];
   int mine = 0;
@@ -523,18 +664,22 @@ extern "C" sa2_status sa2_build_mask(const void* q, const void* k, int dtype, in
   const int all = (kc >= Tk || p >= 1.0) ? 1 : 0;
   const int P2 = max(64, next_pow2(Tk));
   const int rows = BH * Tq, sgrid = cdiv(rows, kSelectWaves), sthreads = 64 * kSelectWaves;
-#define SA2_SELECT(E_)                                                                         \
-  select_wave_kernel<E_><<<sgrid, sthreads, 0, s>>>(sbar, rows, Tk, kc, p, all, m->bitmap,       \
-                                                   m->row_cnt, m->row_idx)
+#define SA2_SELECT(E_, CAND_, MARKED_)                                                        \
+  select_wave_kernel<E_, CAND_><<<sgrid, sthreads, 0, s>>>(sbar, rows, Tk, kc, p, all, MARKED_,   \
+                                                          m->bitmap, m->row_cnt, m->row_idx)
+#define SA2_SELECT_LONG(E_)                                                                   \
+  SA2_SELECT(E_, true, 0);                                                                     \
+  SA2_SELECT(E_, false, 1)
   switch (P2 / 64) {
-    case 1: SA2_SELECT(1); break;
-    case 2: SA2_SELECT(2); break;
-    case 4: SA2_SELECT(4); break;
-    case 8: SA2_SELECT(8); break;
-    case 16: SA2_SELECT(16); break;
-    case 32: SA2_SELECT(32); break;
-    default: SA2_SELECT(64); break;
+    case 1: SA2_SELECT(1, false, 0); break;
+    case 2: SA2_SELECT(2, false, 0); break;
+    case 4: SA2_SELECT(4, false, 0); break;
+    case 8: SA2_SELECT(8, false, 0); break;
+    case 16: SA2_SELECT_LONG(16); break;
+    case 32: SA2_SELECT_LONG(32); break;
+    default: SA2_SELECT_LONG(64); break;
   }
+#undef SA2_SELECT_LONG
 #undef SA2_SELECT
   if (sa2_status st = check_launch("select_wave_kernel")) return st;
 

@@ -250,3 +250,51 @@ def test_distillation_step(wname, k_frac, p):
         for name, mine, g in (("dq", dq, grads[h][0]), ("dk", dk, grads[h][1]),
                               ("dv", dv, grads[h][2])):
             check_grad(f64(mine[0, h]), g / w.H, f"distill {w.name} h{h} {name}")
+
+
+# ---------------------------------------------------------------------------
+# Rows of more than 512 key blocks take candidates first (each lane's best 8
+# of its entries, the lanes holding every 64th key block); the candidates'
+# prefix is used only when no lane's best left-out entry ranks inside it.
+# Mask only (N x N attention would not fit the oracle's dense mode).
+# ---------------------------------------------------------------------------
+
+def _lane_cluster_inputs(N, d, seed):
+    """Key blocks j with j % 64 == 0 score far above the rest: one lane of
+    the selection holds every top block, so the candidates cannot be used."""
+    rng = np.random.default_rng(seed)
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    Q = np.tile(u, (N, 1)) + 0.1 * rng.standard_normal((N, d))
+    K = 0.1 * rng.standard_normal((N, d))
+    for j in range(0, -(-N // 64), 64):
+        K[64 * j:64 * j + 64] += 3.0 * u
+    return Q.astype(np.float32), K.astype(np.float32)
+
+
+@pytest.mark.parametrize("case,N,k_frac,p", [
+    ("candidates", 33000, 0.03, 0.3),
+    ("topk_past_512", 33000, 0.995, 0.0),
+    ("topp_past_512", 33000, 0.01, 0.999),
+    ("lane_cluster", 40000, 0.03, 0.0),
+    ("lane_cluster_topp", 40000, 0.0, 0.5),
+])
+def test_long_row_selection(case, N, k_frac, p):
+    d, bq, bk = 64, 128, 64
+    if case.startswith("lane_cluster"):
+        Qf, Kf = _lane_cluster_inputs(N, d, 28)
+    else:
+        rng = np.random.default_rng(29)
+        Qf = rng.standard_normal((N, d)).astype(np.float32)
+        Kf = rng.standard_normal((N, d)).astype(np.float32)
+    q = torch.from_numpy(Qf).to(torch.bfloat16).reshape(1, 1, N, d).cuda()
+    k = torch.from_numpy(Kf).to(torch.bfloat16).reshape(1, 1, N, d).cuda()
+    _say(f"[long rows] {case} N{N} Tk{-(-N // bk)} k{k_frac} p{p}")
+    mask = sa2.build_mask(q, k, bq, bk, k_frac, p)
+    torch.cuda.synchronize()
+    Q, K = (t.reshape(N, d).to(torch.float64).cpu().numpy() for t in (q, k))
+    hm = O.build_mask_head(Q, K, bq, bk, k_frac, p)
+    bm = mask.bitmap.cpu().numpy()[0, 0]
+    compare_mask(hm, bm, p)
+    check_lists(bm, mask.row_cnt.cpu().numpy()[0, 0], mask.row_idx.cpu().numpy()[0, 0],
+                mask.col_cnt.cpu().numpy()[0, 0], mask.col_idx.cpu().numpy()[0, 0])
