@@ -116,16 +116,28 @@ void score_kernel(const double* __restrict__ qbar, const double* __restrict__ kb
     __syncthreads();
     if (c0 + TK < d) fetch(c0 + TK);
     const int kk_end = min(TK, d - c0);
+    // the operands of step kk + 1 are read from LDS during step kk's FMAs
+    double av[4], bv[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) av[a] = qs[ty + 16 * a][0];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) bv[c] = ks[tx + 16 * c][0];
+#pragma unroll 4
     for (int kk = 0; kk < kk_end; ++kk) {
-      double av[4], bv[4];
+      double an[4], bn[4];
+      const int kn = kk + 1 < kk_end ? kk + 1 : kk;
 #pragma unroll
-      for (int a = 0; a < 4; ++a) av[a] = qs[ty + 16 * a][kk];
+      for (int a = 0; a < 4; ++a) an[a] = qs[ty + 16 * a][kn];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) bv[c] = ks[tx + 16 * c][kk];
+      for (int c = 0; c < 4; ++c) bn[c] = ks[tx + 16 * c][kn];
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[a][c] = fma(av[a], bv[c], acc[a][c]);
+#pragma unroll
+      for (int a = 0; a < 4; ++a) av[a] = an[a];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) bv[c] = bn[c];
     }
   }
 #pragma unroll
@@ -277,16 +289,15 @@ __device__ inline uint64_t first_lane_u64(uint64_t v) {
 }
 
 // Top-p count over entries in ranking order (rank E*lane + e), the first n
-// of them real, given w[e] = exp(S - mx) (0 for the others) and the row total
-// z: the smallest prefix whose mass w / z, summed in ranking order in fp64,
+// of them real, given mass[e] = exp(S - mx) (0 for the others; divided by
+// the row total z in place): the smallest prefix whose mass w / z, summed in ranking order in fp64,
 // reaches p; -1 if the n entries do not reach it.
 template <int E>
-__device__ inline int topp_prefix(const double* w, int lane, int n, double z, double p) {
-  double mass[E];
-  double local = 0.0;
+__device__ inline int topp_prefix(double* mass, int lane, int n, double z, double p) {
+  double local = 0.0;   // the weights become masses in place
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    mass[e] = w[e] / z;
+    mass[e] /= z;
     local += mass[e];
   }
   // exclusive scan of the lane totals over the wave
