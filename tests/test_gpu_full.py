@@ -232,3 +232,38 @@ def test_stress_union_and_oracle(name, stress_inputs):
     want = W.tuned_record(name)["density"]
     _say(f"[stress] {name} density {dens:.5f} (oracle {want:.5f}, target {w.target_density})")
     assert abs(dens - want) <= 1e-3 * want
+
+
+# ---------------------------------------------------------------------------
+# The largest key-block count the mask builder takes (4096: rows of 4096
+# entries, 64 per lane, in the selection), at one head.  Top-k alone keeps 41
+# blocks per row (the candidate path); with p = 0.3 rows keep about 1200
+# (past the 512 candidates: the whole-row sort).
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def max_tk():
+    w = W.Workload("max_tk", 1, 1, 4096 * 64, 64, 128, 64, "normal", 31, "bf16", 0.01, 0.0)
+    _say(f"[max Tk] generating N{w.N} Tq{w.Tq} Tk{w.Tk}")
+    dev, ref = device_inputs(w)
+    return w, dev, ref
+
+
+@pytest.mark.parametrize("p", [0.0, 0.3], ids=["candidates", "whole_rows"])
+def test_max_key_blocks(max_tk, p):
+    w, dev, ref = max_tk
+    q, k, v, do = (dev[t] for t in ("q", "k", "v", "do"))
+    mask = sa2.build_mask(q, k, w.bq, w.bk, w.k_frac, p)
+    torch.cuda.synchronize()
+    assert mask.Tk == 4096
+    bm = mask.bitmap.cpu().numpy()
+    hm = O.build_mask_head(ref["q"][0, 0], ref["k"][0, 0], w.bq, w.bk, w.k_frac, p)
+    compare_mask(hm, bm[0, 0], p)
+    check_lists(bm[0, 0], mask.row_cnt.cpu().numpy()[0, 0], mask.row_idx.cpu().numpy()[0, 0],
+                mask.col_cnt.cpu().numpy()[0, 0], mask.col_idx.cpu().numpy()[0, 0])
+    _say(f"[max Tk] p{p} kept per row {float(mask.row_cnt.float().mean()):.1f}")
+    if p == 0.0:
+        o, lse = sa2.attn_fwd(q, k, v, mask)
+        grads = sa2.attn_bwd(q, k, v, o, lse, do, mask)
+        torch.cuda.synchronize()
+        _spot_check(w, ref, 0, bm[0, 0], o, lse, grads, np.random.default_rng(3))

@@ -127,8 +127,10 @@ def test_ragged_shapes(w):
     run_case(w, w.k_frac, w.p)
 
 
-def test_single_partial_block():
-    w = W.Workload("n50", 1, 2, 50, 64, 64, 64, "normal", 20, "bf16", 0.5, 0.5)
+@pytest.mark.parametrize("N", [50, 1])
+def test_single_partial_block(N):
+    """One query and one key block, partial (50 tokens) or a single token."""
+    w = W.Workload(f"n{N}", 1, 2, N, 64, 64, 64, "normal", 20, "bf16", 0.5, 0.5)
     mask, _ = run_case(w, 0.5, 0.5)
     assert mask.Tq == 1 and mask.Tk == 1
 
