@@ -24,7 +24,7 @@ ARCH = "gfx950"
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
-    # packed-fp32 instructions stay off: they are emitted only from plain code
+    # no packed fp32 arithmetic (v_pk_*_f32) anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
