@@ -14,13 +14,21 @@
 // transposed (O^T = V^T P^T, dQ^T = K^T dS^T).  The V^T and K^T operands are
 // read straight from row-major LDS tiles with ds_read_b64_tr_b16.
 //
-// Backward: dq_kernel first (one workgroup per query block over its row
+// Backward: the dQ kernel first (one workgroup per query block over its row
 // list; it also forms Delta = rowsum(dO * O) and the log2-scaled LSE of its
-// rows and leaves them in the workspace), then dkdv_kernel (one workgroup per key block, walking the query
-// blocks of its column list; each wave owns a 32-row slice of every listed
-// query block and accumulates the whole 64 x d dK and dV tile, and the four
-// partial tiles are summed in LDS in a fixed order).  No atomics: results are
-// bitwise reproducible.
+// rows and leaves them in the workspace), then the dK/dV kernel (key blocks
+// walking the query blocks of their column lists).
+//
+// Kernels: fwd_async_kernel, dq_async_kernel and dkdv_pair_kernel serve bf16
+// and d = 128 (K/V tiles and Q/dO slices copied straight to LDS through
+// buffer resources, double-buffered).  dq_async_kernel's first workgroups
+// also write the dK/dV work plan (dkdv_plan_share): column lists longer than
+// a fair share are cut into segments whose fp32 partials the last segment
+// adds in order.  fwd_kernel, dq_kernel and dkdv_kernel, staged through
+// registers, serve fp32 inputs and d = 64 (in dkdv_kernel each wave owns a
+// 32-row slice of every listed query block and the four partial tiles are
+// summed in LDS in a fixed order).  No value is accumulated atomically: the
+// results are bitwise reproducible.
 #include <math.h>
 
 #include "sa2_common.h"
