@@ -9,13 +9,18 @@ Default workload: the Wan2.1-1.3B-shaped self-attention layer, B=1, H=12,
 N=32760 (21x30x52 latent grid), d=128, bf16, q-block 128, k-block 64,
 k = 3% plus Top-p tuned to 5% density (95% sparsity), forward + backward.
 
+The timed step is that sequence captured once as a HIP graph and replayed K
+times after W warm-up replays (--no-graph: K eager steps).  Per-stage times
+and the roofline figure come from an eager run of the same K steps with HIP
+events between the stages; its step time is reported beside the headline.
+
 Prints one JSON line (stdout).  Effective FLOPs follow the FlashAttention
 convention: forward 4 N^2 d H density, forward+backward 3.5x that.  Beside
 the headline figures the line carries the dense baseline (the same kernels
 with every block kept), the same layer with 64 x 64 blocks, and the fp64
 oracle timed on the host.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline] [--no-graph]
     python bench.py --sweep variants   # mask rules at equal density, one line per case
 """
 from __future__ import annotations
@@ -86,6 +91,8 @@ def parse():
                          "per regime, density and Top-k share; --steps timed steps each)")
     ap.add_argument("--regimes", default=None, help="comma-separated subset of the sweep's "
                     "score regimes (sink, uniform, smooth)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time the eager launches instead of the replayed HIP graph")
     ap.add_argument("--no-second-geometry", action="store_true",
                     help="skip the 64 x 64-block run of the same layer")
     ap.add_argument("--no-dense-baseline", action="store_true",
@@ -164,6 +171,30 @@ def dense_baseline(sa2, q, k, v, do, w, sparse_attn_ms, args):
             "speedup_attention": round(dense_ms / sparse_attn_ms, 2),
             "note": "same kernels and shape, all blocks kept; speedup = dense / sparse "
                     "attention time (forward + backward, mask excluded)"}
+
+
+def graph_replay(step, steps, warmup):
+    """ms per step of the same step captured once in a HIP graph (the library
+    allocates nothing and records no memset) and replayed back to back: the
+    kernels without host launch overhead or inter-kernel gaps."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
 
 
 def second_geometry(sa2, W, q, k, v, do, name="c2_b64", warmup=3, steps=10):
@@ -387,9 +418,13 @@ def main():
         step(events[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
+    eager_ms = wall * 1e3 / args.steps
     per = {st: float(np.mean([events[s][i].elapsed_time(events[s][i + 1])
                               for s in range(args.steps)])) for i, st in enumerate(stages)}
+    # the timed step: the same step captured once as a HIP graph and replayed
+    # (K replays after W, synchronised on both sides), unless --no-graph
+    graph_ms = None if args.no_graph else graph_replay(step, args.steps, args.warmup)
+    ms_step = graph_ms if graph_ms is not None else eager_ms
 
     fwd_flops = 4.0 * N * N * d * H * B * density
     eff_flops = fwd_flops * (3.5 if backward else 1.0)
@@ -432,6 +467,12 @@ def main():
         "mask_builder": {"ms": round(per["mask"], 4), "qk_read_bytes": qk_bytes,
                          "GBps_whole_call": round(mask_gbps, 1), "peak_GBps": PEAK_HBM_GBPS},
     }
+    out["timing"] = {
+        "ms_per_step": round(ms_step, 4),
+        "mode": "HIP graph replay of the captured step" if graph_ms is not None else "eager launches",
+        "eager_ms_per_step": round(eager_ms, 4),
+        "note": "stages_ms and the roofline come from the eager run, with HIP events between "
+                "the stages"}
     if not args.no_dense_baseline and backward:
         out["dense_baseline"] = dense_baseline(sa2, q, k, v, do, w, attn_ms, args)
     if args.workload == "c2" and not args.no_second_geometry:

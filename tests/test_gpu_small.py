@@ -300,3 +300,48 @@ def test_long_row_selection(case, N, k_frac, p):
     compare_mask(hm, bm, p)
     check_lists(bm, mask.row_cnt.cpu().numpy()[0, 0], mask.row_idx.cpu().numpy()[0, 0],
                 mask.col_cnt.cpu().numpy()[0, 0], mask.col_idx.cpu().numpy()[0, 0])
+
+
+def test_graph_replay():
+    """The whole step (mask, forward, backward) captured in one HIP graph:
+    every replay, with eager work and synchronisations between replays,
+    reproduces the eager results bit for bit (the library allocates nothing
+    and writes no memset nodes)."""
+    w = W.Workload("graph", 1, 2, 2000, 128, 128, 64, "normal", 30, "bf16", 0.1, 0.5)
+    dev, _ = device_inputs(w)
+    q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
+    B, H, N, d = q.shape
+    mask = sa2.BlockMask(B, H, N, w.bq, w.bk, q.device)
+    mws = torch.empty(sa2.mask_workspace_bytes(B, H, N, d, w.bq, w.bk), dtype=torch.uint8,
+                      device=q.device)
+    bws = torch.empty(sa2.bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=q.device)
+    o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+
+    def step():
+        sa2.build_mask(q, k, w.bq, w.bk, w.k_frac, w.p, mask=mask, workspace=mws)
+        sa2.attn_fwd(q, k, v, mask, o=o, lse=lse)
+        sa2.attn_bwd(q, k, v, o, lse, do, mask, dq=dq, dk=dk, dv=dv, workspace=bws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()   # eager, on the capture stream, before capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    want = [t.clone() for t in (mask.bitmap, mask.row_cnt, o, lse, dq, dk, dv)]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(3):
+        for t in (o, lse, dq, dk, dv):
+            t.fill_(float("nan"))
+        mask.bitmap.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = (mask.bitmap, mask.row_cnt, o, lse, dq, dk, dv)
+        for a, b in zip(got, want):
+            assert torch.equal(a, b), f"replay {rep}"
+        step()   # eager work between replays
+        torch.cuda.synchronize()
