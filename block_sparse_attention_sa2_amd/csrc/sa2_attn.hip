@@ -312,8 +312,10 @@ void fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
 // Items, in the workspace as int4 {block, first list entry, entries, -1 or
 // split entry * 1024 + segment}; item j of XCD x sits at 8j + x (the
 // workgroup slots that run on XCD x), longest first; unused items have block
-// -1.  Each XCD takes the contiguous share of blocks that xcd_remap gives it,
-// so its L2 sees a narrow band of heads.  Split entries: int4 {block, first
+// -1.  Each XCD takes a contiguous share of the blocks, so its L2 sees a
+// narrow band of heads; the shares are cut at equal cost rather than equal
+// count (densities differ from head to head, and the XCD with the most work
+// would set the kernel's time).  Split entries: int4 {block, first
 // partial slot, segments}, kShareExtra per XCD share, with one completion
 // counter each, which the plan zeroes.
 // ---------------------------------------------------------------------------
@@ -325,8 +327,58 @@ constexpr int kPlanBuckets = 4096;   // list lengths are ranked by min(length, 4
 constexpr int kPlanWorkgroups = 8;   // one per XCD share
 constexpr size_t kPartialFloats = 2 * 64 * 128;   // dV and dK of one key block
 
+// Shares are balanced by cost (see balanced_share): a share's boundaries move
+// at most share_slack(n) items from the equal-count ones.
+__host__ __device__ inline int share_slack(int n) { return ((n + 7) / 8 + 15) / 16; }
 __host__ __device__ inline int plan_items_per_xcd(int ncols) {
-  return (ncols + 7) / 8 + kShareExtra;
+  return (ncols + 7) / 8 + 2 * share_slack(ncols) + kShareExtra;
+}
+
+// XCD share x of n items: [b(x), b(x + 1)), where b(x) is the first item whose
+// predecessors cost at least x / 8 of the total (an item costs its list length
+// plus one), clamped to within share_slack(n) of the equal-count boundary
+// x n / 8.  Every workgroup computes the same boundaries.  pre: blockDim.x
+// entries of LDS.
+__device__ int2 balanced_share(int x, const int32_t* __restrict__ cnt, int n, int cap,
+                               long long* pre, int* bnd) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int per = (n + nt - 1) / nt;
+  const int lo = min(n, tid * per), hi = min(n, lo + per);
+  long long s = 0;
+  for (int i = lo; i < hi; ++i) s += list_len(cnt[i], cap) + 1;
+  pre[tid] = s;
+  if (tid < 2) bnd[tid] = 0;
+  __syncthreads();
+  for (int off = 1; off < nt; off <<= 1) {
+    const long long add = tid >= off ? pre[tid - off] : 0;
+    __syncthreads();
+    pre[tid] += add;
+    __syncthreads();
+  }
+  const long long total = pre[nt - 1], run = pre[tid] - s;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const long long target = ((long long)(x + k) * total + 7) / 8;
+    if (target > 0 && run < target && target <= run + s) {
+      long long acc = run;
+      int b = hi;
+      for (int i = lo; i < hi; ++i) {
+        if (acc >= target) { b = i; break; }
+        acc += list_len(cnt[i], cap) + 1;
+      }
+      bnd[k] = b;
+    }
+  }
+  __syncthreads();
+  const int H = share_slack(n);
+  int b[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int e = (int)((long long)(x + k) * n / 8);
+    b[k] = min(max(bnd[k], max(0, e - H)), min(n, e + H));
+  }
+  __syncthreads();
+  return make_int2(b[0], b[1] - b[0]);
 }
 
 // The plan of XCD share x, by one workgroup of nt threads (a multiple of 64).
@@ -337,8 +389,8 @@ __device__ void dkdv_plan_share(int x, const int32_t* __restrict__ col_cnt, int 
                                 int* __restrict__ done, int* hist, int* scan, long long* red,
                                 int* ctr) {
   const int tid = threadIdx.x, nt = blockDim.x, nw = nt / 64;
-  const int qn = ncols / 8, rn = ncols % 8;
-  const int c0 = x * qn + min(x, rn), len = qn + (x < rn ? 1 : 0);
+  const int2 sh = balanced_share(x, col_cnt, ncols, Tq, red, ctr);
+  const int c0 = sh.x, len = sh.y;
 
   // totals over all blocks and over this share
   long long all = 0, mine = 0;

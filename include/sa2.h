@@ -166,7 +166,7 @@ sa2_status sa2_attn_fwd(const void* q, const void* k, const void* v, int dtype,
  * column lists longer than a fair share of the kernel's resident workgroups
  * are cut into segments, each segment's fp32 partial dK, dV goes to one of
  * 2048 slots of 64 KB, and the partials are added in segment order (128 MB
- * plus 16 bytes per key block and about 16 KB).  The contents need no
+ * plus about 18 bytes per key block and 36 KB).  The contents need no
  * initialisation and are scratch between calls.
  */
 size_t sa2_bwd_workspace_bytes(int B, int H, int N, int d);

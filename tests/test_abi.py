@@ -41,7 +41,9 @@ def test_workspace_sizes():
     stats = up(B * H * 4 * (-(-N // 128)) * 32 * 2 * 4)
     # d = 128 adds the dK/dV plan: items, split entries, their completion
     # counters, partial-sum slots
-    items = up(8 * ((B * H * Tk + 7) // 8 + 128) * 16)
+    ncols = B * H * Tk
+    slack = ((ncols + 7) // 8 + 15) // 16        # cost-balanced XCD shares
+    items = up(8 * ((ncols + 7) // 8 + 2 * slack + 128) * 16)
     splits = up(8 * 128 * 16)
     done = up(8 * 128 * 4)
     partials = up(8 * 2 * 128 * 2 * 64 * 128 * 4)
