@@ -347,14 +347,15 @@ __device__ inline double wave_sum_f64(double v) {
   return v;
 }
 
-// Rows of up to 512 key blocks are sorted whole (E <= 8).  Longer rows keep
+// Rows of up to 256 key blocks are sorted whole (E <= 4).  Longer rows keep
 // only c = max(kc, pc) of their Tk blocks, so they first take candidates
 // (CAND): the row's entries are spread over the lanes (entry j in lane j % 64,
 // so neighbouring key blocks land in different lanes), each lane ranks its
-// own E entries and offers its best 8, and the 512 candidates are sorted.
-// The candidates' first c are the row's first c exactly when every lane's
-// best entry left out (its 9th) ranks after candidate c - 1.  Otherwise, or
-// when c exceeds 512 or the candidates' mass does not reach p, the row is
+// own E entries and offers its best C (4 for rows of up to 512 blocks, 8 for
+// longer ones), and the 64 C candidates are sorted.  The candidates' first c
+// are the row's first c exactly when every lane's best entry left out (its
+// C+1-th) ranks after candidate c - 1.  Otherwise, or when c exceeds 64 C or
+// the candidates' mass does not reach p, the row is
 // marked (row_cnt = -1) and a second launch of the whole-row sort (with
 // `marked`) finishes just the marked rows.  Either way the kept set is the
 // one the full ranking gives.
@@ -364,6 +365,8 @@ void select_wave_kernel(const double* __restrict__ sbar, int nrows, int Tk, int 
                         int all, int marked, uint8_t* __restrict__ bitmap,
                         int32_t* __restrict__ row_cnt, int32_t* __restrict__ row_idx) {
   constexpr int P2 = 64 * E;
+  constexpr int C = E >= 16 ? 8 : E / 2;   // candidates per lane
+  static_assert(!CAND || C < E, "a lane keeps some of its entries back");
   __shared__ uint8_t flags_all[kSelectWaves][P2];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int row = blockIdx.x * kSelectWaves + wv;
@@ -387,14 +390,14 @@ void select_wave_kernel(const double* __restrict__ sbar, int nrows, int Tk, int 
         idx[e] = (uint32_t)j;
       }
       sort_lane<E>(key, idx);
-      uint64_t ck[8];
-      uint32_t ci[8];
+      uint64_t ck[C];
+      uint32_t ci[C];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < C; ++e) {
         ck[e] = key[e];
         ci[e] = idx[e];
       }
-      sort_wave<8>(ck, ci, lane);
+      sort_wave<C>(ck, ci, lane);
       const double mx = key_value(first_lane_u64(ck[0]));
       int pcc = 0;
       if (p > 0.0) {
@@ -403,19 +406,19 @@ void select_wave_kernel(const double* __restrict__ sbar, int nrows, int Tk, int 
         for (int e = 0; e < E; ++e)
           if ((int)idx[e] < Tk) z += exp(key_value(key[e]) - mx);
         z = wave_sum_f64(z);
-        double w[8];
+        double w[C];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) w[e] = exp(key_value(ck[e]) - mx);
-        pcc = topp_prefix<8>(w, lane, 512, z, p);
+        for (int e = 0; e < C; ++e) w[e] = exp(key_value(ck[e]) - mx);
+        pcc = topp_prefix<C>(w, lane, 64 * C, z, p);
       }
       const int cc = max(kc, pcc);
-      if (pcc >= 0 && cc <= 512) {
-        // candidate cc - 1 against every lane's 9th entry
-        const int r = cc - 1, src = r >> 3, er = r & 7;
+      if (pcc >= 0 && cc <= 64 * C) {
+        // candidate cc - 1 against every lane's best entry left out
+        const int r = cc - 1, src = r / C, er = r % C;
         uint64_t kv = ck[0];
         uint32_t iv = ci[0];
 #pragma unroll
-        for (int e = 1; e < 8; ++e)
+        for (int e = 1; e < C; ++e)
           if (e == er) {
             kv = ck[e];
             iv = ci[e];
@@ -424,12 +427,12 @@ void select_wave_kernel(const double* __restrict__ sbar, int nrows, int Tk, int 
             ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(kv >> 32), src) << 32) |
             (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)kv, src);
         const uint32_t ir = (uint32_t)__builtin_amdgcn_readlane((int)iv, src);
-        if (!__any(ranks_before(key[8], idx[8], kr, ir))) {
+        if (!__any(ranks_before(key[C], idx[C], kr, ir))) {
           whole = false;
           c = cc;
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (lane * 8 + e < c) flag[ci[e]] = 1;
+          for (int e = 0; e < C; ++e)
+            if (lane * C + e < c) flag[ci[e]] = 1;
         }
       }
     } else {
@@ -685,7 +688,7 @@ extern "C" sa2_status sa2_build_mask(const void* q, const void* k, int dtype, in
     case 1: SA2_SELECT(1, false, 0); break;
     case 2: SA2_SELECT(2, false, 0); break;
     case 4: SA2_SELECT(4, false, 0); break;
-    case 8: SA2_SELECT(8, false, 0); break;
+    case 8: SA2_SELECT_LONG(8); break;
     case 16: SA2_SELECT_LONG(16); break;
     case 32: SA2_SELECT_LONG(32); break;
     default: SA2_SELECT_LONG(64); break;

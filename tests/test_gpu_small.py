@@ -255,9 +255,10 @@ def test_distillation_step(wname, k_frac, p):
 
 
 # ---------------------------------------------------------------------------
-# Rows of more than 512 key blocks take candidates first (each lane's best 8
-# of its entries, the lanes holding every 64th key block); the candidates'
-# prefix is used only when no lane's best left-out entry ranks inside it.
+# Rows of more than 256 key blocks take candidates first (each lane's best 4
+# of its entries up to 512 key blocks, its best 8 beyond, the lanes holding
+# every 64th key block); the candidates' prefix is used only when no lane's
+# best left-out entry ranks inside it.
 # Mask only (N x N attention would not fit the oracle's dense mode).
 # ---------------------------------------------------------------------------
 
@@ -280,6 +281,9 @@ def _lane_cluster_inputs(N, d, seed):
     ("topp_past_512", 33000, 0.01, 0.999),
     ("lane_cluster", 40000, 0.03, 0.0),
     ("lane_cluster_topp", 40000, 0.0, 0.5),
+    ("candidates_313", 20000, 0.03, 0.3),
+    ("lane_cluster_313", 20000, 0.03, 0.0),
+    ("lane_cluster_topp_313", 20000, 0.0, 0.5),
 ])
 def test_long_row_selection(case, N, k_frac, p):
     d, bq, bk = 64, 128, 64
