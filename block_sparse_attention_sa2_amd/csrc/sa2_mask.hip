@@ -4,7 +4,7 @@
 //
 // Kernels on the caller's stream:
 //   pool       q-bar / k-bar: fp64 means of each block's tokens (HBM stream)
-//   score      S-bar = q-bar k-bar^T / sqrt(d), fp64, 64x64 tiles
+//   score      S-bar = q-bar k-bar^T / sqrt(d), fp64 MFMAs, 16x32 tiles per wave
 //   select     one wave per query-block row: softmax, rank, cut, emit the
 //              bitmap row, row count and ascending row list
 //   columns    transposed lists (query blocks per key block), ascending
@@ -72,83 +72,53 @@ void pool_kernel(const T* __restrict__ q, const T* __restrict__ k, int BH, int N
 }
 
 // ---------------------------------------------------------------------------
-// score: S-bar tile of 64 query blocks x 64 key blocks per workgroup.  The d
-// dimension is walked in chunks of 32 staged in LDS; the next chunk's global
-// loads are issued before the current chunk's products, so their latency
-// overlaps the arithmetic.  Each product is one fp64 sum over d in order.
+// score: S-bar = q-bar k-bar^T / sqrt(d) on the fp64 matrix cores
+// (v_mfma_f64_16x16x4f64), one wave per 16 query blocks x 32 key blocks (two
+// 16 x 16 tiles that share the A operand).  The operands are small and stay
+// in L2, so they are read straight from global memory with 16-byte loads:
+// for the MFMA pair (2u, 2u + 1) lane l holds d indices 8u + 2(l / 16) and
+// the next one, of query block l % 16 (A) and key block l % 16 (B).  Lane
+// layout (measured): A[i][k] comes from lane i + 16k, B[k][j] from lane
+// j + 16k, and D[i][j] lands in element i / 4 of lane j + 16 (i % 4).  Each
+// product is a fp64 sum over d in a fixed order.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256)
+typedef double f64x2 __attribute__((ext_vector_type(2)));
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+constexpr int kScoreWaves = 4;
+
+__global__ __launch_bounds__(64 * kScoreWaves)
 void score_kernel(const double* __restrict__ qbar, const double* __restrict__ kbar, int Tq,
                   int Tk, int d, double sqrt_d, double* __restrict__ sbar) {
-  constexpr int TK = 32;                 // d chunk
-  constexpr int PER = 64 * TK / 256;     // elements of each operand a thread stages per chunk
-  __shared__ double qs[64][TK + 1];
-  __shared__ double ks[64][TK + 1];
-  const int bh = blockIdx.z;
-  const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
-  const int tid = threadIdx.x, tx = tid % 16, ty = tid / 16;
-  const double* qb = qbar + (size_t)bh * Tq * d;
-  const double* kb = kbar + (size_t)bh * Tk * d;
-  double acc[4][4];
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) acc[a][c] = 0.0;
-  double qn[PER], kn[PER];
-  auto fetch = [&](int c0) {
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int e = tid + 256 * u, r = e / TK, c = e % TK;
-      const int ii = i0 + r, jj = j0 + r, cc = c0 + c;
-      qn[u] = (ii < Tq && cc < d) ? qb[(size_t)ii * d + cc] : 0.0;
-      kn[u] = (jj < Tk && cc < d) ? kb[(size_t)jj * d + cc] : 0.0;
-    }
-  };
-  fetch(0);
-  for (int c0 = 0; c0 < d; c0 += TK) {
-    __syncthreads();   // the previous chunk's reads of qs / ks are done
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int e = tid + 256 * u, r = e / TK, c = e % TK;
-      qs[r][c] = qn[u];
-      ks[r][c] = kn[u];
-    }
-    __syncthreads();
-    if (c0 + TK < d) fetch(c0 + TK);
-    const int kk_end = min(TK, d - c0);
-    // the operands of step kk + 1 are read from LDS during step kk's FMAs
-    double av[4], bv[4];
-#pragma unroll
-    for (int a = 0; a < 4; ++a) av[a] = qs[ty + 16 * a][0];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) bv[c] = ks[tx + 16 * c][0];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int tq = (Tq + 15) / 16, tk = (Tk + 31) / 32;
+  const int bh = blockIdx.y;
+  const int t = blockIdx.x * kScoreWaves + wv;   // this wave's 16 x 32 tile
+  if (t >= tq * tk) return;
+  const int i0 = (t / tk) * 16, j0 = (t % tk) * 32;
+  const int r = lane & 15, g = lane >> 4;
+  const int qi = i0 + r, kj0 = j0 + r, kj1 = j0 + 16 + r;
+  // rows past the end read the last row; their products are not stored
+  const double* qp = qbar + ((size_t)bh * Tq + min(qi, Tq - 1)) * d + 2 * g;
+  const double* kp0 = kbar + ((size_t)bh * Tk + min(kj0, Tk - 1)) * d + 2 * g;
+  const double* kp1 = kbar + ((size_t)bh * Tk + min(kj1, Tk - 1)) * d + 2 * g;
+  f64x4 acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll 4
-    for (int kk = 0; kk < kk_end; ++kk) {
-      double an[4], bn[4];
-      const int kn = kk + 1 < kk_end ? kk + 1 : kk;
-#pragma unroll
-      for (int a = 0; a < 4; ++a) an[a] = qs[ty + 16 * a][kn];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) bn[c] = ks[tx + 16 * c][kn];
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[a][c] = fma(av[a], bv[c], acc[a][c]);
-#pragma unroll
-      for (int a = 0; a < 4; ++a) av[a] = an[a];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) bv[c] = bn[c];
-    }
+  for (int u = 0; u < d / 8; ++u) {
+    const f64x2 av = *reinterpret_cast<const f64x2*>(qp + 8 * u);
+    const f64x2 b0 = *reinterpret_cast<const f64x2*>(kp0 + 8 * u);
+    const f64x2 b1 = *reinterpret_cast<const f64x2*>(kp1 + 8 * u);
+    acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(av[0], b0[0], acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(av[0], b1[0], acc1, 0, 0, 0);
+    acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(av[1], b0[1], acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(av[1], b1[1], acc1, 0, 0, 0);
   }
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int ii = i0 + ty + 16 * a;
-    if (ii >= Tq) continue;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int jj = j0 + tx + 16 * c;
-      if (jj < Tk) sbar[((size_t)bh * Tq + ii) * Tk + jj] = acc[a][c] / sqrt_d;
-    }
+  for (int e = 0; e < 4; ++e) {
+    const int i = i0 + 4 * e + g;
+    if (i >= Tq) continue;
+    double* row = sbar + ((size_t)bh * Tq + i) * Tk;
+    if (kj0 < Tk) row[kj0] = acc0[e] / sqrt_d;
+    if (kj1 < Tk) row[kj1] = acc1[e] / sqrt_d;
   }
 }
 
@@ -670,8 +640,8 @@ extern "C" sa2_status sa2_build_mask(const void* q, const void* k, int dtype, in
                                                      Tq, Tk, qbar, kbar);
   if (sa2_status st = check_launch("pool_kernel")) return st;
 
-  score_kernel<<<dim3(cdiv(Tk, 64), cdiv(Tq, 64), BH), 256, 0, s>>>(qbar, kbar, Tq, Tk, d,
-                                                                    sqrt((double)d), sbar);
+  score_kernel<<<dim3(cdiv(cdiv(Tq, 16) * cdiv(Tk, 32), kScoreWaves), BH), 64 * kScoreWaves, 0,
+                 s>>>(qbar, kbar, Tq, Tk, d, sqrt((double)d), sbar);
   if (sa2_status st = check_launch("score_kernel")) return st;
 
   const int kc = topk_count(k_frac, Tk);
