@@ -382,7 +382,7 @@ __device__ int2 balanced_share(int x, const int32_t* __restrict__ cnt, int n, in
 }
 
 // The plan of XCD share x, by one workgroup of nt threads (a multiple of 64).
-// LDS: hist[kPlanBuckets] ints, scan[nt] ints, red[nt / 64] 64-bit sums,
+// LDS: hist[kPlanBuckets] ints, scan[nt] ints, red[nt] 64-bit sums,
 // ctr[2] ints.
 __device__ void dkdv_plan_share(int x, const int32_t* __restrict__ col_cnt, int ncols, int Tq,
                                 int4* __restrict__ items, int4* __restrict__ splits,
