@@ -716,7 +716,7 @@ void dq_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   constexpr int NK = D / 16, ND = D / 32;
   constexpr int TILE = 64 * D;
   constexpr int KCOPIES = 16 / NW;   // copy instructions per wave per tile tensor
-  __shared__ __attribute__((aligned(16))) uint16_t kb0[TILE], kb1[TILE], kb2[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t kb0[TILE], kb1[TILE];
   __shared__ __attribute__((aligned(16))) uint16_t vb0[TILE], vb1[TILE];
   static_assert(TILE * 2 == kPlanBuckets * 4, "the plan's histogram fills one tile buffer");
 
@@ -725,7 +725,7 @@ void dq_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   if (blockIdx.x < kPlanWorkgroups) {
     dkdv_plan_share(blockIdx.x, col_cnt, ncols, Tq, plan_items, plan_splits, plan_done,
                     reinterpret_cast<int*>(kb0), reinterpret_cast<int*>(kb1),
-                    reinterpret_cast<long long*>(kb2), reinterpret_cast<int*>(vb0));
+                    reinterpret_cast<long long*>(vb1), reinterpret_cast<int*>(vb0));
     return;
   }
   const int slot = blockIdx.x - kPlanWorkgroups;
@@ -748,12 +748,11 @@ void dq_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   const int cnt = list_len(row_cnt[wg], Tk);
   const int32_t* lst = row_idx + (size_t)wg * Tk;
   auto key_at = [&](int t) { return t < cnt ? lst[t] * 64 : 0; };
-  int key_t = key_at(0), key_t1 = key_at(1), key_t2 = key_at(2);
+  int key_t = key_at(0), key_t1 = key_at(1);
   if (cnt > 0) {
     copy_groups<KCOPIES / 4>(rk, key_t, w * KCOPIES, kb0, uo);
     copy_groups<KCOPIES / 4>(rv, key_t, w * KCOPIES, vb0, uo);
   }
-  if (cnt > 1) copy_groups<KCOPIES / 4>(rk, key_t1, w * KCOPIES, kb1, uo);
 
   bf16x8 qf[NK], df[NK];
   float dpart = 0.f;
@@ -781,20 +780,16 @@ void dq_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
 #pragma unroll
   for (int db = 0; db < ND; ++db) acc[db] = zero16();
 
-  unrolled_steps<6>(cnt, [&](int t, auto j) {
-    constexpr int J = decltype(j)::value;
-    const uint16_t* kt = J % 3 == 0 ? kb0 : J % 3 == 1 ? kb1 : kb2;
-    const uint16_t* vt = J % 2 == 0 ? vb0 : vb1;
-    uint16_t* vn = J % 2 == 0 ? vb1 : vb0;                            // V(t+1)
-    uint16_t* kn = J % 3 == 0 ? kb2 : J % 3 == 1 ? kb0 : kb1;         // K(t+2)
+  double_buffered(cnt, [&](int t, auto parity) {
+    constexpr bool odd = decltype(parity)::value == 1;
+    const uint16_t* kt = odd ? kb1 : kb0;
+    const uint16_t* vt = odd ? vb1 : vb0;
     const int key0 = key_t;
-    if (t + 1 < cnt) wait_vm_lgkm0<KCOPIES>(); else wait_vm_lgkm0<0>();
+    wait_vm_lgkm0<0>();
     __syncthreads();
-    if (t + 1 < cnt) copy_groups<KCOPIES / 4>(rv, key_t1, w * KCOPIES, vn, uo);
-    if (t + 2 < cnt) copy_groups<KCOPIES / 4>(rk, key_t2, w * KCOPIES, kn, uo);
+    if (t + 1 < cnt) copy_kv_tile<NW>(rk, rv, key_t1, odd ? kb0 : kb1, odd ? vb0 : vb1, w, uo);
     key_t = key_t1;
-    key_t1 = key_t2;
-    key_t2 = key_at(t + 3);
+    key_t1 = key_at(t + 2);
     const SwzAddr A = addr0.fresh();
 
     // the two 32-key halves one after the other, so that only one half's S
