@@ -119,6 +119,8 @@ SMALL = [
     W.Workload("smooth_4k", 1, 1, 4096, 128, 128, 64, "smooth", 16, "bf16", 0.05, 0.5,
                grid=(4, 32, 32)),
     W.Workload("batch2", 2, 2, 640, 64, 64, 64, "normal", 17, "bf16", 0.2, 0.5),
+    W.Workload("batch2_d128", 2, 3, 900, 128, 128, 64, "normal", 18, "bf16", 0.1, 0.5),
+    W.Workload("batch3_d128_q64", 3, 1, 700, 128, 64, 64, "normal", 19, "bf16", 0.15, 0.4),
 ]
 
 
