@@ -423,7 +423,14 @@ def main():
                               for s in range(args.steps)])) for i, st in enumerate(stages)}
     # the timed step: the same step captured once as a HIP graph and replayed
     # (K replays after W, synchronised on both sides), unless --no-graph
-    graph_ms = None if args.no_graph else graph_replay(step, args.steps, args.warmup)
+    graph_ms, graph_error = None, None
+    if not args.no_graph:
+        try:
+            graph_ms = graph_replay(step, args.steps, args.warmup)
+        except RuntimeError as e:   # capture refused by the runtime: report eager timing
+            graph_error = str(e).splitlines()[0][:200]
+            log(f"[bench] graph capture failed ({graph_error}); timing eager launches")
+            torch.cuda.synchronize()
     ms_step = graph_ms if graph_ms is not None else eager_ms
 
     fwd_flops = 4.0 * N * N * d * H * B * density
@@ -469,7 +476,8 @@ def main():
     }
     out["timing"] = {
         "ms_per_step": round(ms_step, 4),
-        "mode": "HIP graph replay of the captured step" if graph_ms is not None else "eager launches",
+        "mode": ("HIP graph replay of the captured step" if graph_ms is not None else
+                 "eager launches" + (f" (graph capture failed: {graph_error})" if graph_error else "")),
         "eager_ms_per_step": round(eager_ms, 4),
         "note": "stages_ms and the roofline come from the eager run, with HIP events between "
                 "the stages"}
