@@ -58,6 +58,31 @@ def _stream(dev: torch.device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
 
+def _out(t, shape, dtype, device, name: str):
+    """A caller-supplied output: the kernels write exactly `shape` elements of
+    `dtype` there, so anything else is refused before a launch."""
+    if (not isinstance(t, torch.Tensor) or tuple(t.shape) != tuple(shape) or t.dtype != dtype
+            or t.device != device or not t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} "
+                         f"on {device}")
+    return t
+
+
+def _workspace(ws, need: int, device):
+    """A workspace tensor (new if None): contiguous bytes on `device`."""
+    if ws is None:
+        return torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    if (not isinstance(ws, torch.Tensor) or ws.device != device or not ws.is_contiguous()
+            or ws.dtype != torch.uint8):
+        raise ValueError(f"workspace must be a contiguous uint8 tensor on {device}")
+    return ws
+
+
+def _same_device(mask, device):
+    if mask.device != device:
+        raise ValueError(f"mask is on {mask.device}, tensors on {device}")
+
+
 def _ptr(t: torch.Tensor) -> ctypes.c_void_p:
     return ctypes.c_void_p(t.data_ptr())
 
@@ -126,9 +151,8 @@ def build_mask(q: torch.Tensor, k: torch.Tensor, bq: int, bk: int, k_frac: float
         raise ValueError("q and k must have the same shape")
     if mask is None:
         mask = BlockMask(B, H, N, bq, bk, q.device, work_order=work_order)
-    need = mask_workspace_bytes(B, H, N, d, bq, bk)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _same_device(mask, q.device)
+    workspace = _workspace(workspace, mask_workspace_bytes(B, H, N, d, bq, bk), q.device)
     L = _lib.lib()
     st = L.sa2_build_mask(_ptr(q), _ptr(k), dt, B, H, N, d, bq, bk, float(k_frac), float(p),
                           ctypes.byref(mask.c_struct()), _ptr(workspace), workspace.numel(),
@@ -143,10 +167,10 @@ def attn_fwd(q, k, v, mask: BlockMask, o=None, lse=None):
     B, H, N, d = _shape(q)
     if _shape(k) != (B, H, N, d) or _shape(v) != (B, H, N, d):
         raise ValueError("q, k, v must have the same shape")
-    if o is None:
-        o = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _same_device(mask, q.device)
+    o = torch.empty_like(q) if o is None else _out(o, q.shape, q.dtype, q.device, "o")
+    lse = (torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else
+           _out(lse, (B, H, N), torch.float32, q.device, "lse"))
     st = _lib.lib().sa2_attn_fwd(_ptr(q), _ptr(k), _ptr(v), dt, B, H, N, d,
                                  ctypes.byref(mask.c_struct()), _ptr(o), _ptr(lse),
                                  _stream(q.device))
@@ -168,12 +192,13 @@ def attn_bwd(q, k, v, o, lse, dout, mask: BlockMask, dq=None, dk=None, dv=None,
             raise ValueError("q, k, v, o, dout must have the same shape")
     if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
-    need = bwd_workspace_bytes(B, H, N, d)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _same_device(mask, q.device)
+    if lse.device != q.device:
+        raise ValueError("lse must be on the tensors' device")
+    dq = torch.empty_like(q) if dq is None else _out(dq, q.shape, q.dtype, q.device, "dq")
+    dk = torch.empty_like(k) if dk is None else _out(dk, k.shape, k.dtype, k.device, "dk")
+    dv = torch.empty_like(v) if dv is None else _out(dv, v.shape, v.dtype, v.device, "dv")
+    workspace = _workspace(workspace, bwd_workspace_bytes(B, H, N, d), q.device)
     st = _lib.lib().sa2_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), dt,
                                  B, H, N, d, ctypes.byref(mask.c_struct()), _ptr(dq), _ptr(dk),
                                  _ptr(dv), _ptr(workspace), workspace.numel(),
@@ -190,13 +215,17 @@ def _bwd_prep(q, k, v, dout, lse, extra):
             raise ValueError("q, k, v, o, dout must have the same shape")
     if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    if lse.device != q.device:
+        raise ValueError("lse must be on the tensors' device")
     return dt, B, H, N, d
 
 
 def attn_bwd_dq(q, k, v, o, lse, dout, mask: BlockMask, workspace: torch.Tensor, dq=None):
     """dQ, and Delta into `workspace` for attn_bwd_dkdv (sa2_attn_bwd_dq)."""
     dt, B, H, N, d = _bwd_prep(q, k, v, dout, lse, (o,))
-    dq = torch.empty_like(q) if dq is None else dq
+    _same_device(mask, q.device)
+    workspace = _workspace(workspace, bwd_workspace_bytes(B, H, N, d), q.device)
+    dq = torch.empty_like(q) if dq is None else _out(dq, q.shape, q.dtype, q.device, "dq")
     st = _lib.lib().sa2_attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
                                     dt, B, H, N, d, ctypes.byref(mask.c_struct()), _ptr(dq),
                                     _ptr(workspace), workspace.numel(), _stream(q.device))
@@ -208,8 +237,10 @@ def attn_bwd_dkdv(q, k, v, lse, dout, mask: BlockMask, workspace: torch.Tensor, 
                   dv=None):
     """dK, dV using the Delta a prior attn_bwd_dq left in `workspace` (sa2_attn_bwd_dkdv)."""
     dt, B, H, N, d = _bwd_prep(q, k, v, dout, lse, ())
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    _same_device(mask, q.device)
+    workspace = _workspace(workspace, bwd_workspace_bytes(B, H, N, d), q.device)
+    dk = torch.empty_like(k) if dk is None else _out(dk, k.shape, k.dtype, k.device, "dk")
+    dv = torch.empty_like(v) if dv is None else _out(dv, v.shape, v.dtype, v.device, "dv")
     st = _lib.lib().sa2_attn_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dout), dt, B, H,
                                       N, d, ctypes.byref(mask.c_struct()), _ptr(dk), _ptr(dv),
                                       _ptr(workspace), workspace.numel(), _stream(q.device))
@@ -250,12 +281,12 @@ def distill_loss_grad(o_student, o_teacher, dout=None, loss=None, workspace=None
     B, H, N, d = _shape(o_student)
     if _shape(o_teacher) != (B, H, N, d):
         raise ValueError("o_student and o_teacher must have the same shape")
-    dout = torch.empty_like(o_student) if dout is None else dout
-    if loss is None:
-        loss = torch.empty((1,), dtype=torch.float64, device=o_student.device)
-    if workspace is None:
-        workspace = torch.empty(max(distill_workspace_bytes(B, H, N, d), 1), dtype=torch.uint8,
-                                device=o_student.device)
+    dev = o_student.device
+    dout = (torch.empty_like(o_student) if dout is None else
+            _out(dout, o_student.shape, o_student.dtype, dev, "dout"))
+    loss = (torch.empty((1,), dtype=torch.float64, device=dev) if loss is None else
+            _out(loss, (1,), torch.float64, dev, "loss"))
+    workspace = _workspace(workspace, distill_workspace_bytes(B, H, N, d), dev)
     st = _lib.lib().sa2_distill_loss_grad(_ptr(o_student), _ptr(o_teacher), dt, B, H, N, d,
                                           _ptr(dout), _ptr(loss), _ptr(workspace),
                                           workspace.numel(), _stream(o_student.device))

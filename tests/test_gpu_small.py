@@ -206,6 +206,34 @@ def test_without_work_orders():
         assert torch.equal(a, b)
 
 
+def test_binding_refuses_malformed_outputs():
+    """Caller-supplied outputs and workspaces of the wrong shape, dtype or
+    layout are refused before any launch (the kernels would write past them)."""
+    dev = torch.device("cuda:0")
+    B, H, N, d = 1, 2, 256, 64
+    g = torch.Generator().manual_seed(3)
+    q, k, v, do = (torch.randn(B, H, N, d, generator=g).to(torch.bfloat16).to(dev)
+                   for _ in range(4))
+    mask = sa2.build_mask(q, k, 64, 64, 0.25, 0.5)
+    with pytest.raises(ValueError):
+        sa2.attn_fwd(q, k, v, mask, o=torch.empty(B, H, N - 1, d, dtype=q.dtype, device=dev))
+    with pytest.raises(ValueError):
+        sa2.attn_fwd(q, k, v, mask, lse=torch.empty(B, H, N, dtype=torch.float16, device=dev))
+    with pytest.raises(ValueError):
+        sa2.attn_fwd(q, k, v, mask, o=torch.empty(B, H, d, N, dtype=q.dtype, device=dev).transpose(2, 3))
+    o, lse = sa2.attn_fwd(q, k, v, mask)
+    with pytest.raises(ValueError):
+        sa2.attn_bwd(q, k, v, o, lse, do, mask, dk=torch.empty(B, H, N, d, dtype=torch.float32,
+                                                               device=dev))
+    with pytest.raises(ValueError):
+        sa2.attn_bwd(q, k, v, o, lse, do, mask,
+                     workspace=torch.empty(1 << 20, dtype=torch.float32, device=dev))
+    with pytest.raises(ValueError):
+        sa2.build_mask(q, k, 64, 64, 0.25, 0.5, workspace=torch.empty(4, dtype=torch.int64,
+                                                                      device=dev))
+    torch.cuda.synchronize()
+
+
 def test_autograd_wrapper():
     w = W.Workload("autograd", 1, 1, 512, 64, 64, 64, "normal", 24, "bf16", 0.25, 0.5)
     dev, ref = device_inputs(w)
