@@ -22,6 +22,7 @@ oracle timed on the host.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline] [--no-graph]
     python bench.py --sweep variants   # mask rules at equal density, one line per case
+    python bench.py --sweep sparsity   # the layer at densities 1 .. 0.01 (Top-k only)
 """
 from __future__ import annotations
 
@@ -86,9 +87,10 @@ def parse():
     ap.add_argument("--cpu-heads", type=int, default=12, help="heads the oracle times (default: the whole layer)")
     ap.add_argument("--no-work-order", action="store_true",
                     help="schedule the attention kernels in their fixed order")
-    ap.add_argument("--sweep", choices=["variants"], default=None,
+    ap.add_argument("--sweep", choices=["variants", "sparsity"], default=None,
                     help="instead of the benchmark line: the mask-rule sweep (one JSON line "
-                         "per regime, density and Top-k share; --steps timed steps each)")
+                         "per regime, density and Top-k share) or the sparsity sweep of the "
+                         "benchmark layer (one line per density); --steps timed steps each")
     ap.add_argument("--regimes", default=None, help="comma-separated subset of the sweep's "
                     "score regimes (sink, uniform, smooth)")
     ap.add_argument("--no-graph", action="store_true",
@@ -344,6 +346,67 @@ def variant_sweep(args):
         torch.cuda.empty_cache()
 
 
+SWEEP_DENSITIES = (1.0, 0.5, 0.25, 0.1, 0.05, 0.025, 0.01)
+
+
+def sparsity_sweep(args):
+    """The benchmark layer (same inputs) at a ladder of densities, Top-k only
+    (k_frac = density, so every row keeps the same number of key blocks):
+    mask + forward + backward time per stage (medians of --steps queued
+    steps), effective TFLOPS, and the attention speedup over the dense run of
+    the same kernels.  One JSON line per density on stdout."""
+    import numpy as np
+    import torch
+
+    import block_sparse_attention_sa2_amd as sa2
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    w = W.WORKLOADS[args.workload]
+    log(f"[sweep] generating {w.name} inputs")
+    x = W.make_inputs(w)
+    q, k, v, do = (W.to_device_dtype(x[t], w.dtype).to(dev) for t in ("q", "k", "v", "do"))
+    del x
+    B, H, N, d = q.shape
+    mask = sa2.BlockMask(B, H, N, w.bq, w.bk, dev, work_order=True)
+    mws = torch.empty(sa2.mask_workspace_bytes(B, H, N, d, w.bq, w.bk), dtype=torch.uint8,
+                      device=dev)
+    bws = torch.empty(sa2.bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
+    o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dense_attn = None
+    for D in SWEEP_DENSITIES:
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)]
+               for _ in range(2 + args.steps)]
+        for ev in evs:
+            ev[0].record()
+            sa2.build_mask(q, k, w.bq, w.bk, D, 0.0, mask=mask, workspace=mws)
+            ev[1].record()
+            sa2.attn_fwd(q, k, v, mask, o=o, lse=lse)
+            ev[2].record()
+            sa2.attn_bwd_dq(q, k, v, o, lse, do, mask, bws, dq=dq)
+            ev[3].record()
+            sa2.attn_bwd_dkdv(q, k, v, lse, do, mask, bws, dk=dk, dv=dv)
+            ev[4].record()
+        torch.cuda.synchronize()
+        stage = np.median(np.array([[ev[i].elapsed_time(ev[i + 1]) for i in range(4)]
+                                    for ev in evs[2:]]), axis=0)
+        dens = mask.density()
+        attn_ms = float(stage[1:].sum())
+        if dense_attn is None:
+            dense_attn = attn_ms
+        flops = 14.0 * N * N * d * H * B * dens
+        print(json.dumps({
+            "workload": w.name, "k_frac": D, "density": round(dens, 5),
+            "sparsity": round(1 - dens, 5),
+            "stages_ms": dict(zip(("mask", "fwd", "bwd_dq", "bwd_dkdv"),
+                                  (round(float(t), 4) for t in stage))),
+            "ms_per_step": round(float(stage.sum()), 4),
+            "effective_tflops": round(flops / (float(stage.sum()) * 1e-3) / 1e12, 1),
+            "attention_effective_tflops": round(flops / (attn_ms * 1e-3) / 1e12, 1),
+            "speedup_attention_vs_dense": round(dense_attn / attn_ms, 2)}), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_probe:
@@ -355,6 +418,9 @@ def main():
         sys.exit(2)
     if args.sweep == "variants":
         variant_sweep(args)
+        return
+    if args.sweep == "sparsity":
+        sparsity_sweep(args)
         return
 
     import numpy as np
