@@ -616,6 +616,8 @@ extern "C" sa2_status sa2_build_mask(const void* q, const void* k, int dtype, in
     return fail(SA2_EINVAL, "sa2_build_mask: workspace smaller than sa2_mask_workspace_bytes()");
   if ((size_t)B * H * Tq > 0x7fffffff || (size_t)B * H * (Tq + Tk) > 0x7fffffff)
     return fail(SA2_EUNSUPPORTED, "sa2_build_mask: too many blocks");
+  if ((size_t)B * H > 65535)   // (b, h) pairs index the second grid dimension
+    return fail(SA2_EUNSUPPORTED, "sa2_build_mask: more than 65535 (batch, head) pairs");
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int BH = B * H;

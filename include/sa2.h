@@ -132,7 +132,8 @@ size_t sa2_mask_workspace_bytes(int B, int H, int N, int d, int bq, int bk);
  * inputs exactly as stored.  mask: geometry fields filled in by the caller
  * (Tq, Tk as above) and all five arrays allocated.  workspace: at least
  * sa2_mask_workspace_bytes(...) bytes of device memory, 256-byte aligned.
- * Limits: Tq, Tk <= 4096.  k_frac <= 0 together with p <= 0 (both rules off)
+ * Limits: Tq, Tk <= 4096 and B*H <= 65535 (else SA2_EUNSUPPORTED).  k_frac <= 0
+ * together with p <= 0 (both rules off)
  * is SA2_EINVAL; NaN parameters are SA2_EINVAL.
  */
 sa2_status sa2_build_mask(const void* q, const void* k, int dtype,

@@ -85,6 +85,12 @@ def test_build_mask_validation():
         (dict(N=300), _lib.SA2_EINVAL),          # mask geometry no longer matches
         (dict(wsb=16), _lib.SA2_EINVAL),
     ]
+    # more (batch, head) pairs than a grid dimension holds
+    big = _lib.Sa2Mask(1, 70000, 256, 64, 64, 4, 4, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20,
+                       None, None)
+    st = L.sa2_build_mask(FAKE, FAKE, 0, 1, 70000, 256, 64, 64, 64, 0.1, 0.5, ctypes.byref(big),
+                          ws, 1 << 40, None)
+    assert st == _lib.SA2_EUNSUPPORTED, st
     for kw, want in cases:
         st, msg = _status_and_msg(call(args(**kw)))
         assert st == want, (kw, st, msg)
