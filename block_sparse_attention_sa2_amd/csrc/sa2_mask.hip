@@ -325,10 +325,11 @@ __device__ inline double wave_sum_f64(double v) {
 // longer ones), and the 64 C candidates are sorted.  The candidates' first c
 // are the row's first c exactly when every lane's best entry left out (its
 // C+1-th) ranks after candidate c - 1.  Otherwise, or when c exceeds 64 C or
-// the candidates' mass does not reach p, the row is
-// marked (row_cnt = -1) and a second launch of the whole-row sort (with
-// `marked`) finishes just the marked rows.  Either way the kept set is the
-// one the full ranking gives.
+// the candidates' mass does not reach p, the whole row is sorted: in the same
+// wave for rows of up to 512 blocks (their E entries are still in its
+// registers), and for longer rows by a second launch of the whole-row sort
+// (with `marked`) that finishes just the rows marked row_cnt = -1.  Either way
+// the kept set is the one the full ranking gives.
 template <int E, bool CAND>
 __global__ __launch_bounds__(64 * kSelectWaves)
 void select_wave_kernel(const double* __restrict__ sbar, int nrows, int Tk, int kc, double p,
@@ -413,12 +414,15 @@ void select_wave_kernel(const double* __restrict__ sbar, int nrows, int Tk, int 
         idx[e] = (uint32_t)j;
       }
     }
-    if constexpr (CAND) {
+    if constexpr (CAND && E > 8) {
       if (whole) {   // left to the whole-row launch
         if (lane == 0) row_cnt[row] = -1;
         return;
       }
-    } else {
+    }
+    // rows of up to 512 blocks whose candidates fall short are sorted whole
+    // here, from the same registers (a bitonic network takes any input order)
+    if (!CAND || whole) {
       sort_wave<E>(key, idx, lane);
       int pc = 0;
       if (p >= 1.0) {
@@ -660,7 +664,7 @@ extern "C" sa2_status sa2_build_mask(const void* q, const void* k, int dtype, in
     case 1: SA2_SELECT(1, false, 0); break;
     case 2: SA2_SELECT(2, false, 0); break;
     case 4: SA2_SELECT(4, false, 0); break;
-    case 8: SA2_SELECT_LONG(8); break;
+    case 8: SA2_SELECT(8, true, 0); break;
     case 16: SA2_SELECT_LONG(16); break;
     case 32: SA2_SELECT_LONG(32); break;
     default: SA2_SELECT_LONG(64); break;
