@@ -163,6 +163,31 @@ class HeadMask:
                     out[i] = True
         return out
 
+    def allowed_counts(self, p: float, tol: float) -> list[set[int]]:
+        """Per row, the kept counts that an exact evaluation in another
+        summation order may give when the running mass at the Top-p cut lies
+        within tol of p.
+
+        The cut is pc = the first m whose running sum run[m-1] reaches p, so
+        run[pc-2] < p <= run[pc-1].  If run[pc-2] is within tol of p, another
+        order may already reach p there (Top-p keeps pc - 1); if run[pc-1] is
+        within tol of p, another order may still fall short (Top-p keeps
+        pc + 1).  The row keeps max(kc, that count), so a shifted cut below
+        kc changes nothing.  Every set holds the row's own count.
+        """
+        Tq, Tk = self.S.shape
+        out = [{int(c)} for c in self.count]
+        if p <= 0 or p >= 1:
+            return out
+        for i in range(Tq):
+            run = np.cumsum(self.P[i, self.order[i]])
+            m = int(self.pc[i])
+            if m >= 2 and abs(run[m - 2] - p) <= tol:
+                out[i].add(max(int(self.kc), m - 1))
+            if m <= Tk - 1 and abs(run[m - 1] - p) <= tol:
+                out[i].add(max(int(self.kc), m + 1))
+        return out
+
 
 def build_mask_head(Q: np.ndarray, K: np.ndarray, bq: int, bk: int,
                     k_frac: float, p: float) -> HeadMask:

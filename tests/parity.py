@@ -3,12 +3,17 @@
 Tolerances (from the statement of the problem this build answers):
   mask   bit-exact, except blocks whose pooled score lies within 1e-6 of
          the row's selection threshold (the score of the row's last kept
-         block), and rows whose cumulative mass at the Top-p cut lies
-         within 1e-6 of p ("mass near-ties");
+         block), and rows whose cumulative mass at the Top-p cut lies within
+         1e-12 of p ("mass near-ties": both sides sum in fp64, in different
+         orders); such a row may keep one block more or fewer than the
+         oracle's, and must still be a prefix of the oracle's ranking;
   O      max-abs <= 1e-2 and mean-abs <= 1e-3;
   dQ, dK, dV   relative Frobenius error <= 2e-2.
 """
 from __future__ import annotations
+
+import json
+import os
 
 import numpy as np
 import torch
@@ -17,7 +22,7 @@ import oracle as O
 import workloads as W
 
 SCORE_TOL = 1e-6
-MASS_TOL = 1e-6
+MASS_TOL = 1e-12
 O_MAX_ABS = 1e-2
 O_MEAN_ABS = 1e-3
 GRAD_REL_FRO = 2e-2
@@ -48,8 +53,10 @@ def compare_mask(hm: O.HeadMask, bitmap_gpu: np.ndarray, p: float):
     """
     bm = hm.bitmap
     diff_rows = np.nonzero((bm != bitmap_gpu).any(axis=1))[0]
+    if diff_rows.size == 0:
+        return bm.shape[0], 0, 0
     tau = hm.threshold()
-    near_p = hm.mass_near_p(p, MASS_TOL)
+    allowed = hm.allowed_counts(p, MASS_TOL)
     ties = 0
     mass = 0
     for i in diff_rows:
@@ -57,9 +64,9 @@ def compare_mask(hm: O.HeadMask, bitmap_gpu: np.ndarray, p: float):
         if np.all(np.abs(hm.S[i, js] - tau[i]) <= SCORE_TOL):
             ties += len(js)
             continue
-        if near_p[i]:
-            # the GPU row must still be a prefix of the oracle's ranking
-            n = int(bitmap_gpu[i].sum())
+        n = int(bitmap_gpu[i].sum())
+        if n != int(hm.count[i]) and n in allowed[i]:
+            # the Top-p cut moved by one block: still a prefix of the ranking
             want = np.zeros_like(bm[i])
             want[hm.order[i, :n]] = 1
             assert np.array_equal(want, bitmap_gpu[i]), f"row {i}: not a ranking prefix"
@@ -67,8 +74,30 @@ def compare_mask(hm: O.HeadMask, bitmap_gpu: np.ndarray, p: float):
             continue
         raise AssertionError(
             f"row {i}: blocks {js.tolist()} differ; scores {hm.S[i, js].tolist()}, "
-            f"threshold {tau[i]}, counts oracle {int(bm[i].sum())} gpu {int(bitmap_gpu[i].sum())}")
+            f"threshold {tau[i]}, counts oracle {int(bm[i].sum())} gpu {n}")
     return bm.shape[0] - len(diff_rows), ties, mass
+
+
+def log_mask_exceptions(test: str, workload: str, heads: int, rows: int, exact_rows: int,
+                        tie_blocks: int, mass_rows: int) -> None:
+    """Append one JSON line of mask-comparison totals to $SA2_PARITY_LOG (if set)."""
+    path = os.environ.get("SA2_PARITY_LOG")
+    if not path:
+        return
+    rec = dict(test=test, workload=workload, heads=heads, rows=rows, exact_rows=exact_rows,
+               score_tie_blocks=tie_blocks, mass_near_tie_rows=mass_rows,
+               score_tol=SCORE_TOL, mass_tol=MASS_TOL)
+    with open(path, "a") as fh:
+        fh.write(json.dumps(rec) + "\n")
+
+
+def log_parity(test: str, workload: str, **errors) -> None:
+    """Append one JSON line of worst-case numeric errors to $SA2_PARITY_LOG (if set)."""
+    path = os.environ.get("SA2_PARITY_LOG")
+    if not path:
+        return
+    with open(path, "a") as fh:
+        fh.write(json.dumps(dict(test=test, workload=workload, **errors)) + "\n")
 
 
 def check_lists(bitmap: np.ndarray, row_cnt, row_idx, col_cnt, col_idx):
@@ -110,19 +139,12 @@ def rel_fro(a: np.ndarray, b: np.ndarray) -> float:
 
 
 def check_forward(o_gpu: np.ndarray, lse_gpu: np.ndarray, o_ref: np.ndarray, lse_ref: np.ndarray,
-                  what: str = "", scale_with_output: bool = False):
-    """O within max-abs 1e-2 / mean-abs 1e-3 and LSE within 1e-2.
-
-    scale_with_output: P enters the P.V product as bf16, whose rounding is up
-    to 2^-9 of each term, so the error of O grows with |O|; the absolute
-    tolerances hold for |O| <= 2.5.  For inputs with larger outputs they are
-    multiplied by max|O| / 2.5.
-    """
+                  what: str = ""):
+    """O within max-abs 1e-2 / mean-abs 1e-3 and LSE within 1e-2."""
     err = np.abs(o_gpu - o_ref)
-    f = max(1.0, float(np.abs(o_ref).max()) / 2.5) if scale_with_output else 1.0
     assert np.isfinite(o_gpu).all(), f"{what}: non-finite O"
-    assert err.max() <= O_MAX_ABS * f, f"{what}: O max-abs {err.max():.3e} (factor {f:.2f})"
-    assert err.mean() <= O_MEAN_ABS * f, f"{what}: O mean-abs {err.mean():.3e} (factor {f:.2f})"
+    assert err.max() <= O_MAX_ABS, f"{what}: O max-abs {err.max():.3e}"
+    assert err.mean() <= O_MEAN_ABS, f"{what}: O mean-abs {err.mean():.3e}"
     lerr = np.abs(lse_gpu - lse_ref).max()
     assert lerr <= LSE_MAX_ABS, f"{what}: LSE max-abs {lerr:.3e}"
     return float(err.max()), float(err.mean())

@@ -59,6 +59,41 @@ def test_hand_worked_masks():
     assert n == 14
 
 
+def _closed_form_runs():
+    """r1..r3 of the row m = [0, 2, -1, 1] from their closed forms (see the fixture)."""
+    e = math.e
+    Z = e * e + e + 1.0 + 1.0 / e
+    return {"r1": e * e / Z, "r2": (e * e + e) / Z, "r3": (e * e + e + 1.0) / Z}
+
+
+def test_checker_threshold_hand_worked():
+    """HeadMask.threshold(): the pooled score of each row's last kept block."""
+    fx = json.loads((GOLDEN / "mask_checker_hand.json").read_text())
+    for c in fx["threshold_cases"]:
+        Q, K = _hand_qk(c["m"])
+        hm = O.build_mask_head(Q, K, 8, 2, c["k_frac"], c["p"])
+        assert int(hm.count[0]) == c["count"], c
+        assert hm.threshold()[0] == c["threshold"], c
+
+
+def test_checker_mass_near_p_hand_worked():
+    """HeadMask.mass_near_p() and allowed_counts() at the Top-p cut: rows whose
+    running mass lies 5e-7 and 2e-6 from p, on either side of the cut, and a
+    Top-k count that hides a moved cut."""
+    fx = json.loads((GOLDEN / "mask_checker_hand.json").read_text())
+    runs = _closed_form_runs()
+    Q, K = _hand_qk([0.0, 2.0, -1.0, 1.0])
+    for c in fx["mass_cases"]:
+        p = runs[c["base"]] + c["offset"]
+        hm = O.build_mask_head(Q, K, 8, 2, c["k_frac"], p)
+        assert int(hm.pc[0]) == c["pc"], c
+        assert bool(hm.mass_near_p(p, c["tol"])[0]) == c["near"], c
+        assert hm.allowed_counts(p, c["tol"])[0] == set(c["allowed"]), c
+    # the rules are off: nothing is near, only the own count is allowed
+    hm = O.build_mask_head(Q, K, 8, 2, 0.5, 0.0)
+    assert not hm.mass_near_p(0.0, 1.0)[0] and hm.allowed_counts(0.0, 1.0)[0] == {2}
+
+
 def test_pooling_brute_force_and_ragged():
     X = _rand((13, 3), 1)
     P = O.pool_blocks(X, 4)      # blocks of 4, 4, 4, 1
