@@ -132,8 +132,19 @@ def cpu_baseline(w, k_frac, p, ref, heads, eff_flops_layer):
             "sample": f"{heads} of {w.H} heads of the same layer (mask + forward + backward, "
                       f"numpy fp64, gathered over kept blocks); {dt:.2f} s; "
                       f"ms/layer extrapolated x{w.H // heads if w.H % heads == 0 else w.H / heads:.3g}",
-            "ms_per_layer": dt * 1e3 * w.H / heads, "seconds": dt,
-            "cpu": platform.processor() or platform.machine()}
+            "ms_per_layer": dt * 1e3 * w.H / heads, "seconds": dt, "cpu": cpu_model()}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), else the machine type."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
 
 
 def dense_baseline(sa2, q, k, v, do, w, sparse_attn_ms, args):

@@ -170,6 +170,19 @@ __device__ inline bf16x8 rd_tr(const uint16_t* tile, const SwzAddr& A, int t, in
              lds_read_tr(reinterpret_cast<const uint16_t*>(b + A.tr(t, db, 1))));
 }
 
+// Eight terms of Delta_t = sum_c dO_tc O_tc: O as stored, dO as the bf16
+// MFMA operand it enters dP = dO V^T with (for fp32 inputs the rounded
+// values), so that dP - Delta cancels exactly where the row's P is one-hot.
+template <typename T>
+__device__ inline float delta_part(const T* o8, bf16x8 dof) {
+  float a[8];
+  load8_f32(o8, a);
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += a[i] * (float)dof[i];
+  return s;
+}
+
 // ---------------------------------------------------------------------------
 // Forward
 // ---------------------------------------------------------------------------
@@ -267,13 +280,23 @@ void fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
         ps += pv;
       }
     lsum += ps;
-    // O^T += V^T P^T over four 16-key steps
+    // O^T += V^T P^T over four 16-key steps.  For fp32 inputs P enters as a
+    // pair of bf16 terms (its rounding and the rounding's residual), so that
+    // O carries P to about 16 bits rather than bf16's 8.
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
       const bf16x8 pf = pack8(s[tt >> 1], 8 * (tt & 1));
 #pragma unroll
       for (int db = 0; db < ND; ++db)
         acc[db] = mfma32(tr_operand<D, kCols>(v_lds, 16 * tt, 32 * db, lane), pf, acc[db]);
+      if constexpr (sizeof(T) == 4) {
+        bf16x8 lo;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) lo[i] = (__bf16)(s[tt >> 1][8 * (tt & 1) + i] - (float)pf[i]);
+#pragma unroll
+        for (int db = 0; db < ND; ++db)
+          acc[db] = mfma32(tr_operand<D, kCols>(v_lds, 16 * tt, 32 * db, lane), lo, acc[db]);
+      }
     }
   }
   const float ltot = wave_sum32(lsum);
@@ -761,13 +784,7 @@ void dq_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const size_t off = base + (size_t)qrow * D + 16 * kk + 8 * h;
     qf[kk] = qvalid ? load8(q + off) : zero8();
     df[kk] = qvalid ? load8(dout + off) : zero8();
-    if (qvalid) {
-      float a[8], b[8];
-      load8_f32(o + off, a);
-      load8_f32(dout + off, b);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) dpart += a[i] * b[i];
-    }
+    if (qvalid) dpart += delta_part(o + off, df[kk]);
   }
   // Delta = rowsum(dO * O): the two half-waves hold alternate 8-wide pieces
   // of the row.  Both statistics of every row of the block, padding rows
@@ -1312,13 +1329,7 @@ void dq_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __rest
     const size_t off = base + (size_t)qrow * D + 16 * kk + 8 * h;
     qf[kk] = qvalid ? load8(q + off) : zero8();
     df[kk] = qvalid ? load8(dout + off) : zero8();
-    if (qvalid) {
-      float a[8], b[8];
-      load8_f32(o + off, a);
-      load8_f32(dout + off, b);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) dpart += a[i] * b[i];
-    }
+    if (qvalid) dpart += delta_part(o + off, df[kk]);
   }
   // Delta = rowsum(dO * O): the two half-waves hold alternate 8-wide pieces
   // of the row.  It is kept for the dK/dV kernel.  Padding rows: dO = 0 and
@@ -1621,6 +1632,8 @@ extern "C" sa2_status sa2_attn_bwd_dq(const void* q, const void* k, const void* 
   if (!aligned16(o) || !aligned16(dq))
     return fail(SA2_EINVAL, "sa2_attn_bwd_dq: pointers must be 16-byte aligned");
   if (!m->row_cnt || !m->row_idx) return fail(SA2_EINVAL, "sa2_attn_bwd_dq: mask row lists are null");
+  if (dtype == SA2_BF16 && d == 128 && !m->col_cnt)   // the dK/dV plan reads the column counts
+    return fail(SA2_EINVAL, "sa2_attn_bwd_dq: mask column counts are null (bf16, d = 128)");
   by_type<DqLaunch>(dtype, d, bwd_args(q, k, v, o, lse, dout, B, H, N, d, m, dq, nullptr, nullptr, ws, stream));
   return check_launch("dq_kernel");
 }

@@ -80,8 +80,10 @@ typedef enum { SA2_BF16 = 0, SA2_F32 = 1 } sa2_dtype;
  *
  * sa2_build_mask writes all these arrays; the attention calls read row_cnt /
  * row_idx (forward, dQ) and col_cnt / col_idx (dK, dV), and the orders when
- * present.  A caller may supply its own mask to the attention calls as long as
- * the lists are ascending, duplicate-free and in range, every row_cnt is at
+ * present.  For bf16 and d = 128 the dQ call also reads col_cnt (it writes
+ * the dK/dV work plan, which depends on the column counts).  A caller may
+ * supply its own mask to the attention calls as long as the lists are
+ * ascending, duplicate-free and in range, every row_cnt is at
  * least 1, and the orders (if given) are permutations.  A mask that breaks
  * these rules gives undefined outputs but no access out of range: counts are
  * clamped to [0, Tk] (rows) and [0, Tq] (columns), list entries outside the
@@ -201,7 +203,8 @@ sa2_status sa2_attn_bwd(const void* q, const void* k, const void* v,
  * row list, and Delta_t = sum_c dO_tc O_tc and lse_t * log2(e), which it
  * leaves in `workspace` for sa2_attn_bwd_dkdv, together with (bf16, d = 128)
  * the dK/dV work plan made from the mask's column counts.  Arguments as for
- * sa2_attn_bwd.
+ * sa2_attn_bwd; it reads row_cnt and row_idx, and for bf16 with d = 128 also
+ * col_cnt (SA2_EINVAL if that is NULL).
  */
 sa2_status sa2_attn_bwd_dq(const void* q, const void* k, const void* v,
                            const void* o, const float* lse, const void* dout,

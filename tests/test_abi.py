@@ -116,6 +116,23 @@ def test_attention_validation():
     assert st == _lib.SA2_EINVAL and "workspace" in msg
 
 
+def test_dq_refuses_a_mask_without_column_counts():
+    """bf16, d = 128: the dQ call writes the dK/dV plan from col_cnt, so a
+    mask without it is refused before any launch (fake pointers, never read)."""
+    L = _lib.lib()
+    B, H, N, bq, bk = 1, 1, 256, 128, 64
+    m = _lib.Sa2Mask(B, H, N, bq, bk, 2, 4, 1 << 20, 1 << 20, 1 << 20, None, 1 << 20, None, None)
+    ws = ctypes.c_void_p(1 << 20)
+    wsb = L.sa2_bwd_workspace_bytes(B, H, N, 128)
+    st, msg = _status_and_msg(L.sa2_attn_bwd_dq(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, B, H, N,
+                                                128, ctypes.byref(m), FAKE, ws, wsb, None))
+    assert st == _lib.SA2_EINVAL and "column counts" in msg, msg
+    st, msg = _status_and_msg(L.sa2_attn_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, B, H, N,
+                                             128, ctypes.byref(m), FAKE, FAKE, FAKE, ws, wsb,
+                                             None))
+    assert st == _lib.SA2_EINVAL and "column counts" in msg, msg
+
+
 def test_python_binding_refuses_cpu_tensors():
     import torch
     import block_sparse_attention_sa2_amd as sa2

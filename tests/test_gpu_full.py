@@ -3,16 +3,23 @@ benchmark times (one call per step over all heads).
 
 * Wan2.1-1.3B-shaped layer (H=12, N=32760 = 21x30x52, d=128, bf16, q-block
   128, k-block 64, k = 3%, p tuned for 5% density), forward and backward,
-  and the same layer in a second block geometry (64 x 64 blocks):
-  the whole mask of every head against the oracle; O, LSE, dQ, dK, dV on
-  sampled blocks of every head (first, a random interior one, the ragged
-  last one); closed-form invariants of the gradients on every head.
-* 14B-720p-shaped layer (H=40, N=75600 = 21x45x80): the mask of heads 0 and
-  39 against the oracle, sampled attention blocks of those heads, and the
-  union invariants on every head.
+  and the same layer in a second block geometry (64 x 64 blocks): the whole
+  mask of every head against the oracle; every element of O, LSE, dQ, dK and
+  dV of every head against the oracle's gathered evaluation; closed-form
+  invariants of the gradients on every head.
+* 14B-720p-shaped layer (H=40, N=75600 = 21x45x80): heads 0 and 39 in full
+  against the oracle (mask, O, LSE, dQ, dK, dV); on all 40 heads, the hybrid
+  mask equals the union of the library's Top-k-only and Top-p-only masks,
+  every row keeps at least kc blocks, and the gradient invariants hold
+  (evaluated on the device in fp64).
 * Mask-rule stress (H=8, N=16384): three score regimes x four densities; the
   hybrid mask contains the Top-k-only and Top-p-only masks on every head and
-  equals their union; head 0 against the oracle; sampled attention blocks.
+  equals their union; head 0 against the oracle in full.
+* The largest key-block count (4096) at one head.
+
+Mask-comparison totals (rows compared, exact rows, score near-tie blocks,
+mass near-tie rows) and the worst numeric errors are appended to the file
+named by $SA2_PARITY_LOG when it is set.
 """
 from __future__ import annotations
 
@@ -27,7 +34,7 @@ import oracle as O
 import workloads as W
 
 from parity import (GRAD_REL_FRO, check_forward, check_grad, check_lists, check_orders,
-                    compare_mask, device_inputs, f64, rel_fro)
+                    compare_mask, device_inputs, f64, log_mask_exceptions, log_parity)
 
 pytestmark = pytest.mark.gpu
 
@@ -45,47 +52,59 @@ def _row_lists(mask_np_bm):
     return [np.nonzero(r)[0] for r in mask_np_bm]
 
 
-def _spot_check(w, ref, h, bm_h, o, lse, grads, rng, n_q=3, n_k=3):
-    """O/LSE and gradients of a few blocks of head h against the oracle."""
+def _whole_head(w, ref, h, bm_h, o, lse, grads, b=0):
+    """Every element of O, LSE (and dQ, dK, dV) of head h against the oracle's
+    gathered evaluation (each query block over its kept key blocks only);
+    returns the worst errors."""
     Q, K, V, dO = _head_np(ref, h)
     rows = _row_lists(bm_h)
-    Tq, Tk = bm_h.shape
-    qbs = sorted({0, Tq - 1, *rng.integers(1, Tq - 1, size=n_q - 2).tolist()})
-    kbs = sorted({0, Tk - 1, *rng.integers(1, Tk - 1, size=n_k - 2).tolist()})
-    o_h, l_h = f64(o[0, h]), f64(lse[0, h])
-    for i in qbs:
-        lo, hi = O.block_range(i, w.bq, w.N)
-        oi, li = O.forward_query_block(Q, K, V, rows, w.bq, w.bk, i)
-        check_forward(o_h[lo:hi], l_h[lo:hi], oi, li, f"{w.name} h{h} qblock {i}")
     if grads is None:
-        return
-    dq, dk, dv = (f64(g[0, h]) for g in grads)
-    mine, want = [], []
-    for i in qbs:
-        lo, hi = O.block_range(i, w.bq, w.N)
-        mine.append(dq[lo:hi])
-        want.append(O.dq_query_block(Q, K, V, dO, rows, w.bq, w.bk, i))
-    check_grad(np.concatenate(mine), np.concatenate(want), f"{w.name} h{h} dq")
-    mk, wk, mv, wv = [], [], [], []
-    for j in kbs:
-        lo, hi = O.block_range(j, w.bk, w.N)
-        k_j, v_j = O.dkdv_key_block(Q, K, V, dO, rows, w.bq, w.bk, j)
-        mk.append(dk[lo:hi]); wk.append(k_j)
-        mv.append(dv[lo:hi]); wv.append(v_j)
-    if np.linalg.norm(np.concatenate(wk)) > 0:
-        check_grad(np.concatenate(mk), np.concatenate(wk), f"{w.name} h{h} dk")
-        check_grad(np.concatenate(mv), np.concatenate(wv), f"{w.name} h{h} dv")
+        Oo, L = O.attention_gathered(Q, K, V, rows, w.bq, w.bk)
+    else:
+        Oo, L, rq, rk, rv = O.attention_gathered(Q, K, V, rows, w.bq, w.bk, dO=dO)
+    om, oa = check_forward(f64(o[b, h]), f64(lse[b, h]), Oo, L, f"{w.name} h{h}")
+    out = dict(o_max=om, o_mean=oa)
+    if grads is not None:
+        for name, g, want in zip(("dq", "dk", "dv"), grads, (rq, rk, rv)):
+            out[name] = check_grad(f64(g[b, h]), want, f"{w.name} h{h} {name}")
+    return out
+
+
+def _worst(acc, e):
+    for k_, v_ in e.items():
+        acc[k_] = max(acc.get(k_, 0.0), v_)
+    return acc
 
 
 def _invariants(q, k, dq, dk, dv, do, h):
-    """sum_u dK_u = 0, sum_u dV_u = sum_t dO_t, <Q, dQ> = <K, dK> (fixed mask)."""
-    Q, K = f64(q[0, h]), f64(k[0, h])
-    dQ, dK, dV, dO = (f64(t[0, h]) for t in (dq, dk, dv, do))
-    scale = np.abs(dK).sum(axis=0).max()
-    assert np.abs(dK.sum(axis=0)).max() <= GRAD_REL_FRO * scale, f"h{h}: sum dK"
-    assert rel_fro(dV.sum(axis=0), dO.sum(axis=0)) <= GRAD_REL_FRO, f"h{h}: sum dV"
-    a, b = (Q * dQ).sum(), (K * dK).sum()
-    assert abs(a - b) <= GRAD_REL_FRO * max(abs(a), abs(b), np.abs(Q * dQ).sum() * 1e-3), f"h{h}: <Q,dQ>"
+    """sum_u dK_u = 0, sum_u dV_u = sum_t dO_t, <Q, dQ> = <K, dK> (fixed mask),
+    on the device in fp64."""
+    Q, K, dQ, dK, dV, dO = (t[0, h].double() for t in (q, k, dq, dk, dv, do))
+    scale = float(dK.abs().sum(dim=0).max())
+    assert float(dK.sum(dim=0).abs().max()) <= GRAD_REL_FRO * scale, f"h{h}: sum dK"
+    sv, so = dV.sum(dim=0), dO.sum(dim=0)
+    assert float((sv - so).norm()) <= GRAD_REL_FRO * float(so.norm()), f"h{h}: sum dV"
+    qd, kd = float((Q * dQ).sum()), float((K * dK).sum())
+    floor = float((Q * dQ).abs().sum()) * 1e-3
+    assert abs(qd - kd) <= GRAD_REL_FRO * max(abs(qd), abs(kd), floor), f"h{h}: <Q,dQ>"
+
+
+def _mask_all_heads(test, w, mask, ref, k_frac, p, heads):
+    """The mask of `heads` against the oracle (bitmap, lists), with the totals logged."""
+    bm = mask.bitmap.cpu().numpy()
+    rc, ri = mask.row_cnt.cpu().numpy(), mask.row_idx.cpu().numpy()
+    cc, ci = mask.col_cnt.cpu().numpy(), mask.col_idx.cpu().numpy()
+    exact = ties = mass = 0
+    for h in heads:
+        hm = O.build_mask_head(ref["q"][0, h], ref["k"][0, h], w.bq, w.bk, k_frac, p)
+        e_, t_, m_ = compare_mask(hm, bm[0, h], p)
+        exact += e_; ties += t_; mass += m_
+        check_lists(bm[0, h], rc[0, h], ri[0, h], cc[0, h], ci[0, h])
+    rows = len(heads) * mask.Tq
+    _say(f"[{w.name}] mask: {rows} rows, {exact} exact, {ties} score near-tie blocks, "
+         f"{mass} mass near-tie rows")
+    log_mask_exceptions(test, w.name, len(heads), rows, exact, ties, mass)
+    return bm
 
 
 # ---------------------------------------------------------------------------
@@ -108,28 +127,26 @@ def wan13(request):
 
 def test_wan13_mask_all_heads(wan13):
     w, mask, ref = wan13["w"], wan13["mask"], wan13["ref"]
-    bm = mask.bitmap.cpu().numpy()
-    rc, ri = mask.row_cnt.cpu().numpy(), mask.row_idx.cpu().numpy()
-    cc, ci = mask.col_cnt.cpu().numpy(), mask.col_idx.cpu().numpy()
-    check_orders(rc, cc, mask.row_order.cpu().numpy(), mask.col_order.cpu().numpy())
-    ties = mass = 0
-    for h in range(w.H):
-        Q, K = ref["q"][0, h], ref["k"][0, h]
-        hm = O.build_mask_head(Q, K, w.bq, w.bk, wan13["k_frac"], wan13["p"])
-        _, t_, m_ = compare_mask(hm, bm[0, h], wan13["p"])
-        ties += t_; mass += m_
-        check_lists(bm[0, h], rc[0, h], ri[0, h], cc[0, h], ci[0, h])
+    check_orders(mask.row_cnt.cpu().numpy(), mask.col_cnt.cpu().numpy(),
+                 mask.row_order.cpu().numpy(), mask.col_order.cpu().numpy())
+    _mask_all_heads("wan13_mask_all_heads", w, mask, ref, wan13["k_frac"], wan13["p"],
+                    range(w.H))
     dens = mask.density()
-    _say(f"[wan1.3B] density {dens:.5f}, near-tie blocks {ties}, mass near-tie rows {mass}")
+    _say(f"[wan1.3B] density {dens:.5f}")
     assert abs(dens - 0.05) <= 0.02 * 0.05 + 1e-4
 
 
-def test_wan13_attention_sampled(wan13):
+def test_wan13_attention_whole_layer(wan13):
+    """O, LSE, dQ, dK, dV: every element of every head against the oracle."""
     w, ref = wan13["w"], wan13["ref"]
     bm = wan13["mask"].bitmap.cpu().numpy()
-    rng = np.random.default_rng(0)
+    worst = {}
     for h in range(w.H):
-        _spot_check(w, ref, h, bm[0, h], wan13["o"], wan13["lse"], wan13["grads"], rng)
+        _worst(worst, _whole_head(w, ref, h, bm[0, h], wan13["o"], wan13["lse"],
+                                  wan13["grads"]))
+    _say(f"[{w.name}] worst over {w.H} heads: " +
+         ", ".join(f"{k_} {v_:.2e}" for k_, v_ in worst.items()))
+    log_parity("wan13_attention_whole_layer", w.name, heads=w.H, **worst)
 
 
 def test_wan13_gradient_invariants(wan13):
@@ -157,28 +174,46 @@ def wan14():
     return dict(w=w, k_frac=k_frac, p=p, dev=dev, ref=ref, mask=mask, o=o, lse=lse, grads=grads)
 
 
-def test_wan14_mask_and_attention(wan14):
+def test_wan14_heads_against_the_oracle(wan14):
+    """Heads 0 and 39 in full: mask, O, LSE, dQ, dK, dV."""
     w, mask, ref = wan14["w"], wan14["mask"], wan14["ref"]
-    bm = mask.bitmap.cpu().numpy()
-    rc, ri = mask.row_cnt.cpu().numpy(), mask.row_idx.cpu().numpy()
-    cc, ci = mask.col_cnt.cpu().numpy(), mask.col_idx.cpu().numpy()
-    rng = np.random.default_rng(1)
-    for h in (0, w.H - 1):
-        hm = O.build_mask_head(ref["q"][0, h], ref["k"][0, h], w.bq, w.bk, wan14["k_frac"],
-                               wan14["p"])
-        compare_mask(hm, bm[0, h], wan14["p"])
-        check_lists(bm[0, h], rc[0, h], ri[0, h], cc[0, h], ci[0, h])
-        _spot_check(w, ref, h, bm[0, h], wan14["o"], wan14["lse"], wan14["grads"], rng)
+    heads = (0, w.H - 1)
+    bm = _mask_all_heads("wan14_heads_against_the_oracle", w, mask, ref, wan14["k_frac"],
+                         wan14["p"], heads)
+    worst = {}
+    for h in heads:
+        _worst(worst, _whole_head(w, ref, h, bm[0, h], wan14["o"], wan14["lse"],
+                                  wan14["grads"]))
+    _say(f"[{w.name}] worst over heads {heads}: " +
+         ", ".join(f"{k_} {v_:.2e}" for k_, v_ in worst.items()))
+    log_parity("wan14_heads_against_the_oracle", w.name, heads=len(heads), **worst)
     dens = mask.density()
     _say(f"[wan14B] density {dens:.5f}")
     assert abs(dens - 0.05) <= 0.02 * 0.05 + 1e-4
 
 
-def test_wan14_rows_keep_the_topk_prefix(wan14):
-    """Every row of every head keeps at least kc blocks and its top-ranked block."""
-    w, mask = wan14["w"], wan14["mask"]
+def test_wan14_union_every_head(wan14):
+    """On all 40 heads: the hybrid mask contains the library's Top-k-only and
+    Top-p-only masks and equals their union (gist.science 2A), and every row
+    keeps at least kc blocks."""
+    w, mask, dev = wan14["w"], wan14["mask"], wan14["dev"]
+    q, k = dev["q"], dev["k"]
+    hy = mask.bitmap
+    ko = sa2.build_mask(q, k, w.bq, w.bk, wan14["k_frac"], 0.0).bitmap
+    po = sa2.build_mask(q, k, w.bq, w.bk, 0.0, wan14["p"]).bitmap
+    torch.cuda.synchronize()
+    assert torch.all(hy >= ko) and torch.all(hy >= po)
+    assert torch.equal(hy, torch.maximum(ko, po))
     kc = O.topk_count(wan14["k_frac"], mask.Tk)
+    assert int(ko.sum(dim=-1).min()) == kc and int(ko.sum(dim=-1).max()) == kc
     assert int(mask.row_cnt.min().item()) >= kc
+
+
+def test_wan14_gradient_invariants_every_head(wan14):
+    w, dev = wan14["w"], wan14["dev"]
+    dq, dk, dv = wan14["grads"]
+    for h in range(w.H):
+        _invariants(dev["q"], dev["k"], dq, dk, dv, dev["do"], h)
 
 
 # ---------------------------------------------------------------------------
@@ -221,13 +256,16 @@ def test_stress_union_and_oracle(name, stress_inputs):
     torch.cuda.synchronize()
     bm = hy_bm.cpu().numpy()
     hm = O.build_mask_head(ref["q"][0, 0], ref["k"][0, 0], w.bq, w.bk, k_frac, p)
-    compare_mask(hm, bm[0, 0], p)
+    ex, ti, ma = compare_mask(hm, bm[0, 0], p)
+    log_mask_exceptions("stress_union_and_oracle", name, 1, w.Tq, ex, ti, ma)
     # each rule on its own, as a mode of its own, against the oracle
     ko_h = O.build_mask_head(ref["q"][0, 0], ref["k"][0, 0], w.bq, w.bk, k_frac, 0.0)
     compare_mask(ko_h, ko.cpu().numpy()[0, 0], 0.0)
     po_h = O.build_mask_head(ref["q"][0, 0], ref["k"][0, 0], w.bq, w.bk, 0.0, p)
-    compare_mask(po_h, po.cpu().numpy()[0, 0], p)
-    _spot_check(w, ref, 0, bm[0, 0], o, lse, grads, np.random.default_rng(2))
+    ex, ti, ma = compare_mask(po_h, po.cpu().numpy()[0, 0], p)
+    log_mask_exceptions("stress_union_and_oracle/top-p only", name, 1, w.Tq, ex, ti, ma)
+    worst = _whole_head(w, ref, 0, bm[0, 0], o, lse, grads)
+    log_parity("stress_union_and_oracle", name, heads=1, **worst)
     dens = hy.density()
     want = W.tuned_record(name)["density"]
     _say(f"[stress] {name} density {dens:.5f} (oracle {want:.5f}, target {w.target_density})")
@@ -256,14 +294,11 @@ def test_max_key_blocks(max_tk, p):
     mask = sa2.build_mask(q, k, w.bq, w.bk, w.k_frac, p)
     torch.cuda.synchronize()
     assert mask.Tk == 4096
-    bm = mask.bitmap.cpu().numpy()
-    hm = O.build_mask_head(ref["q"][0, 0], ref["k"][0, 0], w.bq, w.bk, w.k_frac, p)
-    compare_mask(hm, bm[0, 0], p)
-    check_lists(bm[0, 0], mask.row_cnt.cpu().numpy()[0, 0], mask.row_idx.cpu().numpy()[0, 0],
-                mask.col_cnt.cpu().numpy()[0, 0], mask.col_idx.cpu().numpy()[0, 0])
+    bm = _mask_all_heads(f"max_key_blocks p{p}", w, mask, ref, w.k_frac, p, [0])
     _say(f"[max Tk] p{p} kept per row {float(mask.row_cnt.float().mean()):.1f}")
     if p == 0.0:
         o, lse = sa2.attn_fwd(q, k, v, mask)
         grads = sa2.attn_bwd(q, k, v, o, lse, do, mask)
         torch.cuda.synchronize()
-        _spot_check(w, ref, 0, bm[0, 0], o, lse, grads, np.random.default_rng(3))
+        worst = _whole_head(w, ref, 0, bm[0, 0], o, lse, grads)
+        log_parity("max_key_blocks", w.name, heads=1, **worst)
