@@ -21,8 +21,8 @@ import torch
 from . import _lib
 from ._lib import Sa2Mask, check
 
-__all__ = ["BlockMask", "build_mask", "attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv",
-           "sparse_attention", "SparseAttention", "version", "mask_workspace_bytes",
+__all__ = ["BlockMask", "build_mask", "build_mask_noalloc", "attn_fwd", "attn_bwd", "attn_bwd_dq",
+           "attn_bwd_dkdv", "sparse_attention", "SparseAttention", "version", "mask_workspace_bytes",
            "bwd_workspace_bytes"]
 
 _DTYPES = {torch.bfloat16: _lib.SA2_BF16, torch.float32: _lib.SA2_F32}
@@ -158,6 +158,23 @@ def build_mask(q: torch.Tensor, k: torch.Tensor, bq: int, bk: int, k_frac: float
                           ctypes.byref(mask.c_struct()), _ptr(workspace), workspace.numel(),
                           _stream(q.device))
     check("sa2_build_mask", st)
+    return mask
+
+
+def build_mask_noalloc(q: torch.Tensor, k: torch.Tensor, bq: int, bk: int, k_frac: float,
+                       p: float, mask: BlockMask) -> BlockMask:
+    """The same mask as build_mask, written into the caller's `mask` with no
+    workspace and no allocation by the library (sa2_build_mask_noalloc); for
+    geometries whose workspace fits SA2_MASK_NOALLOC_MAX_BYTES."""
+    dt = _dtype_code(q, k)
+    B, H, N, d = _shape(q)
+    if _shape(k) != (B, H, N, d):
+        raise ValueError("q and k must have the same shape")
+    _same_device(mask, q.device)
+    st = _lib.lib().sa2_build_mask_noalloc(_ptr(q), _ptr(k), dt, B, H, N, d, bq, bk,
+                                           float(k_frac), float(p),
+                                           ctypes.byref(mask.c_struct()), _stream(q.device))
+    check("sa2_build_mask_noalloc", st)
     return mask
 
 

@@ -8,6 +8,7 @@ LIB_PATH = Path(__file__).resolve().parent / "libsa2.so"
 
 SA2_OK, SA2_EINVAL, SA2_EUNSUPPORTED, SA2_EDEVICE = 0, 1, 2, 3
 SA2_BF16, SA2_F32 = 0, 1
+SA2_MASK_NOALLOC_MAX_BYTES = 64 << 20   # include/sa2.h
 STATUS_NAMES = {0: "SA2_OK", 1: "SA2_EINVAL", 2: "SA2_EUNSUPPORTED", 3: "SA2_EDEVICE"}
 
 
@@ -34,6 +35,7 @@ SIGNATURES = {
     "sa2_last_error": ([], ctypes.c_char_p),
     "sa2_mask_workspace_bytes": ([_I, _I, _I, _I, _I, _I], _Z),
     "sa2_build_mask": ([_P, _P, _I, _I, _I, _I, _I, _I, _I, _D, _D, _MP, _P, _Z, _P], _I),
+    "sa2_build_mask_noalloc": ([_P, _P, _I, _I, _I, _I, _I, _I, _I, _D, _D, _MP, _P], _I),
     "sa2_attn_fwd": ([_P, _P, _P, _I, _I, _I, _I, _I, _MP, _P, _P, _P], _I),
     "sa2_bwd_workspace_bytes": ([_I, _I, _I, _I], _Z),
     "sa2_attn_bwd": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _MP, _P, _P, _P, _P, _Z, _P], _I),

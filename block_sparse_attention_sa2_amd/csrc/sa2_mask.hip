@@ -13,6 +13,9 @@
 // evaluation except where two scores, or the mass and p, agree to ~1e-15.
 #include <math.h>
 
+#include <mutex>
+#include <string>
+
 #include "sa2_common.h"
 
 namespace sa2 {
@@ -590,39 +593,128 @@ extern "C" size_t sa2_mask_workspace_bytes(int B, int H, int N, int d, int bq, i
   return up(BH * Tq * d * 8) + up(BH * Tk * d * 8) + up(BH * Tq * Tk * 8);
 }
 
+namespace sa2 {
+
+// Arguments of a mask build that can be checked on the host alone (no
+// workspace involved).
+static sa2_status check_mask_args(const char* fn, const void* q, const void* k, int dtype, int B,
+                                  int H, int N, int d, int bq, int bk, double k_frac, double p,
+                                  const sa2_mask* m) {
+  const std::string f(fn);
+  if (!q || !k || !m) return fail(SA2_EINVAL, f + ": null pointer");
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0 || bq <= 0 || bk <= 0)
+    return fail(SA2_EINVAL, f + ": B, H, N, d, bq, bk must be positive");
+  if (dtype != SA2_BF16 && dtype != SA2_F32) return fail(SA2_EINVAL, f + ": unknown dtype");
+  if (d % 8 != 0 || d > 256)
+    return fail(SA2_EUNSUPPORTED, f + ": d must be a multiple of 8 and at most 256");
+  if (!aligned16(q) || !aligned16(k)) return fail(SA2_EINVAL, f + ": q/k not 16-byte aligned");
+  if (std::isnan(k_frac) || std::isnan(p)) return fail(SA2_EINVAL, f + ": NaN k_frac or p");
+  if (k_frac <= 0.0 && p <= 0.0)
+    return fail(SA2_EINVAL, f + ": k_frac <= 0 and p <= 0 select nothing");
+  const int Tq = cdiv(N, bq), Tk = cdiv(N, bk);
+  if (m->B != B || m->H != H || m->N != N || m->bq != bq || m->bk != bk || m->Tq != Tq ||
+      m->Tk != Tk)
+    return fail(SA2_EINVAL, f + ": mask geometry does not match the call");
+  if (!m->bitmap || !m->row_cnt || !m->row_idx || !m->col_cnt || !m->col_idx)
+    return fail(SA2_EINVAL, f + ": mask array is null");
+  if (Tk > kMaxTk) return fail(SA2_EUNSUPPORTED, f + ": more than 4096 key blocks");
+  if (Tq > kMaxTk) return fail(SA2_EUNSUPPORTED, f + ": more than 4096 query blocks");
+  if ((size_t)B * H * Tq > 0x7fffffff || (size_t)B * H * (Tq + Tk) > 0x7fffffff)
+    return fail(SA2_EUNSUPPORTED, f + ": too many blocks");
+  if ((size_t)B * H > 65535)   // (b, h) pairs index the second grid dimension
+    return fail(SA2_EUNSUPPORTED, f + ": more than 65535 (batch, head) pairs");
+  return SA2_OK;
+}
+
+// The launches of a mask build; arguments already checked, ws large enough.
+static sa2_status launch_mask(const void* q, const void* k, int dtype, int B, int H, int N, int d,
+                              int bq, int bk, double k_frac, double p, const sa2_mask* m,
+                              void* ws, void* stream);
+
+// ---------------------------------------------------------------------------
+// Allocation-free variant: the workspace is a file-scope device array.  Each
+// GPU holds its own copy from module load until the process ends; host code
+// reaches it only through the address hipGetSymbolAddress returns for the
+// device (kept per device below), never through the array's name.  Every
+// call on one GPU uses the same array, so calls that overlap on one GPU
+// (e.g. on two streams) race.  Nothing in it needs to start at zero: every
+// byte a kernel reads was written earlier in the same call.
+// ---------------------------------------------------------------------------
+constexpr size_t kMaskScratchBytes = SA2_MASK_NOALLOC_MAX_BYTES;
+static __device__ __align__(256) unsigned char scratch[kMaskScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static void* g_scratch[kMaxDevices];
+static std::mutex g_scratch_mu;
+
+// The device address of `scratch` on `dev` (looked up once per device, with
+// that device current).
+static sa2_status scratch_on(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SA2_EUNSUPPORTED, "sa2_build_mask_noalloc: device ordinal out of range");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess)
+      return fail(SA2_EDEVICE, "sa2_build_mask_noalloc: hipGetDevice failed");
+    if (cur != dev && hipSetDevice(dev) != hipSuccess)
+      return fail(SA2_EDEVICE, "sa2_build_mask_noalloc: hipSetDevice failed");
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !ptr)
+      return fail(SA2_EDEVICE, std::string("sa2_build_mask_noalloc: hipGetSymbolAddress: ") +
+                                   hipGetErrorString(e));
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return SA2_OK;
+}
+
+}  // namespace sa2
+
+extern "C" sa2_status sa2_build_mask_noalloc(const void* q, const void* k, int dtype, int B,
+                                             int H, int N, int d, int bq, int bk, double k_frac,
+                                             double p, const sa2_mask* m, void* stream) {
+  if (sa2_status st = check_mask_args("sa2_build_mask_noalloc", q, k, dtype, B, H, N, d, bq, bk,
+                                      k_frac, p, m))
+    return st;
+  const size_t need = sa2_mask_workspace_bytes(B, H, N, d, bq, bk);
+  if (need > kMaskScratchBytes)
+    return fail(SA2_EUNSUPPORTED,
+                "sa2_build_mask_noalloc: this geometry needs " + std::to_string(need) +
+                    " bytes of workspace, more than the " + std::to_string(kMaskScratchBytes) +
+                    " of the static scratch array; use sa2_build_mask with a workspace");
+  int dev = -1;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const hipError_t e = s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess)
+    return fail(SA2_EDEVICE, "sa2_build_mask_noalloc: cannot tell the stream's device");
+  void* ws = nullptr;
+  if (sa2_status st = scratch_on(dev, &ws)) return st;
+  return launch_mask(q, k, dtype, B, H, N, d, bq, bk, k_frac, p, m, ws, stream);
+}
+
 extern "C" sa2_status sa2_build_mask(const void* q, const void* k, int dtype, int B, int H, int N,
                                      int d, int bq, int bk, double k_frac, double p,
                                      const sa2_mask* m, void* ws, size_t ws_bytes,
                                      void* stream) {
-  if (!q || !k || !m || !ws) return fail(SA2_EINVAL, "sa2_build_mask: null pointer");
-  if (B <= 0 || H <= 0 || N <= 0 || d <= 0 || bq <= 0 || bk <= 0)
-    return fail(SA2_EINVAL, "sa2_build_mask: B, H, N, d, bq, bk must be positive");
-  if (dtype != SA2_BF16 && dtype != SA2_F32)
-    return fail(SA2_EINVAL, "sa2_build_mask: unknown dtype");
-  if (d % 8 != 0 || d > 256)
-    return fail(SA2_EUNSUPPORTED, "sa2_build_mask: d must be a multiple of 8 and at most 256");
-  if (!aligned16(q) || !aligned16(k)) return fail(SA2_EINVAL, "sa2_build_mask: q/k not 16-byte aligned");
+  if (sa2_status st = check_mask_args("sa2_build_mask", q, k, dtype, B, H, N, d, bq, bk, k_frac,
+                                      p, m))
+    return st;
+  if (!ws) return fail(SA2_EINVAL, "sa2_build_mask: null pointer");
   if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
     return fail(SA2_EINVAL, "sa2_build_mask: workspace not 256-byte aligned");
-  if (std::isnan(k_frac) || std::isnan(p)) return fail(SA2_EINVAL, "sa2_build_mask: NaN k_frac or p");
-  if (k_frac <= 0.0 && p <= 0.0)
-    return fail(SA2_EINVAL, "sa2_build_mask: k_frac <= 0 and p <= 0 select nothing");
-  const int Tq = cdiv(N, bq), Tk = cdiv(N, bk);
-  if (m->B != B || m->H != H || m->N != N || m->bq != bq || m->bk != bk || m->Tq != Tq ||
-      m->Tk != Tk)
-    return fail(SA2_EINVAL, "sa2_build_mask: mask geometry does not match the call");
-  if (!m->bitmap || !m->row_cnt || !m->row_idx || !m->col_cnt || !m->col_idx)
-    return fail(SA2_EINVAL, "sa2_build_mask: mask array is null");
-  if (Tk > kMaxTk) return fail(SA2_EUNSUPPORTED, "sa2_build_mask: more than 4096 key blocks");
-  if (Tq > kMaxTk) return fail(SA2_EUNSUPPORTED, "sa2_build_mask: more than 4096 query blocks");
-  const size_t need = sa2_mask_workspace_bytes(B, H, N, d, bq, bk);
-  if (ws_bytes < need)
+  if (ws_bytes < sa2_mask_workspace_bytes(B, H, N, d, bq, bk))
     return fail(SA2_EINVAL, "sa2_build_mask: workspace smaller than sa2_mask_workspace_bytes()");
-  if ((size_t)B * H * Tq > 0x7fffffff || (size_t)B * H * (Tq + Tk) > 0x7fffffff)
-    return fail(SA2_EUNSUPPORTED, "sa2_build_mask: too many blocks");
-  if ((size_t)B * H > 65535)   // (b, h) pairs index the second grid dimension
-    return fail(SA2_EUNSUPPORTED, "sa2_build_mask: more than 65535 (batch, head) pairs");
+  return launch_mask(q, k, dtype, B, H, N, d, bq, bk, k_frac, p, m, ws, stream);
+}
 
+namespace sa2 {
+static sa2_status launch_mask(const void* q, const void* k, int dtype, int B, int H, int N, int d,
+                              int bq, int bk, double k_frac, double p, const sa2_mask* m,
+                              void* ws, void* stream) {
+  const int Tq = cdiv(N, bq), Tk = cdiv(N, bk);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int BH = B * H;
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -683,3 +775,4 @@ extern "C" sa2_status sa2_build_mask(const void* q, const void* k, int dtype, in
   }
   return SA2_OK;
 }
+}  // namespace sa2

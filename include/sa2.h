@@ -144,6 +144,28 @@ sa2_status sa2_build_mask(const void* q, const void* k, int dtype,
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * sa2_build_mask without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  It computes exactly what sa2_build_mask
+ * computes, with the same arguments apart from the workspace, and allocates
+ * nothing: its fp64 pooled blocks and score matrix live in a static device
+ * array of SA2_MASK_NOALLOC_MAX_BYTES bytes that each GPU the library runs
+ * on holds from module load until the process ends.  A geometry whose
+ * sa2_mask_workspace_bytes() exceeds that is refused with SA2_EUNSUPPORTED
+ * before anything is enqueued (the 1.3B-shaped layer needs 22 MB with
+ * 128 x 64 blocks and 38 MB with 64 x 64 blocks; the 14B-shaped one 296 MB).
+ * The kernels run on the device of `stream` (the current device if NULL).
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (e.g. on two streams without ordering between them) race.  Nothing in
+ * the array needs to start at zero.
+ */
+#define SA2_MASK_NOALLOC_MAX_BYTES ((size_t)64 << 20)
+sa2_status sa2_build_mask_noalloc(const void* q, const void* k, int dtype,
+                                  int B, int H, int N, int d, int bq, int bk,
+                                  double k_frac, double p, const sa2_mask* mask,
+                                  void* stream);
+
+/*
  * Block-sparse attention forward (gist.science, section 2C: tiles are kept or
  * dropped whole; dropped tiles cost neither the matmuls nor the softmax).
  *

@@ -133,6 +133,24 @@ def test_dq_refuses_a_mask_without_column_counts():
     assert st == _lib.SA2_EINVAL and "column counts" in msg, msg
 
 
+def test_noalloc_mask_refuses_a_geometry_beyond_the_scratch():
+    """The 14B-shaped layer needs 296 MB of mask workspace, more than the
+    static scratch array: refused before anything touches a device."""
+    L = _lib.lib()
+    B, H, N, d, bq, bk = 1, 40, 75600, 128, 128, 64
+    assert L.sa2_mask_workspace_bytes(B, H, N, d, bq, bk) > _lib.SA2_MASK_NOALLOC_MAX_BYTES
+    m = _lib.Sa2Mask(B, H, N, bq, bk, -(-N // bq), -(-N // bk), 1 << 20, 1 << 20, 1 << 20,
+                     1 << 20, 1 << 20, None, None)
+    st, msg = _status_and_msg(L.sa2_build_mask_noalloc(FAKE, FAKE, 0, B, H, N, d, bq, bk, 0.03,
+                                                       0.1, ctypes.byref(m), None))
+    assert st == _lib.SA2_EUNSUPPORTED and "static scratch" in msg, msg
+    # the 1.3B-shaped layer fits, in both block geometries; argument checks come first
+    assert L.sa2_mask_workspace_bytes(1, 12, 32760, 128, 64, 64) <= _lib.SA2_MASK_NOALLOC_MAX_BYTES
+    st, msg = _status_and_msg(L.sa2_build_mask_noalloc(FAKE, FAKE, 0, B, H, N, d, bq, bk, 0.0,
+                                                       0.0, ctypes.byref(m), None))
+    assert st == _lib.SA2_EINVAL and msg.startswith("sa2_build_mask_noalloc"), msg
+
+
 def test_python_binding_refuses_cpu_tensors():
     import torch
     import block_sparse_attention_sa2_amd as sa2
