@@ -86,8 +86,6 @@ def parse():
     ap.add_argument("--workload", default="c2", help="workload key (default: 1.3B layer fwd+bwd)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=12, help="heads the oracle times (default: the whole layer)")
-    ap.add_argument("--no-work-order", action="store_true",
-                    help="schedule the attention kernels in their fixed order")
     ap.add_argument("--sweep", choices=["variants", "sparsity"], default=None,
                     help="instead of the benchmark line: the mask-rule sweep (one JSON line "
                          "per regime, density and Top-k share) or the sparsity sweep of the "
@@ -155,18 +153,19 @@ def dense_baseline(sa2, q, k, v, do, w, sparse_attn_ms, args):
     import torch
     B, H, N, d = q.shape
     dev = q.device
-    mask = sa2.BlockMask(B, H, N, w.bq, w.bk, dev, work_order=True)
+    mask = sa2.BlockMask(B, H, N, w.bq, w.bk, dev)
     mws = torch.empty(sa2.mask_workspace_bytes(B, H, N, d, w.bq, w.bk), dtype=torch.uint8, device=dev)
     sa2.build_mask(q, k, w.bq, w.bk, 1.0, 0.0, mask=mask, workspace=mws)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     bws = torch.empty(sa2.bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
+    fws = torch.empty(max(1, sa2.fwd_workspace_bytes(B, H, N, d)), dtype=torch.uint8, device=dev)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     times = []
     for it in range(2 + 5):
         ev[0].record()
-        sa2.attn_fwd(q, k, v, mask, o=o, lse=lse)
+        sa2.attn_fwd(q, k, v, mask, o=o, lse=lse, workspace=fws)
         ev[1].record()
         sa2.attn_bwd_dq(q, k, v, o, lse, do, mask, bws, dq=dq)
         ev[2].record()
@@ -220,19 +219,20 @@ def second_geometry(sa2, W, q, k, v, do, name="c2_b64", warmup=3, steps=10):
     k_frac, p = W.tuned_params(name)
     B, H, N, d = q.shape
     dev = q.device
-    mask = sa2.BlockMask(B, H, N, w.bq, w.bk, dev, work_order=True)
+    mask = sa2.BlockMask(B, H, N, w.bq, w.bk, dev)
     mws = torch.empty(sa2.mask_workspace_bytes(B, H, N, d, w.bq, w.bk), dtype=torch.uint8, device=dev)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     bws = torch.empty(sa2.bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
+    fws = torch.empty(max(1, sa2.fwd_workspace_bytes(B, H, N, d)), dtype=torch.uint8, device=dev)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
     times = []
     for it in range(warmup + steps):
         ev[0].record()
         sa2.build_mask(q, k, w.bq, w.bk, k_frac, p, mask=mask, workspace=mws)
         ev[1].record()
-        sa2.attn_fwd(q, k, v, mask, o=o, lse=lse)
+        sa2.attn_fwd(q, k, v, mask, o=o, lse=lse, workspace=fws)
         ev[2].record()
         sa2.attn_bwd_dq(q, k, v, o, lse, do, mask, bws, dq=dq)
         ev[3].record()
@@ -301,15 +301,17 @@ def variant_sweep(args):
         q, k, v, do = (W.to_device_dtype(x[t], w.dtype).to(dev) for t in ("q", "k", "v", "do"))
         del x
         B, H, N, d = q.shape
-        mask = sa2.BlockMask(B, H, N, w.bq, w.bk, dev, work_order=True)
+        mask = sa2.BlockMask(B, H, N, w.bq, w.bk, dev)
         mws = torch.empty(sa2.mask_workspace_bytes(B, H, N, d, w.bq, w.bk), dtype=torch.uint8,
                           device=dev)
         bws = torch.empty(sa2.bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
+        fws = torch.empty(max(1, sa2.fwd_workspace_bytes(B, H, N, d)), dtype=torch.uint8,
+                          device=dev)
         o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
         lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
-        dense = sa2.BlockMask(B, H, N, w.bq, w.bk, dev, work_order=True)
+        dense = sa2.BlockMask(B, H, N, w.bq, w.bk, dev)
         sa2.build_mask(q, k, w.bq, w.bk, 1.0, 0.0, mask=dense, workspace=mws)
-        o_dense, _ = sa2.attn_fwd(q, k, v, dense)
+        o_dense, _ = sa2.attn_fwd(q, k, v, dense, workspace=fws)
         ref_norm = float(o_dense.float().norm())
         for D in W.C4_DENSITIES:
             for r in ratios:
@@ -326,7 +328,7 @@ def variant_sweep(args):
                     ev[0].record()
                     sa2.build_mask(q, k, w.bq, w.bk, k_frac, p, mask=mask, workspace=mws)
                     ev[1].record()
-                    sa2.attn_fwd(q, k, v, mask, o=o, lse=lse)
+                    sa2.attn_fwd(q, k, v, mask, o=o, lse=lse, workspace=fws)
                     ev[2].record()
                     sa2.attn_bwd_dq(q, k, v, o, lse, do, mask, bws, dq=dq)
                     ev[3].record()
@@ -380,10 +382,11 @@ def sparsity_sweep(args):
     q, k, v, do = (W.to_device_dtype(x[t], w.dtype).to(dev) for t in ("q", "k", "v", "do"))
     del x
     B, H, N, d = q.shape
-    mask = sa2.BlockMask(B, H, N, w.bq, w.bk, dev, work_order=True)
+    mask = sa2.BlockMask(B, H, N, w.bq, w.bk, dev)
     mws = torch.empty(sa2.mask_workspace_bytes(B, H, N, d, w.bq, w.bk), dtype=torch.uint8,
                       device=dev)
     bws = torch.empty(sa2.bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
+    fws = torch.empty(max(1, sa2.fwd_workspace_bytes(B, H, N, d)), dtype=torch.uint8, device=dev)
     o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
     dense_attn = None
@@ -394,7 +397,7 @@ def sparsity_sweep(args):
             ev[0].record()
             sa2.build_mask(q, k, w.bq, w.bk, D, 0.0, mask=mask, workspace=mws)
             ev[1].record()
-            sa2.attn_fwd(q, k, v, mask, o=o, lse=lse)
+            sa2.attn_fwd(q, k, v, mask, o=o, lse=lse, workspace=fws)
             ev[2].record()
             sa2.attn_bwd_dq(q, k, v, o, lse, do, mask, bws, dq=dq)
             ev[3].record()
@@ -460,12 +463,13 @@ def main():
     B, H, N, d = q.shape
 
     # everything the step touches is allocated once, outside the timed region
-    mask = sa2.BlockMask(B, H, N, w.bq, w.bk, dev, work_order=not args.no_work_order)
+    mask = sa2.BlockMask(B, H, N, w.bq, w.bk, dev)
     mws = torch.empty(sa2.mask_workspace_bytes(B, H, N, d, w.bq, w.bk), dtype=torch.uint8, device=dev)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     bws = torch.empty(sa2.bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
+    fws = torch.empty(max(1, sa2.fwd_workspace_bytes(B, H, N, d)), dtype=torch.uint8, device=dev)
     backward = w.backward and do is not None
     stages = ["mask", "fwd"] + (["bwd_dq", "bwd_dkdv"] if backward else [])
 
@@ -476,7 +480,7 @@ def main():
         mark(0)
         sa2.build_mask(q, k, w.bq, w.bk, k_frac, p, mask=mask, workspace=mws)
         mark(1)
-        sa2.attn_fwd(q, k, v, mask, o=o, lse=lse)
+        sa2.attn_fwd(q, k, v, mask, o=o, lse=lse, workspace=fws)
         mark(2)
         if backward:
             sa2.attn_bwd_dq(q, k, v, o, lse, do, mask, bws, dq=dq)

@@ -88,15 +88,17 @@ def _ptr(t: torch.Tensor) -> ctypes.c_void_p:
 
 
 class BlockMask:
-    """The hybrid block mask of every (batch, head): bitmap plus row and column lists.
+    """The hybrid block mask of every (batch, head): bitmap, row and column
+    lists, and the attention kernels' work plans made from the list counts.
 
     Arrays (device, caller-owned through this object):
       bitmap  uint8 [B, H, Tq, Tk]
       row_cnt int32 [B, H, Tq];  row_idx int32 [B, H, Tq, Tk] (first row_cnt valid)
       col_cnt int32 [B, H, Tk];  col_idx int32 [B, H, Tk, Tq] (first col_cnt valid)
+      row_plan, col_plan  int32 (sa2_mask_plan_bytes / 4 entries each)
     """
 
-    def __init__(self, B: int, H: int, N: int, bq: int, bk: int, device, work_order: bool = True):
+    def __init__(self, B: int, H: int, N: int, bq: int, bk: int, device):
         self.B, self.H, self.N, self.bq, self.bk = B, H, N, bq, bk
         self.Tq = -(-N // bq)
         self.Tk = -(-N // bk)
@@ -107,15 +109,14 @@ class BlockMask:
         self.row_idx = torch.empty((B, H, self.Tq, self.Tk), **i32)
         self.col_cnt = torch.empty((B, H, self.Tk), **i32)
         self.col_idx = torch.empty((B, H, self.Tk, self.Tq), **i32)
-        # optional work orders (longest lists first); None: fixed XCD-aware order
-        self.row_order = torch.empty((B * H * self.Tq,), **i32) if work_order else None
-        self.col_order = torch.empty((B * H * self.Tk,), **i32) if work_order else None
+        L = _lib.lib()
+        self.row_plan = torch.empty((L.sa2_mask_plan_bytes(B, H, N, bq, bk, 0) // 4,), **i32)
+        self.col_plan = torch.empty((L.sa2_mask_plan_bytes(B, H, N, bq, bk, 1) // 4,), **i32)
         self._c = Sa2Mask(B, H, N, bq, bk, self.Tq, self.Tk,
                           self.bitmap.data_ptr(), self.row_cnt.data_ptr(),
                           self.row_idx.data_ptr(), self.col_cnt.data_ptr(),
-                          self.col_idx.data_ptr(),
-                          self.row_order.data_ptr() if work_order else None,
-                          self.col_order.data_ptr() if work_order else None)
+                          self.col_idx.data_ptr(), self.row_plan.data_ptr(),
+                          self.col_plan.data_ptr())
 
     @property
     def device(self):
@@ -123,6 +124,12 @@ class BlockMask:
 
     def c_struct(self) -> Sa2Mask:
         return self._c
+
+    def remake_plans(self) -> None:
+        """Remake the work plans from the list counts (sa2_mask_plans), after
+        the caller wrote the lists itself."""
+        check("sa2_mask_plans", _lib.lib().sa2_mask_plans(ctypes.byref(self._c),
+                                                          _stream(self.device)))
 
     def density(self) -> float:
         """Kept block pairs over all block pairs (sparsity = 1 - density)."""
@@ -142,15 +149,14 @@ def mask_workspace_bytes(B, H, N, d, bq, bk) -> int:
 
 
 def build_mask(q: torch.Tensor, k: torch.Tensor, bq: int, bk: int, k_frac: float, p: float,
-               mask: BlockMask | None = None, workspace: torch.Tensor | None = None,
-               work_order: bool = True) -> BlockMask:
+               mask: BlockMask | None = None, workspace: torch.Tensor | None = None) -> BlockMask:
     """Hybrid Top-k + Top-p block mask of q, k (sa2_build_mask)."""
     dt = _dtype_code(q, k)
     B, H, N, d = _shape(q)
     if _shape(k) != (B, H, N, d):
         raise ValueError("q and k must have the same shape")
     if mask is None:
-        mask = BlockMask(B, H, N, bq, bk, q.device, work_order=work_order)
+        mask = BlockMask(B, H, N, bq, bk, q.device)
     _same_device(mask, q.device)
     workspace = _workspace(workspace, mask_workspace_bytes(B, H, N, d, bq, bk), q.device)
     L = _lib.lib()
@@ -178,7 +184,11 @@ def build_mask_noalloc(q: torch.Tensor, k: torch.Tensor, bq: int, bk: int, k_fra
     return mask
 
 
-def attn_fwd(q, k, v, mask: BlockMask, o=None, lse=None):
+def fwd_workspace_bytes(B, H, N, d) -> int:
+    return int(_lib.lib().sa2_fwd_workspace_bytes(B, H, N, d))
+
+
+def attn_fwd(q, k, v, mask: BlockMask, o=None, lse=None, workspace=None):
     """Block-sparse attention forward (sa2_attn_fwd) -> (o, lse)."""
     dt = _dtype_code(q, k, v)
     B, H, N, d = _shape(q)
@@ -188,9 +198,10 @@ def attn_fwd(q, k, v, mask: BlockMask, o=None, lse=None):
     o = torch.empty_like(q) if o is None else _out(o, q.shape, q.dtype, q.device, "o")
     lse = (torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else
            _out(lse, (B, H, N), torch.float32, q.device, "lse"))
+    workspace = _workspace(workspace, fwd_workspace_bytes(B, H, N, d), q.device)
     st = _lib.lib().sa2_attn_fwd(_ptr(q), _ptr(k), _ptr(v), dt, B, H, N, d,
                                  ctypes.byref(mask.c_struct()), _ptr(o), _ptr(lse),
-                                 _stream(q.device))
+                                 _ptr(workspace), workspace.numel(), _stream(q.device))
     check("sa2_attn_fwd", st)
     return o, lse
 

@@ -20,7 +20,7 @@ class Sa2Mask(ctypes.Structure):
         ("Tk", ctypes.c_int32),
         ("bitmap", ctypes.c_void_p), ("row_cnt", ctypes.c_void_p), ("row_idx", ctypes.c_void_p),
         ("col_cnt", ctypes.c_void_p), ("col_idx", ctypes.c_void_p),
-        ("row_order", ctypes.c_void_p), ("col_order", ctypes.c_void_p),
+        ("row_plan", ctypes.c_void_p), ("col_plan", ctypes.c_void_p),
     ]
 
 
@@ -34,9 +34,12 @@ SIGNATURES = {
     "sa2_version": ([], ctypes.c_char_p),
     "sa2_last_error": ([], ctypes.c_char_p),
     "sa2_mask_workspace_bytes": ([_I, _I, _I, _I, _I, _I], _Z),
+    "sa2_mask_plan_bytes": ([_I, _I, _I, _I, _I, _I], _Z),
+    "sa2_mask_plans": ([_MP, _P], _I),
     "sa2_build_mask": ([_P, _P, _I, _I, _I, _I, _I, _I, _I, _D, _D, _MP, _P, _Z, _P], _I),
     "sa2_build_mask_noalloc": ([_P, _P, _I, _I, _I, _I, _I, _I, _I, _D, _D, _MP, _P], _I),
-    "sa2_attn_fwd": ([_P, _P, _P, _I, _I, _I, _I, _I, _MP, _P, _P, _P], _I),
+    "sa2_fwd_workspace_bytes": ([_I, _I, _I, _I], _Z),
+    "sa2_attn_fwd": ([_P, _P, _P, _I, _I, _I, _I, _I, _MP, _P, _P, _P, _Z, _P], _I),
     "sa2_bwd_workspace_bytes": ([_I, _I, _I, _I], _Z),
     "sa2_attn_bwd": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _MP, _P, _P, _P, _P, _Z, _P], _I),
     "sa2_attn_bwd_dq": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _MP, _P, _P, _Z, _P], _I),

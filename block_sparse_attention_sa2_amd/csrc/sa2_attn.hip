@@ -32,6 +32,7 @@
 #include <math.h>
 
 #include "sa2_common.h"
+#include "sa2_plan.h"
 
 namespace sa2 {
 
@@ -106,10 +107,6 @@ __device__ inline bf16x8 tr_operand(const uint16_t* lds, int kbase, int nbase, i
   const bf16x4 hi = lds_read_tr(lds + Tile<D, L>::off(r + 8, c));
   return cat(lo, hi);
 }
-
-// A list length read from a mask, clamped to [0, cap]: a malformed mask
-// then gives wrong values but no access past the lists and no unbounded loop.
-__device__ inline int list_len(int n, int cap) { return min(max(n, 0), cap); }
 
 // Rows of the running max only move when the tile maximum exceeds them by
 // more than this (log2 units): P then stays below 2^8, and the rescale of the
@@ -315,195 +312,6 @@ void fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
 }
 
 // ---------------------------------------------------------------------------
-// dK/dV work plan.  A key block's column list is walked by one workgroup, so
-// a long list (an attention sink is kept by every query block) would set the
-// kernel's time by itself.  The plan cuts every list longer than L into
-// nearly equal segments; a segment's workgroup writes fp32 partial dK, dV to
-// a slot of the workspace and counts itself done on the block's completion
-// counter; the workgroup that finds itself last adds the block's partials in
-// segment order and writes dK, dV.  Values are never accumulated atomically
-// and the order of the sum is fixed, so results are reproducible bit for bit;
-// no workgroup waits for another.
-//
-// L is the larger of kMinSegment and twice the mean load of the kernel's
-// resident workgroups (kDkdvSlots), so that only lists that would set the
-// kernel's time are cut (each cut costs a partial write, a device-scope
-// release and the final sum), and per XCD share at least
-// total / kShareExtra, which bounds a share's extra segments by kShareExtra
-// and its partial slots by 2 kShareExtra.
-//
-// Items, in the workspace as int4 {block, first list entry, entries, -1 or
-// split entry * 1024 + segment}; item j of XCD x sits at 8j + x (the
-// workgroup slots that run on XCD x), longest first; unused items have block
-// -1.  Each XCD takes a contiguous share of the blocks, so its L2 sees a
-// narrow band of heads; the shares are cut at equal cost rather than equal
-// count (densities differ from head to head, and the XCD with the most work
-// would set the kernel's time).  Split entries: int4 {block, first
-// partial slot, segments}, kShareExtra per XCD share, with one completion
-// counter each, which the plan zeroes.
-// ---------------------------------------------------------------------------
-constexpr int kDkdvSlots = 1024;     // 256 CUs x 4 resident dK/dV workgroups
-constexpr int kMinSegment = 8;
-constexpr int kFairShares = 2;       // lists up to this many mean loads stay whole
-constexpr int kShareExtra = 128;     // extra segments (and split blocks) per XCD share
-constexpr int kPlanBuckets = 4096;   // list lengths are ranked by min(length, 4095)
-constexpr int kPlanWorkgroups = 8;   // one per XCD share
-constexpr size_t kPartialFloats = 2 * 64 * 128;   // dV and dK of one key block
-
-// Shares are balanced by cost (see balanced_share): a share's boundaries move
-// at most share_slack(n) items from the equal-count ones.
-__host__ __device__ inline int share_slack(int n) { return ((n + 7) / 8 + 15) / 16; }
-__host__ __device__ inline int plan_items_per_xcd(int ncols) {
-  return (ncols + 7) / 8 + 2 * share_slack(ncols) + kShareExtra;
-}
-
-// XCD share x of n items: [b(x), b(x + 1)), where b(x) is the first item whose
-// predecessors cost at least x / 8 of the total (an item costs its list length
-// plus one), clamped to within share_slack(n) of the equal-count boundary
-// x n / 8.  Every workgroup computes the same boundaries.  pre: blockDim.x
-// entries of LDS.
-__device__ int2 balanced_share(int x, const int32_t* __restrict__ cnt, int n, int cap,
-                               long long* pre, int* bnd) {
-  const int tid = threadIdx.x, nt = blockDim.x;
-  const int per = (n + nt - 1) / nt;
-  const int lo = min(n, tid * per), hi = min(n, lo + per);
-  long long s = 0;
-  for (int i = lo; i < hi; ++i) s += list_len(cnt[i], cap) + 1;
-  pre[tid] = s;
-  if (tid < 2) bnd[tid] = 0;
-  __syncthreads();
-  for (int off = 1; off < nt; off <<= 1) {
-    const long long add = tid >= off ? pre[tid - off] : 0;
-    __syncthreads();
-    pre[tid] += add;
-    __syncthreads();
-  }
-  const long long total = pre[nt - 1], run = pre[tid] - s;
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const long long target = ((long long)(x + k) * total + 7) / 8;
-    if (target > 0 && run < target && target <= run + s) {
-      long long acc = run;
-      int b = hi;
-      for (int i = lo; i < hi; ++i) {
-        if (acc >= target) { b = i; break; }
-        acc += list_len(cnt[i], cap) + 1;
-      }
-      bnd[k] = b;
-    }
-  }
-  __syncthreads();
-  const int H = share_slack(n);
-  int b[2];
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int e = (int)((long long)(x + k) * n / 8);
-    b[k] = min(max(bnd[k], max(0, e - H)), min(n, e + H));
-  }
-  __syncthreads();
-  return make_int2(b[0], b[1] - b[0]);
-}
-
-// The plan of XCD share x, by one workgroup of nt threads (a multiple of 64).
-// LDS: hist[kPlanBuckets] ints, scan[nt] ints, red[nt] 64-bit sums,
-// ctr[2] ints.
-__device__ void dkdv_plan_share(int x, const int32_t* __restrict__ col_cnt, int ncols, int Tq,
-                                int4* __restrict__ items, int4* __restrict__ splits,
-                                int* __restrict__ done, int* hist, int* scan, long long* red,
-                                int* ctr) {
-  const int tid = threadIdx.x, nt = blockDim.x, nw = nt / 64;
-  const int2 sh = balanced_share(x, col_cnt, ncols, Tq, red, ctr);
-  const int c0 = sh.x, len = sh.y;
-
-  // totals over all blocks and over this share
-  long long all = 0, mine = 0;
-  for (int c = tid; c < ncols; c += nt) {
-    const int n = list_len(col_cnt[c], Tq);
-    all += n;
-    if (c >= c0 && c < c0 + len) mine += n;
-  }
-  for (int off = 32; off > 0; off >>= 1) {
-    all += __shfl_xor(all, off);
-    mine += __shfl_xor(mine, off);
-  }
-  if ((tid & 63) == 0) red[tid >> 6] = all;
-  __syncthreads();
-  long long total = 0;
-  for (int w = 0; w < nw; ++w) total += red[w];
-  __syncthreads();
-  if ((tid & 63) == 0) red[tid >> 6] = mine;
-  for (int c = tid; c < kPlanBuckets; c += nt) hist[c] = 0;
-  if (tid == 0) ctr[0] = ctr[1] = 0;
-  __syncthreads();
-  long long share = 0;
-  for (int w = 0; w < nw; ++w) share += red[w];
-  const long long Lg =
-      max((long long)kMinSegment, kFairShares * ((total + kDkdvSlots - 1) / kDkdvSlots));
-  const int L = (int)max(Lg, (share + kShareExtra - 1) / kShareExtra);
-  auto nseg = [&](int n) { return n > L ? (n + L - 1) / L : 1; };
-  auto seg = [&](int n, int ns, int s, int& start) {
-    const int base = n / ns, rem = n % ns;
-    start = s * base + min(s, rem);
-    return base + (s < rem ? 1 : 0);
-  };
-  auto bucket = [](int ln) { return min(ln, kPlanBuckets - 1); };
-
-  // histogram of segment lengths, then first position of each bucket in
-  // descending order (as in the mask's work orders)
-  for (int j = tid; j < len; j += nt) {
-    const int n = list_len(col_cnt[c0 + j], Tq), ns = nseg(n);
-    for (int s2 = 0; s2 < ns; ++s2) {
-      int st;
-      atomicAdd(&hist[bucket(seg(n, ns, s2, st))], 1);
-    }
-  }
-  __syncthreads();
-  const int per = kPlanBuckets / nt;   // nt divides kPlanBuckets
-  const int lo = tid * per, hi = lo + per;
-  int local = 0;
-  for (int r = lo; r < hi; ++r) local += hist[kPlanBuckets - 1 - r];
-  scan[tid] = local;
-  __syncthreads();
-  for (int off = 1; off < nt; off <<= 1) {
-    const int add = tid >= off ? scan[tid - off] : 0;
-    __syncthreads();
-    scan[tid] += add;
-    __syncthreads();
-  }
-  const int nitems = scan[nt - 1];
-  int run = scan[tid] - local;
-  for (int r = lo; r < hi; ++r) {
-    const int c = kPlanBuckets - 1 - r;
-    const int h = hist[c];
-    hist[c] = run;
-    run += h;
-  }
-  __syncthreads();
-  for (int j = tid; j < len; j += nt) {
-    const int col = c0 + j, n = list_len(col_cnt[col], Tq), ns = nseg(n);
-    int entry = -1;
-    if (ns > 1) {
-      const int p0 = 2 * kShareExtra * x + atomicAdd(&ctr[1], ns);
-      entry = kShareExtra * x + atomicAdd(&ctr[0], 1);
-      splits[entry] = make_int4(col, p0, ns, 0);
-    }
-    for (int s2 = 0; s2 < ns; ++s2) {
-      int st;
-      const int ln = seg(n, ns, s2, st);
-      items[8 * atomicAdd(&hist[bucket(ln)], 1) + x] =
-          make_int4(col, st, ln, ns > 1 ? entry * 1024 + s2 : -1);
-    }
-  }
-  __syncthreads();
-  const int J = plan_items_per_xcd(ncols);
-  for (int j = nitems + tid; j < J; j += nt) items[8 * j + x] = make_int4(-1, 0, 0, -1);
-  for (int j = ctr[0] + tid; j < kShareExtra; j += nt)
-    splits[kShareExtra * x + j] = make_int4(-1, 0, 0, 0);
-  for (int j = tid; j < kShareExtra; j += nt) done[kShareExtra * x + j] = 0;
-}
-
-
-// ---------------------------------------------------------------------------
 // Asynchronous tile copies (bf16, d = 128), global -> LDS through buffer
 // resources.  Rows of 256 bytes are copied in groups of four: lane l's 16
 // bytes of group i land in LDS unit 64i + l, i.e. row 4i + l/16 and unit
@@ -576,22 +384,36 @@ __device__ inline void wait_vm_lgkm0() {
 // (see double_buffered).  The LDS operands of each MFMA group are read well
 // ahead of their MFMAs (sched_group_barrier fixes the issue order), so that
 // LDS latency overlaps the matrix work instead of stalling it.
+//
+// One workgroup per item of the row plan: a query block's row list, or one
+// segment of a long one.  A segment leaves its unnormalised fp32 O^T rows,
+// running maximum m and row sum l in a partial slot; the last segment of the
+// row combines the slots in segment order:
+//   M = max_s m_s,  l = sum_s l_s 2^(m_s - M),  O = sum_s O_s 2^(m_s - M) / l,
+//   LSE = (M + log2 l) ln 2,
+// which is the softmax over the whole row (each segment's m and O_s, l_s are
+// consistent under the lazy rescale, whatever m it settled on).
 template <int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4 ? 2 : 1, 2)))
 void fwd_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
-                      const bf16_t* __restrict__ v, const int32_t* __restrict__ row_cnt,
-                      const int32_t* __restrict__ row_idx, const int32_t* __restrict__ order,
-                      int N, int Tq, int Tk, float scale_log2, bf16_t* __restrict__ o,
+                      const bf16_t* __restrict__ v, const int32_t* __restrict__ row_idx,
+                      const int4* __restrict__ items, const int4* __restrict__ splits,
+                      int* __restrict__ done, float* __restrict__ partials, int nrows, int N,
+                      int Tq, int Tk, float scale_log2, bf16_t* __restrict__ o,
                       float* __restrict__ lse) {
   constexpr int D = 128;
   constexpr int NK = D / 16, ND = D / 32;
   constexpr int TILE = 64 * D;
   constexpr int KCOPIES = 16 / NW;   // copy instructions per wave per tile tensor
+  constexpr int BQ = NW * 32;
   __shared__ __attribute__((aligned(16))) uint16_t kb0[TILE], kb1[TILE];
   __shared__ __attribute__((aligned(16))) uint16_t vb0[TILE], vb1[TILE];
+  __shared__ int last_segment;
 
-  const int wg = order ? order[blockIdx.x] : xcd_remap(blockIdx.x, gridDim.x);
-  if ((unsigned)wg >= gridDim.x) return;   // a malformed work order
+  const int4 item = items[blockIdx.x];
+  int4 sp;
+  if (!plan_item_ok(item, nrows, Tk, kRowPlan, splits, sp)) return;
+  const int wg = item.x;
   const int bh = wg / Tq, qi = wg % Tq;
   const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
   const int h = lane >> 5, l32 = lane & 31;
@@ -614,9 +436,9 @@ void fwd_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
   for (int db = 0; db < ND; ++db) acc[db] = zero16();
   float m = -INFINITY, lsum = 0.f;
 
-  // the list is walked with scalar loads, one entry ahead of its copy
-  const int cnt = list_len(row_cnt[wg], Tk);
-  const int32_t* lst = row_idx + (size_t)wg * Tk;
+  // the list (segment) is walked with scalar loads, one entry ahead of its copy
+  const int cnt = item.z;
+  const int32_t* lst = row_idx + (size_t)wg * Tk + item.y;
   auto key_at = [&](int t) { return t < cnt ? lst[t] * 64 : 0; };
   int key_cur = key_at(0);
   if (cnt > 0) copy_kv_tile<NW>(rk, rv, key_cur, kb0, vb0, w, uo);
@@ -709,52 +531,105 @@ void fwd_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
   });
 
   const float ltot = wave_sum32(lsum);
-  const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-  if (qvalid) {
-    bf16_t* orow = o + base + (size_t)qrow * D;
+  if (item.w < 0) {
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    if (qvalid) {
+      bf16_t* orow = o + base + (size_t)qrow * D;
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          store4(orow + 32 * db + 8 * g + 4 * h, acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv,
+                 acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv);
+      if (h == 0)
+        lse[(size_t)bh * N + qrow] = ltot > 0.f ? (m + __log2f(ltot)) * kLn2 : -INFINITY;
+    }
+    return;
+  }
+  // one segment of a split row: O^T rows, m and l into its partial slot
+  // ([BQ rows][D] unnormalised O, then m[BQ], l[BQ])
+  const int entry = item.w >> 10, seg = item.w & 1023;
+  {
+    const int r = w * 32 + l32;
+    float* part = partials + (size_t)(sp.y + seg) * kFwdPartialFloats;
 #pragma unroll
     for (int db = 0; db < ND; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g)
-        store4(orow + 32 * db + 8 * g + 4 * h, acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv,
-               acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv);
-    if (h == 0)
-      lse[(size_t)bh * N + qrow] = ltot > 0.f ? (m + __log2f(ltot)) * kLn2 : -INFINITY;
+        store4(part + (size_t)r * D + 32 * db + 8 * g + 4 * h, acc[db][4 * g],
+               acc[db][4 * g + 1], acc[db][4 * g + 2], acc[db][4 * g + 3]);
+    part[(size_t)BQ * D + (h == 0 ? r : BQ + r)] = h == 0 ? m : ltot;
   }
+  // release the partial, count this segment done; the last one combines
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) last_segment = atomicAdd(&done[entry], 1) == sp.z - 1;
+  __syncthreads();
+  if (!last_segment) return;
+  __threadfence();
+  // two threads per row, each half of its D columns
+  const int r = tid >> 1, c0 = (tid & 1) * (D / 2);
+  const float* part0 = partials + (size_t)sp.y * kFwdPartialFloats;
+  float M = -INFINITY;
+  for (int s2 = 0; s2 < sp.z; ++s2)
+    M = fmaxf(M, part0[(size_t)s2 * kFwdPartialFloats + (size_t)BQ * D + r]);
+  float osum[D / 2];
+#pragma unroll
+  for (int c = 0; c < D / 2; ++c) osum[c] = 0.f;
+  float lt = 0.f;
+  if (M > -INFINITY) {
+    for (int s2 = 0; s2 < sp.z; ++s2) {
+      const float* ps = part0 + (size_t)s2 * kFwdPartialFloats;
+      const float wgt = __builtin_amdgcn_exp2f(ps[(size_t)BQ * D + r] - M);
+      lt += ps[(size_t)BQ * D + BQ + r] * wgt;
+#pragma unroll
+      for (int c = 0; c < D / 2; c += 4) {
+        const f32x4 x4 = *reinterpret_cast<const f32x4*>(ps + (size_t)r * D + c0 + c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) osum[c + i] += x4[i] * wgt;
+      }
+    }
+  }
+  const int row = qi * BQ + r;
+  if (row < N) {
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    bf16_t* orow = o + base + (size_t)row * D + c0;
+#pragma unroll
+    for (int c = 0; c < D / 2; c += 4)
+      store4(orow + c, osum[c] * inv, osum[c + 1] * inv, osum[c + 2] * inv, osum[c + 3] * inv);
+    if ((tid & 1) == 0)
+      lse[(size_t)bh * N + row] = lt > 0.f ? (M + __log2f(lt)) * kLn2 : -INFINITY;
+  }
+  if (tid == 0) done[entry] = 0;   // ready for the next call
 }
 
-// dQ for bf16 and d = 128 with the same K and V rings as the forward.
+// dQ for bf16 and d = 128 with the same K and V rings as the forward, one
+// workgroup per item of the row plan.  A segment of a split row leaves its
+// fp32 dQ^T rows in a partial slot; the last segment adds the slots in
+// segment order.  Every segment forms Delta and the LSE of its rows; the
+// first (or the whole row) leaves them in the workspace for dK/dV.
 template <int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4 ? 2 : 1, 2)))
 void dq_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                      const bf16_t* __restrict__ v, const bf16_t* __restrict__ o,
                      const bf16_t* __restrict__ dout, const float* __restrict__ lse,
-                     float* __restrict__ stats, const int32_t* __restrict__ row_cnt,
-                     const int32_t* __restrict__ row_idx,
-                     const int32_t* __restrict__ order, int N, int Tq, int Tk, float scale_log2,
-                     float scale, bf16_t* __restrict__ dq, const int32_t* __restrict__ col_cnt,
-                     int ncols, int4* __restrict__ plan_items, int4* __restrict__ plan_splits,
-                     int* __restrict__ plan_done) {
+                     float* __restrict__ stats, const int32_t* __restrict__ row_idx,
+                     const int4* __restrict__ items, const int4* __restrict__ splits,
+                     int* __restrict__ done, float* __restrict__ partials, int nrows, int N,
+                     int Tq, int Tk, float scale_log2, float scale, bf16_t* __restrict__ dq) {
   constexpr int D = 128;
   constexpr int NK = D / 16, ND = D / 32;
   constexpr int TILE = 64 * D;
   constexpr int KCOPIES = 16 / NW;   // copy instructions per wave per tile tensor
+  constexpr int BQ = NW * 32;
   __shared__ __attribute__((aligned(16))) uint16_t kb0[TILE], kb1[TILE];
   __shared__ __attribute__((aligned(16))) uint16_t vb0[TILE], vb1[TILE];
-  static_assert(TILE * 2 == kPlanBuckets * 4, "the plan's histogram fills one tile buffer");
+  __shared__ int last_segment;
 
-  // The first workgroups write the dK/dV plan of one XCD share each (it
-  // depends on the column counts only), in the tile buffers' LDS.
-  if (blockIdx.x < kPlanWorkgroups) {
-    dkdv_plan_share(blockIdx.x, col_cnt, ncols, Tq, plan_items, plan_splits, plan_done,
-                    reinterpret_cast<int*>(kb0), reinterpret_cast<int*>(kb1),
-                    reinterpret_cast<long long*>(vb1), reinterpret_cast<int*>(vb0));
-    return;
-  }
-  const int slot = blockIdx.x - kPlanWorkgroups;
-  const int nslots = gridDim.x - kPlanWorkgroups;
-  const int wg = order ? order[slot] : xcd_remap(slot, nslots);
-  if ((unsigned)wg >= (unsigned)nslots) return;   // a malformed work order
+  const int4 item = items[blockIdx.x];
+  int4 sp;
+  if (!plan_item_ok(item, nrows, Tk, kRowPlan, splits, sp)) return;
+  const int wg = item.x;
   const int bh = wg / Tq, qi = wg % Tq;
   const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
   const int h = lane >> 5, l32 = lane & 31;
@@ -768,8 +643,8 @@ void dq_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   const bool qvalid = qrow < N;
 
   // the first tiles' copies go out before the row loads below
-  const int cnt = list_len(row_cnt[wg], Tk);
-  const int32_t* lst = row_idx + (size_t)wg * Tk;
+  const int cnt = item.z;
+  const int32_t* lst = row_idx + (size_t)wg * Tk + item.y;
   auto key_at = [&](int t) { return t < cnt ? lst[t] * 64 : 0; };
   int key_t = key_at(0), key_t1 = key_at(1);
   if (cnt > 0) {
@@ -791,7 +666,8 @@ void dq_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   // (zeros) included, are kept for the dK/dV kernel.
   const float dl = wave_sum32(dpart);
   const float l2 = qvalid ? lse[(size_t)bh * N + qrow] * kLog2e : 0.f;
-  stats[stat_lse2(bh, stat_groups(N), qrow) + 32 * h] = h ? dl : l2;
+  if (item.w < 0 || (item.w & 1023) == 0)
+    stats[stat_lse2(bh, stat_groups(N), qrow) + 32 * h] = h ? dl : l2;
 
   f32x16 acc[ND];
 #pragma unroll
@@ -842,15 +718,61 @@ void dq_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     }
   });
 
-  if (qvalid) {
-    bf16_t* row = dq + base + (size_t)qrow * D;
+  if (item.w < 0) {
+    if (qvalid) {
+      bf16_t* row = dq + base + (size_t)qrow * D;
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          store4(row + 32 * db + 8 * g + 4 * h, acc[db][4 * g] * scale,
+                 acc[db][4 * g + 1] * scale, acc[db][4 * g + 2] * scale,
+                 acc[db][4 * g + 3] * scale);
+    }
+    return;
+  }
+  // one segment of a split row: fp32 dQ^T rows into its partial slot
+  const int entry = item.w >> 10, seg = item.w & 1023;
+  {
+    const int r = w * 32 + l32;
+    float* part = partials + (size_t)(sp.y + seg) * kDqPartialFloats + (size_t)r * D;
 #pragma unroll
     for (int db = 0; db < ND; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g)
-        store4(row + 32 * db + 8 * g + 4 * h, acc[db][4 * g] * scale, acc[db][4 * g + 1] * scale,
-               acc[db][4 * g + 2] * scale, acc[db][4 * g + 3] * scale);
+        store4(part + 32 * db + 8 * g + 4 * h, acc[db][4 * g], acc[db][4 * g + 1],
+               acc[db][4 * g + 2], acc[db][4 * g + 3]);
   }
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) last_segment = atomicAdd(&done[entry], 1) == sp.z - 1;
+  __syncthreads();
+  if (!last_segment) return;
+  __threadfence();
+  // two threads per row, each half of its D columns, segments in order
+  const int r = tid >> 1, c0 = (tid & 1) * (D / 2);
+  const float* part0 = partials + (size_t)sp.y * kDqPartialFloats + (size_t)r * D + c0;
+  float gsum[D / 2];
+#pragma unroll
+  for (int c = 0; c < D / 2; ++c) gsum[c] = 0.f;
+  for (int s2 = 0; s2 < sp.z; ++s2) {
+    const float* ps = part0 + (size_t)s2 * kDqPartialFloats;
+#pragma unroll
+    for (int c = 0; c < D / 2; c += 4) {
+      const f32x4 x4 = *reinterpret_cast<const f32x4*>(ps + c);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) gsum[c + i] += x4[i];
+    }
+  }
+  const int row = qi * BQ + r;
+  if (row < N) {
+    bf16_t* grow = dq + base + (size_t)row * D + c0;
+#pragma unroll
+    for (int c = 0; c < D / 2; c += 4)
+      store4(grow + c, gsum[c] * scale, gsum[c + 1] * scale, gsum[c + 2] * scale,
+             gsum[c + 3] * scale);
+  }
+  if (tid == 0) done[entry] = 0;   // ready for the next call
 }
 
 // ---------------------------------------------------------------------------
@@ -1086,16 +1008,8 @@ void dkdv_pair_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
   // an entry that does not fit this call (a plan written for another mask,
   // or never written) is skipped, so nothing is read or written out of range
   const int4 item = items[blockIdx.x];
-  if (item.x < 0 || item.x >= ncols || item.y < 0 || item.z < 0 || item.y + item.z > Tq) return;
-  int4 sp = make_int4(0, 0, 0, 0);   // {block, first partial slot, segments}
-  if (item.w >= 0) {
-    const int entry = item.w >> 10, seg = item.w & 1023;
-    if (entry >= 8 * kShareExtra) return;
-    sp = splits[entry];
-    if (sp.x != item.x || sp.y < 0 || sp.z < 2 || seg >= sp.z ||
-        sp.y + sp.z > 16 * kShareExtra)
-      return;
-  }
+  int4 sp;   // {block, first partial slot, segments}
+  if (!plan_item_ok(item, ncols, Tq, kColPlan, splits, sp)) return;
   const int wg = item.x;
   const int bh = wg / Tk, kj = wg % Tk;
   const int key0 = kj * 64;
@@ -1428,29 +1342,53 @@ static sa2_status check_common(const char* fn, int dtype, int B, int H, int N, i
   return SA2_OK;
 }
 
+// A plan's pointers: from the mask's plan array (items, split entries, the
+// completion counters of one kernel) and the partial slots of a workspace.
+struct PlanPtrs {
+  const int4 *items, *splits;
+  int* done;
+  float* partials;
+};
+static PlanPtrs plan_ptrs(int32_t* plan, int n, PlanKind kd, int ndone, int which,
+                          float* partials) {
+  const PlanLayout l = plan_layout(n, kd, ndone);
+  char* b = reinterpret_cast<char*>(plan);
+  return PlanPtrs{reinterpret_cast<const int4*>(b + l.items),
+                  reinterpret_cast<const int4*>(b + l.splits),
+                  reinterpret_cast<int*>(b + l.done) + (size_t)8 * kd.extra * which, partials};
+}
+static size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+// Partial slots of a plan kind: 2 `extra` per XCD share.
+static size_t partial_bytes(PlanKind kd, size_t floats) {
+  return (size_t)8 * 2 * kd.extra * floats * sizeof(float);
+}
+
 template <typename T, int D, int NW>
 static void launch_fwd(const void* q, const void* k, const void* v, const sa2_mask* m, int BH,
                        int N, float sl2, void* o, float* lse, hipStream_t s) {
   fwd_kernel<T, D, NW><<<BH * m->Tq, NW * 64, 0, s>>>(
       static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), m->row_cnt,
-      m->row_idx, m->row_order, N, m->Tq, m->Tk, sl2, static_cast<T*>(o), lse);
+      m->row_idx, nullptr, N, m->Tq, m->Tk, sl2, static_cast<T*>(o), lse);
 }
 
 template <int NW>
 static void launch_fwd_async(const void* q, const void* k, const void* v, const sa2_mask* m,
-                             int BH, int N, float sl2, void* o, float* lse, hipStream_t s) {
-  fwd_async_kernel<NW><<<BH * m->Tq, NW * 64, 0, s>>>(
+                             int BH, int N, float sl2, void* o, float* lse, const PlanPtrs& rp,
+                             hipStream_t s) {
+  const int nrows = BH * m->Tq;
+  fwd_async_kernel<NW><<<8 * plan_items_per_xcd(nrows, kRowPlan), NW * 64, 0, s>>>(
       static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
-      static_cast<const bf16_t*>(v), m->row_cnt, m->row_idx, m->row_order, N, m->Tq, m->Tk, sl2,
-      static_cast<bf16_t*>(o), lse);
+      static_cast<const bf16_t*>(v), m->row_idx, rp.items, rp.splits, rp.done, rp.partials,
+      nrows, N, m->Tq, m->Tk, sl2, static_cast<bf16_t*>(o), lse);
 }
 
 template <typename T, int D>
 static void dispatch_fwd(const void* q, const void* k, const void* v, const sa2_mask* m, int BH,
-                         int N, float sl2, void* o, float* lse, hipStream_t s) {
+                         int N, float sl2, void* o, float* lse, const PlanPtrs& rp,
+                         hipStream_t s) {
   if constexpr (D == 128 && sizeof(T) == 2) {
-    if (m->bq == 128) launch_fwd_async<4>(q, k, v, m, BH, N, sl2, o, lse, s);
-    else launch_fwd_async<2>(q, k, v, m, BH, N, sl2, o, lse, s);
+    if (m->bq == 128) launch_fwd_async<4>(q, k, v, m, BH, N, sl2, o, lse, rp, s);
+    else launch_fwd_async<2>(q, k, v, m, BH, N, sl2, o, lse, rp, s);
     return;
   }
   if (m->bq == 128) launch_fwd<T, D, 4>(q, k, v, m, BH, N, sl2, o, lse, s);
@@ -1465,9 +1403,7 @@ struct BwdArgs {
   float sl2, scale;
   void *dq, *dk, *dv;
   float* stats;
-  int4 *items, *splits;   // dK/dV plan (bf16, d = 128)
-  int* done;
-  float* partials;
+  PlanPtrs rows, cols;   // dQ and dK/dV plans (bf16, d = 128)
   hipStream_t s;
 };
 
@@ -1475,13 +1411,14 @@ template <typename T, int D>
 static void launch_dq(const BwdArgs& a) {
   const sa2_mask* m = a.m;
   if constexpr (D == 128 && sizeof(T) == 2) {
+    const int nrows = a.BH * m->Tq;
 #define SA2_DQ_ASYNC_ARGS                                                                     \
   static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k),                            \
       static_cast<const bf16_t*>(a.v), static_cast<const bf16_t*>(a.o),                        \
-      static_cast<const bf16_t*>(a.dout), a.lse, a.stats, m->row_cnt, m->row_idx,               \
-      m->row_order, a.N, m->Tq, m->Tk, a.sl2, a.scale, static_cast<bf16_t*>(a.dq), m->col_cnt, \
-      a.BH * m->Tk, a.items, a.splits, a.done
-    const int grid = kPlanWorkgroups + a.BH * m->Tq;
+      static_cast<const bf16_t*>(a.dout), a.lse, a.stats, m->row_idx, a.rows.items,            \
+      a.rows.splits, a.rows.done, a.rows.partials, nrows, a.N, m->Tq, m->Tk, a.sl2, a.scale,   \
+      static_cast<bf16_t*>(a.dq)
+    const int grid = 8 * plan_items_per_xcd(nrows, kRowPlan);
     if (m->bq == 128) dq_async_kernel<4><<<grid, 256, 0, a.s>>>(SA2_DQ_ASYNC_ARGS);
     else dq_async_kernel<2><<<grid, 128, 0, a.s>>>(SA2_DQ_ASYNC_ARGS);
 #undef SA2_DQ_ASYNC_ARGS
@@ -1491,7 +1428,7 @@ static void launch_dq(const BwdArgs& a) {
   static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),          \
       static_cast<const T*>(a.o), static_cast<const T*>(a.dout), a.lse, a.stats,              \
       m->row_cnt,                                                                             \
-      m->row_idx, m->row_order, a.N, m->Tq, m->Tk, a.sl2, a.scale, static_cast<T*>(a.dq)
+      m->row_idx, nullptr, a.N, m->Tq, m->Tk, a.sl2, a.scale, static_cast<T*>(a.dq)
   if (m->bq == 128) dq_kernel<T, D, 4><<<a.BH * m->Tq, 256, 0, a.s>>>(SA2_DQ_ARGS);
   else dq_kernel<T, D, 2><<<a.BH * m->Tq, 128, 0, a.s>>>(SA2_DQ_ARGS);
 #undef SA2_DQ_ARGS
@@ -1504,10 +1441,11 @@ static void launch_dkdv(const BwdArgs& a) {
     const int ncols = a.BH * m->Tk;
 #define SA2_DKDV_PAIR_ARGS                                                                  \
   static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k),                            \
-      static_cast<const bf16_t*>(a.v), static_cast<const bf16_t*>(a.dout), a.stats, a.items,   \
-      m->col_idx, a.N, m->Tq, m->Tk, a.sl2, a.scale, static_cast<bf16_t*>(a.dk),               \
-      static_cast<bf16_t*>(a.dv), a.splits, a.done, a.partials, ncols
-    const int grid = 8 * plan_items_per_xcd(ncols);
+      static_cast<const bf16_t*>(a.v), static_cast<const bf16_t*>(a.dout), a.stats,             \
+      a.cols.items, m->col_idx, a.N, m->Tq, m->Tk, a.sl2, a.scale,                             \
+      static_cast<bf16_t*>(a.dk), static_cast<bf16_t*>(a.dv), a.cols.splits, a.cols.done,      \
+      a.cols.partials, ncols
+    const int grid = 8 * plan_items_per_xcd(ncols, kColPlan);
     if (m->bq == 128) dkdv_pair_kernel<128><<<grid, 128, 0, a.s>>>(SA2_DKDV_PAIR_ARGS);
     else dkdv_pair_kernel<64><<<grid, 128, 0, a.s>>>(SA2_DKDV_PAIR_ARGS);
 #undef SA2_DKDV_PAIR_ARGS
@@ -1515,7 +1453,7 @@ static void launch_dkdv(const BwdArgs& a) {
   }
 #define SA2_DKDV_ARGS                                                                         \
   static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),          \
-      static_cast<const T*>(a.dout), a.stats, m->col_cnt, m->col_idx, m->col_order, a.N,      \
+      static_cast<const T*>(a.dout), a.stats, m->col_cnt, m->col_idx, nullptr, a.N,          \
       m->Tq, m->Tk, a.sl2, a.scale, static_cast<T*>(a.dk), static_cast<T*>(a.dv)
   if (m->bq == 128) dkdv_kernel<T, D, 128><<<a.BH * m->Tk, 256, 0, a.s>>>(SA2_DKDV_ARGS);
   else dkdv_kernel<T, D, 64><<<a.BH * m->Tk, 256, 0, a.s>>>(SA2_DKDV_ARGS);
@@ -1535,26 +1473,20 @@ static void by_type(int dtype, int d, const BwdArgs& a) {
 }
 
 // Workspace regions of the backward, each 256-byte aligned: the row
-// statistics; for d = 128 also the dK/dV plan (items, split blocks) and the
-// partial-sum slots of split key blocks.
+// statistics; for d = 128 also the partial slots of split dQ rows and of
+// split dK/dV columns.
 struct BwdWorkspace {
-  size_t stats, items, splits, done, partials, total;
+  size_t stats, dq_partials, dkdv_partials, total;
 };
 static BwdWorkspace bwd_workspace(int B, int H, int N, int d) {
-  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   BwdWorkspace w{};
   w.stats = 0;
-  size_t off = up((size_t)B * H * stat_groups(N) * 256);
+  size_t off = up256((size_t)B * H * stat_groups(N) * 256);
   if (d == 128) {
-    const int ncols = (int)std::min<size_t>((size_t)B * H * cdiv(N, 64), 0x7fffffff);
-    w.items = off;
-    off = up(off + (size_t)8 * plan_items_per_xcd(ncols) * sizeof(int4));
-    w.splits = off;
-    off = up(off + (size_t)8 * kShareExtra * sizeof(int4));
-    w.done = off;
-    off = up(off + (size_t)8 * kShareExtra * sizeof(int));
-    w.partials = off;
-    off = up(off + (size_t)8 * 2 * kShareExtra * kPartialFloats * sizeof(float));
+    w.dq_partials = off;
+    off = up256(off + partial_bytes(kRowPlan, kDqPartialFloats));
+    w.dkdv_partials = off;
+    off = up256(off + partial_bytes(kColPlan, kPartialFloats));
   }
   w.total = off;
   return w;
@@ -1581,36 +1513,58 @@ static BwdArgs bwd_args(const void* q, const void* k, const void* v, const void*
   const double sc = 1.0 / sqrt((double)d);
   const BwdWorkspace w = bwd_workspace(B, H, N, d);
   char* base = static_cast<char*>(ws);
-  return BwdArgs{q, k, v, o, dout, lse, m, B * H, N, (float)(1.4426950408889634 * sc),
-                 (float)sc, dq, dk, dv, reinterpret_cast<float*>(base + w.stats),
-                 d == 128 ? reinterpret_cast<int4*>(base + w.items) : nullptr,
-                 d == 128 ? reinterpret_cast<int4*>(base + w.splits) : nullptr,
-                 d == 128 ? reinterpret_cast<int*>(base + w.done) : nullptr,
-                 d == 128 ? reinterpret_cast<float*>(base + w.partials) : nullptr,
-                 reinterpret_cast<hipStream_t>(stream)};
+  BwdArgs a{q, k, v, o, dout, lse, m, B * H, N, (float)(1.4426950408889634 * sc), (float)sc,
+            dq, dk, dv, reinterpret_cast<float*>(base + w.stats), PlanPtrs{}, PlanPtrs{},
+            reinterpret_cast<hipStream_t>(stream)};
+  if (d == 128) {
+    a.rows = plan_ptrs(m->row_plan, B * H * m->Tq, kRowPlan, kRowCounters, 1,
+                       reinterpret_cast<float*>(base + w.dq_partials));
+    a.cols = plan_ptrs(m->col_plan, B * H * m->Tk, kColPlan, kColCounters, 0,
+                       reinterpret_cast<float*>(base + w.dkdv_partials));
+  }
+  return a;
 }
 
 }  // namespace sa2
 
 using namespace sa2;
 
+extern "C" size_t sa2_fwd_workspace_bytes(int B, int H, int N, int d) {
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return 0;
+  return d == 128 ? up256(partial_bytes(kRowPlan, kFwdPartialFloats)) : 0;
+}
+
 extern "C" sa2_status sa2_attn_fwd(const void* q, const void* k, const void* v, int dtype, int B,
                                    int H, int N, int d, const sa2_mask* m, void* o, float* lse,
-                                   void* stream) {
+                                   void* ws, size_t ws_bytes, void* stream) {
   if (!q || !k || !v || !o || !lse) return fail(SA2_EINVAL, "sa2_attn_fwd: null pointer");
   if (sa2_status st = check_common("sa2_attn_fwd", dtype, B, H, N, d, m)) return st;
   if (!m->row_cnt || !m->row_idx) return fail(SA2_EINVAL, "sa2_attn_fwd: mask row lists are null");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return fail(SA2_EINVAL, "sa2_attn_fwd: pointers must be 16-byte aligned");
+  const size_t need = sa2_fwd_workspace_bytes(B, H, N, d);
+  if (need > 0) {
+    if (!ws) return fail(SA2_EINVAL, "sa2_attn_fwd: null workspace");
+    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+      return fail(SA2_EINVAL, "sa2_attn_fwd: workspace not 256-byte aligned");
+    if (ws_bytes < need)
+      return fail(SA2_EINVAL, "sa2_attn_fwd: workspace smaller than sa2_fwd_workspace_bytes()");
+  }
+  const bool planned = dtype == SA2_BF16 && d == 128;
+  if (planned && (!m->row_plan || !aligned16(m->row_plan)))
+    return fail(SA2_EINVAL, "sa2_attn_fwd: mask row plan is null or misaligned (bf16, d = 128)");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int BH = B * H;
   const float sl2 = (float)(1.4426950408889634 / sqrt((double)d));
+  const PlanPtrs rp = planned ? plan_ptrs(m->row_plan, BH * m->Tq, kRowPlan, kRowCounters, 0,
+                                          static_cast<float*>(ws))
+                              : PlanPtrs{};
   if (dtype == SA2_BF16) {
-    if (d == 128) dispatch_fwd<bf16_t, 128>(q, k, v, m, BH, N, sl2, o, lse, s);
-    else dispatch_fwd<bf16_t, 64>(q, k, v, m, BH, N, sl2, o, lse, s);
+    if (d == 128) dispatch_fwd<bf16_t, 128>(q, k, v, m, BH, N, sl2, o, lse, rp, s);
+    else dispatch_fwd<bf16_t, 64>(q, k, v, m, BH, N, sl2, o, lse, rp, s);
   } else {
-    if (d == 128) dispatch_fwd<float, 128>(q, k, v, m, BH, N, sl2, o, lse, s);
-    else dispatch_fwd<float, 64>(q, k, v, m, BH, N, sl2, o, lse, s);
+    if (d == 128) dispatch_fwd<float, 128>(q, k, v, m, BH, N, sl2, o, lse, rp, s);
+    else dispatch_fwd<float, 64>(q, k, v, m, BH, N, sl2, o, lse, rp, s);
   }
   return check_launch("fwd_kernel");
 }
@@ -1632,8 +1586,8 @@ extern "C" sa2_status sa2_attn_bwd_dq(const void* q, const void* k, const void* 
   if (!aligned16(o) || !aligned16(dq))
     return fail(SA2_EINVAL, "sa2_attn_bwd_dq: pointers must be 16-byte aligned");
   if (!m->row_cnt || !m->row_idx) return fail(SA2_EINVAL, "sa2_attn_bwd_dq: mask row lists are null");
-  if (dtype == SA2_BF16 && d == 128 && !m->col_cnt)   // the dK/dV plan reads the column counts
-    return fail(SA2_EINVAL, "sa2_attn_bwd_dq: mask column counts are null (bf16, d = 128)");
+  if (dtype == SA2_BF16 && d == 128 && (!m->row_plan || !aligned16(m->row_plan)))
+    return fail(SA2_EINVAL, "sa2_attn_bwd_dq: mask row plan is null or misaligned (bf16, d = 128)");
   by_type<DqLaunch>(dtype, d, bwd_args(q, k, v, o, lse, dout, B, H, N, d, m, dq, nullptr, nullptr, ws, stream));
   return check_launch("dq_kernel");
 }
@@ -1649,6 +1603,9 @@ extern "C" sa2_status sa2_attn_bwd_dkdv(const void* q, const void* k, const void
   if (!aligned16(dk) || !aligned16(dv))
     return fail(SA2_EINVAL, "sa2_attn_bwd_dkdv: pointers must be 16-byte aligned");
   if (!m->col_cnt || !m->col_idx) return fail(SA2_EINVAL, "sa2_attn_bwd_dkdv: mask column lists are null");
+  if (dtype == SA2_BF16 && d == 128 && (!m->col_plan || !aligned16(m->col_plan)))
+    return fail(SA2_EINVAL,
+                "sa2_attn_bwd_dkdv: mask column plan is null or misaligned (bf16, d = 128)");
   by_type<DkdvLaunch>(dtype, d, bwd_args(q, k, v, nullptr, lse, dout, B, H, N, d, m, nullptr, dk, dv, ws, stream));
   return check_launch("dkdv_kernel");
 }

@@ -8,7 +8,7 @@
 //   select     one wave per query-block row: softmax, rank, cut, emit the
 //              bitmap row, row count and ascending row list
 //   columns    transposed lists (query blocks per key block), ascending
-//   order      optional work orders (longest lists first)
+//   plan       the work plans of the attention kernels (sa2_plan.h)
 // fp64 throughout keeps the ranking and the Top-p cut equal to an exact
 // evaluation except where two scores, or the mass and p, agree to ~1e-15.
 #include <math.h>
@@ -17,6 +17,7 @@
 #include <string>
 
 #include "sa2_common.h"
+#include "sa2_plan.h"
 
 namespace sa2 {
 
@@ -520,53 +521,27 @@ void columns_kernel(const uint8_t* __restrict__ bitmap, int Tq, int Tk,
 // among equal counts is whatever the LDS atomics give (it affects scheduling
 // only).
 // ---------------------------------------------------------------------------
-constexpr int kOrderThreads = 1024;
+// The mask's work plans (see sa2_plan.h), one workgroup per XCD share and
+// kind of list: workgroups 0..7 the row plan, 8..15 the column plan.
+constexpr int kPlanThreads = 1024;
 
-__global__ __launch_bounds__(kOrderThreads)
-void order_kernel(const int32_t* __restrict__ row_cnt, int nrows, int row_max,
-                  const int32_t* __restrict__ col_cnt, int ncols, int col_max,
-                  int32_t* __restrict__ row_order, int32_t* __restrict__ col_order) {
-  __shared__ int hist[kMaxTk + 1];
-  __shared__ int scan[kOrderThreads];
-  const int which = blockIdx.x / 8, x = blockIdx.x % 8;
-  const int32_t* cnt = which == 0 ? row_cnt : col_cnt;
-  int32_t* order = which == 0 ? row_order : col_order;
-  const int n = which == 0 ? nrows : ncols;
-  const int nb = (which == 0 ? row_max : col_max) + 1;   // counts 0 .. max
-  // this XCD's share of the natural order (as in xcd_remap)
-  const int qn = n / 8, rn = n % 8;
-  const int c0 = x * qn + min(x, rn), len = qn + (x < rn ? 1 : 0);
-  const int tid = threadIdx.x;
-  for (int c = tid; c < nb; c += kOrderThreads) hist[c] = 0;
-  __syncthreads();
-  for (int j = tid; j < len; j += kOrderThreads) atomicAdd(&hist[cnt[c0 + j]], 1);
-  __syncthreads();
-  // first position of each count in descending-count order
-  const int per = (nb + kOrderThreads - 1) / kOrderThreads;
-  const int lo = tid * per, hi = min(nb, lo + per);   // positions in descending order
-  int local = 0;
-  for (int r = lo; r < hi; ++r) local += hist[nb - 1 - r];
-  scan[tid] = local;
-  __syncthreads();
-  for (int off = 1; off < kOrderThreads; off <<= 1) {
-    const int add = tid >= off ? scan[tid - off] : 0;
-    __syncthreads();
-    scan[tid] += add;
-    __syncthreads();
-  }
-  int run = scan[tid] - local;
-  for (int r = lo; r < hi; ++r) {
-    const int c = nb - 1 - r;
-    const int h = hist[c];
-    hist[c] = run;
-    run += h;
-  }
-  __syncthreads();
-  // rank j within the share goes to slot 8j + x (slots i with i % 8 == x)
-  for (int j = tid; j < len; j += kOrderThreads) {
-    const int id = c0 + j;
-    order[8 * atomicAdd(&hist[cnt[id]], 1) + x] = id;
-  }
+__global__ __launch_bounds__(kPlanThreads)
+void plan_kernel(const int32_t* __restrict__ row_cnt, int nrows, int Tk,
+                 int32_t* __restrict__ row_plan, const int32_t* __restrict__ col_cnt, int ncols,
+                 int Tq, int32_t* __restrict__ col_plan) {
+  __shared__ int hist[kPlanBuckets];
+  __shared__ int scan[kPlanThreads];
+  __shared__ long long red[kPlanThreads];
+  __shared__ int ctr[2];
+  const int x = blockIdx.x % 8;
+  const bool rows = blockIdx.x < 8;
+  const PlanKind kd = rows ? kRowPlan : kColPlan;
+  const int n = rows ? nrows : ncols, ndone = rows ? kRowCounters : kColCounters;
+  const PlanLayout l = plan_layout(n, kd, ndone);
+  char* b = reinterpret_cast<char*>(rows ? row_plan : col_plan);
+  plan_share(x, rows ? row_cnt : col_cnt, n, rows ? Tk : Tq, kd,
+             reinterpret_cast<int4*>(b + l.items), reinterpret_cast<int4*>(b + l.splits),
+             reinterpret_cast<int*>(b + l.done), ndone, hist, scan, red, ctr);
 }
 
 static int next_pow2(int x) {
@@ -615,8 +590,11 @@ static sa2_status check_mask_args(const char* fn, const void* q, const void* k, 
   if (m->B != B || m->H != H || m->N != N || m->bq != bq || m->bk != bk || m->Tq != Tq ||
       m->Tk != Tk)
     return fail(SA2_EINVAL, f + ": mask geometry does not match the call");
-  if (!m->bitmap || !m->row_cnt || !m->row_idx || !m->col_cnt || !m->col_idx)
+  if (!m->bitmap || !m->row_cnt || !m->row_idx || !m->col_cnt || !m->col_idx || !m->row_plan ||
+      !m->col_plan)
     return fail(SA2_EINVAL, f + ": mask array is null");
+  if (!aligned16(m->row_plan) || !aligned16(m->col_plan))
+    return fail(SA2_EINVAL, f + ": mask plans must be 16-byte aligned");
   if (Tk > kMaxTk) return fail(SA2_EUNSUPPORTED, f + ": more than 4096 key blocks");
   if (Tq > kMaxTk) return fail(SA2_EUNSUPPORTED, f + ": more than 4096 query blocks");
   if ((size_t)B * H * Tq > 0x7fffffff || (size_t)B * H * (Tq + Tk) > 0x7fffffff)
@@ -695,6 +673,32 @@ extern "C" sa2_status sa2_build_mask_noalloc(const void* q, const void* k, int d
   return launch_mask(q, k, dtype, B, H, N, d, bq, bk, k_frac, p, m, ws, stream);
 }
 
+extern "C" size_t sa2_mask_plan_bytes(int B, int H, int N, int bq, int bk, int columns) {
+  if (B <= 0 || H <= 0 || N <= 0 || bq <= 0 || bk <= 0 || (columns != 0 && columns != 1))
+    return 0;
+  const size_t n = (size_t)B * H * cdiv(N, columns ? bk : bq);
+  if (n > 0x7fffffff) return 0;
+  return columns ? plan_layout((int)n, kColPlan, kColCounters).bytes
+                 : plan_layout((int)n, kRowPlan, kRowCounters).bytes;
+}
+
+extern "C" sa2_status sa2_mask_plans(const sa2_mask* m, void* stream) {
+  if (!m) return fail(SA2_EINVAL, "sa2_mask_plans: null mask");
+  if (m->B <= 0 || m->H <= 0 || m->N <= 0 || m->bq <= 0 || m->bk <= 0 ||
+      m->Tq != cdiv(m->N, m->bq) || m->Tk != cdiv(m->N, m->bk))
+    return fail(SA2_EINVAL, "sa2_mask_plans: inconsistent mask geometry");
+  if ((size_t)m->B * m->H * (m->Tq + m->Tk) > 0x7fffffff)
+    return fail(SA2_EUNSUPPORTED, "sa2_mask_plans: too many blocks");
+  if (!m->row_cnt || !m->col_cnt || !m->row_plan || !m->col_plan)
+    return fail(SA2_EINVAL, "sa2_mask_plans: mask array is null");
+  if (!aligned16(m->row_plan) || !aligned16(m->col_plan))
+    return fail(SA2_EINVAL, "sa2_mask_plans: mask plans must be 16-byte aligned");
+  const int BH = m->B * m->H;
+  plan_kernel<<<16, kPlanThreads, 0, reinterpret_cast<hipStream_t>(stream)>>>(
+      m->row_cnt, BH * m->Tq, m->Tk, m->row_plan, m->col_cnt, BH * m->Tk, m->Tq, m->col_plan);
+  return check_launch("plan_kernel");
+}
+
 extern "C" sa2_status sa2_build_mask(const void* q, const void* k, int dtype, int B, int H, int N,
                                      int d, int bq, int bk, double k_frac, double p,
                                      const sa2_mask* m, void* ws, size_t ws_bytes,
@@ -725,7 +729,6 @@ static sa2_status launch_mask(const void* q, const void* k, int dtype, int B, in
   w += up((size_t)BH * Tk * d * 8);
   double* sbar = reinterpret_cast<double*>(w);
   w += up((size_t)BH * Tq * Tk * 8);
-  const bool orders = m->row_order != nullptr && m->col_order != nullptr;
 
   const int nblk = BH * (Tq + Tk);
   if (dtype == SA2_BF16)
@@ -768,11 +771,8 @@ static sa2_status launch_mask(const void* q, const void* k, int dtype, int B, in
   columns_kernel<<<dim3(cdiv(Tk, kColsPerGroup), BH), 256, 0, s>>>(m->bitmap, Tq, Tk,
                                                                     m->col_cnt, m->col_idx);
   if (sa2_status st = check_launch("columns_kernel")) return st;
-  if (orders) {
-    order_kernel<<<16, kOrderThreads, 0, s>>>(m->row_cnt, BH * Tq, Tk, m->col_cnt, BH * Tk, Tq,
-                                             m->row_order, m->col_order);
-    if (sa2_status st = check_launch("order_kernel")) return st;
-  }
-  return SA2_OK;
+  plan_kernel<<<16, kPlanThreads, 0, s>>>(m->row_cnt, BH * Tq, Tk, m->row_plan, m->col_cnt,
+                                          BH * Tk, Tq, m->col_plan);
+  return check_launch("plan_kernel");
 }
 }  // namespace sa2

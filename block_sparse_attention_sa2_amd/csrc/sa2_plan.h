@@ -1,0 +1,251 @@
+// Work plans of the attention kernels (gfx950 / CDNA4).  Shared by the mask
+// builder, which writes a mask's plans once, and the attention kernels,
+// which walk them.
+#pragma once
+
+#include "sa2_common.h"
+
+namespace sa2 {
+
+// A list length read from a mask, clamped to [0, cap]: a malformed mask
+// then gives wrong values but no access past the lists and no unbounded loop.
+__device__ inline int list_len(int n, int cap) { return min(max(n, 0), cap); }
+
+// ---------------------------------------------------------------------------
+// Work plans.  One workgroup walks one list (a query block's row list in the
+// forward and dQ kernels, a key block's column list in the dK/dV kernel), so
+// a long list would set a kernel's time by itself: an attention sink is kept
+// by every query block, and under Top-p a few rows of a skewed head keep most
+// key blocks (gist.science section 1).  A plan cuts every list longer than L
+// into nearly equal segments; a segment's workgroup writes fp32 partial sums
+// to a slot of the workspace and counts itself done on the list's completion
+// counter; the workgroup that finds itself last combines the list's partials
+// in segment order and writes the outputs.  Values are never accumulated
+// atomically and the order of every sum is fixed, so results are
+// reproducible bit for bit; no workgroup waits for another.
+//
+// L is the larger of kMinSegment and `fair` times the mean load of the
+// kernel's resident workgroups (`slots`), so that only lists that would set
+// the kernel's time are cut (each cut costs a partial write, a device-scope
+// release and the final combine), and per XCD share at least total / `extra`,
+// which bounds a share's extra segments by `extra` and its partial slots by
+// 2 `extra`.
+//
+// Items, in the mask's plan array as int4 {list, first list entry, entries, -1 or
+// split entry * 1024 + segment}; item j of XCD x sits at 8j + x (the
+// workgroup slots that run on XCD x), longest first; unused items have list
+// -1.  Each XCD takes a contiguous share of the lists, so its L2 sees a
+// narrow band of heads.  Column shares are cut at equal cost rather than
+// equal count (densities differ from head to head, and the XCD with the most
+// dK/dV work would set the kernel's time); row shares keep equal counts (the
+// cost-balanced cut measured 1% slower for the forward and dQ).  Split
+// entries: int4 {list, first partial slot, segments}, `extra` per XCD share,
+// with one completion counter each, which the plan zeroes.
+// ---------------------------------------------------------------------------
+struct PlanKind {
+  int slots;      // resident workgroups of the kernel that walks the lists
+  int fair;       // lists up to this many mean loads stay whole
+  int extra;      // extra segments (and split lists) per XCD share
+  bool balanced;  // XCD shares cut at equal cost (else at equal count)
+};
+constexpr PlanKind kColPlan{1024, 2, 128, true};   // dK/dV: 256 CUs x 4 workgroups
+constexpr PlanKind kRowPlan{512, 1, 64, false};    // forward, dQ: 256 CUs x 2
+constexpr int kMinSegment = 8;
+constexpr int kPlanBuckets = 4096;   // list lengths are ranked by min(length, 4095)
+constexpr size_t kPartialFloats = 2 * 64 * 128;           // dV and dK of one key block
+constexpr size_t kFwdPartialFloats = 128 * 128 + 2 * 128;  // O of a query block, m, l
+constexpr size_t kDqPartialFloats = 128 * 128;             // dQ of a query block
+
+// Cost-balanced shares move a boundary at most share_slack(n) items from the
+// equal-count one.
+__host__ __device__ inline int share_slack(int n) { return ((n + 7) / 8 + 15) / 16; }
+__host__ __device__ inline int plan_items_per_xcd(int n, PlanKind k) {
+  return (n + 7) / 8 + (k.balanced ? 2 * share_slack(n) : 0) + k.extra;
+}
+
+// XCD share x of n items: [b(x), b(x + 1)), where b(x) is the first item whose
+// predecessors cost at least x / 8 of the total (an item costs its list length
+// plus one), clamped to within share_slack(n) of the equal-count boundary
+// x n / 8.  Every workgroup computes the same boundaries.  pre: blockDim.x
+// entries of LDS.
+static __device__ int2 balanced_share(int x, const int32_t* __restrict__ cnt, int n, int cap,
+                               long long* pre, int* bnd) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int per = (n + nt - 1) / nt;
+  const int lo = min(n, tid * per), hi = min(n, lo + per);
+  long long s = 0;
+  for (int i = lo; i < hi; ++i) s += list_len(cnt[i], cap) + 1;
+  pre[tid] = s;
+  if (tid < 2) bnd[tid] = 0;
+  __syncthreads();
+  for (int off = 1; off < nt; off <<= 1) {
+    const long long add = tid >= off ? pre[tid - off] : 0;
+    __syncthreads();
+    pre[tid] += add;
+    __syncthreads();
+  }
+  const long long total = pre[nt - 1], run = pre[tid] - s;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const long long target = ((long long)(x + k) * total + 7) / 8;
+    if (target > 0 && run < target && target <= run + s) {
+      long long acc = run;
+      int b = hi;
+      for (int i = lo; i < hi; ++i) {
+        if (acc >= target) { b = i; break; }
+        acc += list_len(cnt[i], cap) + 1;
+      }
+      bnd[k] = b;
+    }
+  }
+  __syncthreads();
+  const int H = share_slack(n);
+  int b[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int e = (int)((long long)(x + k) * n / 8);
+    b[k] = min(max(bnd[k], max(0, e - H)), min(n, e + H));
+  }
+  __syncthreads();
+  return make_int2(b[0], b[1] - b[0]);
+}
+
+// The plan of XCD share x of n lists (lengths cnt, each at most cap), by one
+// workgroup of nt threads (a multiple of 64 that divides kPlanBuckets).
+// LDS: hist[kPlanBuckets] ints, scan[nt] ints, red[nt] 64-bit sums, ctr[2].
+static __device__ void plan_share(int x, const int32_t* __restrict__ cnt, int n, int cap, PlanKind kd,
+                           int4* __restrict__ items, int4* __restrict__ splits,
+                           int* __restrict__ done, int ndone, int* hist, int* scan,
+                           long long* red, int* ctr) {
+  const int tid = threadIdx.x, nt = blockDim.x, nw = nt / 64;
+  int2 sh;
+  if (kd.balanced) {
+    sh = balanced_share(x, cnt, n, cap, red, ctr);
+  } else {
+    const int q = n / 8, r = n % 8;
+    sh = make_int2(x * q + min(x, r), q + (x < r ? 1 : 0));
+  }
+  const int c0 = sh.x, len = sh.y;
+
+  // totals over all lists and over this share
+  long long all = 0, mine = 0;
+  for (int c = tid; c < n; c += nt) {
+    const int ln = list_len(cnt[c], cap);
+    all += ln;
+    if (c >= c0 && c < c0 + len) mine += ln;
+  }
+  for (int off = 32; off > 0; off >>= 1) {
+    all += __shfl_xor(all, off);
+    mine += __shfl_xor(mine, off);
+  }
+  if ((tid & 63) == 0) red[tid >> 6] = all;
+  __syncthreads();
+  long long total = 0;
+  for (int w = 0; w < nw; ++w) total += red[w];
+  __syncthreads();
+  if ((tid & 63) == 0) red[tid >> 6] = mine;
+  for (int c = tid; c < kPlanBuckets; c += nt) hist[c] = 0;
+  if (tid == 0) ctr[0] = ctr[1] = 0;
+  __syncthreads();
+  long long share = 0;
+  for (int w = 0; w < nw; ++w) share += red[w];
+  const long long Lg =
+      max((long long)kMinSegment, kd.fair * ((total + kd.slots - 1) / kd.slots));
+  const int L = (int)max(Lg, (share + kd.extra - 1) / kd.extra);
+  auto nseg = [&](int ln) { return ln > L ? (ln + L - 1) / L : 1; };
+  auto seg = [&](int ln, int ns, int s, int& start) {
+    const int base = ln / ns, rem = ln % ns;
+    start = s * base + min(s, rem);
+    return base + (s < rem ? 1 : 0);
+  };
+  auto bucket = [](int ln) { return min(ln, kPlanBuckets - 1); };
+
+  // histogram of segment lengths, then first position of each bucket in
+  // descending order (as in the mask's work orders)
+  for (int j = tid; j < len; j += nt) {
+    const int ln = list_len(cnt[c0 + j], cap), ns = nseg(ln);
+    for (int s2 = 0; s2 < ns; ++s2) {
+      int st;
+      atomicAdd(&hist[bucket(seg(ln, ns, s2, st))], 1);
+    }
+  }
+  __syncthreads();
+  const int per = kPlanBuckets / nt;   // nt divides kPlanBuckets
+  const int lo = tid * per, hi = lo + per;
+  int local = 0;
+  for (int r = lo; r < hi; ++r) local += hist[kPlanBuckets - 1 - r];
+  scan[tid] = local;
+  __syncthreads();
+  for (int off = 1; off < nt; off <<= 1) {
+    const int add = tid >= off ? scan[tid - off] : 0;
+    __syncthreads();
+    scan[tid] += add;
+    __syncthreads();
+  }
+  const int nitems = scan[nt - 1];
+  int run = scan[tid] - local;
+  for (int r = lo; r < hi; ++r) {
+    const int c = kPlanBuckets - 1 - r;
+    const int h = hist[c];
+    hist[c] = run;
+    run += h;
+  }
+  __syncthreads();
+  for (int j = tid; j < len; j += nt) {
+    const int id = c0 + j, ln = list_len(cnt[id], cap), ns = nseg(ln);
+    int entry = -1;
+    if (ns > 1) {
+      const int p0 = 2 * kd.extra * x + atomicAdd(&ctr[1], ns);
+      entry = kd.extra * x + atomicAdd(&ctr[0], 1);
+      splits[entry] = make_int4(id, p0, ns, 0);
+    }
+    for (int s2 = 0; s2 < ns; ++s2) {
+      int st;
+      const int sl = seg(ln, ns, s2, st);
+      items[8 * atomicAdd(&hist[bucket(sl)], 1) + x] =
+          make_int4(id, st, sl, ns > 1 ? entry * 1024 + s2 : -1);
+    }
+  }
+  __syncthreads();
+  const int J = plan_items_per_xcd(n, kd);
+  for (int j = nitems + tid; j < J; j += nt) items[8 * j + x] = make_int4(-1, 0, 0, -1);
+  for (int j = ctr[0] + tid; j < kd.extra; j += nt)
+    splits[kd.extra * x + j] = make_int4(-1, 0, 0, 0);
+  for (int a = 0; a < ndone; ++a)
+    for (int j = tid; j < kd.extra; j += nt) done[8 * kd.extra * a + kd.extra * x + j] = 0;
+}
+
+// A plan item checked against the call: {list, first entry, entries, split}
+// with the split entry it names (sp = {list, first partial slot, segments}).
+// An item that does not fit (a plan written for another mask, or never
+// written) is refused, so nothing is read or written out of range.
+__device__ inline bool plan_item_ok(const int4 item, int nlists, int cap, PlanKind kd,
+                                    const int4* __restrict__ splits, int4& sp) {
+  if (item.x < 0 || item.x >= nlists || item.y < 0 || item.z < 0 || item.y + item.z > cap)
+    return false;
+  sp = make_int4(0, 0, 0, 0);
+  if (item.w < 0) return true;
+  const int entry = item.w >> 10, seg = item.w & 1023;
+  if (entry >= 8 * kd.extra) return false;
+  sp = splits[entry];
+  return sp.x == item.x && sp.y >= 0 && sp.z >= 2 && seg < sp.z && sp.y + sp.z <= 16 * kd.extra;
+}
+
+
+// Byte offsets of a plan in its int32 array: items, split entries, then
+// `ndone` counter arrays.
+struct PlanLayout {
+  size_t items, splits, done, bytes;
+};
+__host__ __device__ inline PlanLayout plan_layout(int n, PlanKind kd, int ndone) {
+  PlanLayout l;
+  l.items = 0;
+  l.splits = (size_t)8 * plan_items_per_xcd(n, kd) * sizeof(int4);
+  l.done = l.splits + (size_t)8 * kd.extra * sizeof(int4);
+  l.bytes = l.done + (size_t)ndone * 8 * kd.extra * sizeof(int);
+  return l;
+}
+constexpr int kRowCounters = 2;   // forward, dQ
+constexpr int kColCounters = 1;   // dK/dV
+
+}  // namespace sa2

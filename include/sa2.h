@@ -67,27 +67,30 @@ typedef enum { SA2_BF16 = 0, SA2_F32 = 1 } sa2_dtype;
  *   col_cnt  int32 [B, H, Tk]: query blocks that keep each key block.
  *   col_idx  int32 [B, H, Tk, Tq]: the first col_cnt entries are those query
  *            blocks, ascending (the transposed index the backward walks).
- *   row_order, col_order  optional (may be NULL) int32 [B*H*Tq], [B*H*Tk]:
- *            a work order for the attention kernels: a permutation of the
- *            flat (b*H + h)*Tq + i (resp. *Tk + j) indices.  Workgroup slot s
- *            runs on XCD s % 8; the slots of XCD x hold the x-th contiguous
- *            eighth of the flat indices (the fixed XCD-aware order), sorted
- *            by decreasing row_cnt (col_cnt), so that each XCD's L2 serves a
- *            narrow band of heads and each XCD starts its longest lists
- *            first.  The order among equal counts is unspecified; it changes
- *            scheduling only, never results.  When NULL the kernels use the
- *            fixed XCD-aware order itself.
+ *   row_plan, col_plan  int32 arrays of sa2_mask_plan_bytes(..., 0) and
+ *            (..., 1) bytes, 16-byte aligned: the work plans of the bf16,
+ *            d = 128 attention kernels, made from row_cnt (forward, dQ) and
+ *            col_cnt (dK/dV).  A plan assigns the lists to workgroup slots,
+ *            XCD by XCD (slot s runs on XCD s % 8; XCD x takes the x-th
+ *            contiguous eighth of the lists, rows by count and columns by
+ *            cost), longest first, and cuts a list much longer than the mean
+ *            load of the kernel's resident workgroups into segments whose
+ *            partial sums the list's last segment combines in a fixed order.
+ *            Each plan also holds the completion counters of the kernels
+ *            that walk it (rows: forward and dQ; columns: dK/dV): the plan
+ *            zeroes them and each kernel leaves them zeroed, so attention
+ *            calls that use one mask must not run at the same time.
  *
- * sa2_build_mask writes all these arrays; the attention calls read row_cnt /
- * row_idx (forward, dQ) and col_cnt / col_idx (dK, dV), and the orders when
- * present.  For bf16 and d = 128 the dQ call also reads col_cnt (it writes
- * the dK/dV work plan, which depends on the column counts).  A caller may
- * supply its own mask to the attention calls as long as the lists are
- * ascending, duplicate-free and in range, every row_cnt is at
- * least 1, and the orders (if given) are permutations.  A mask that breaks
- * these rules gives undefined outputs but no access out of range: counts are
- * clamped to [0, Tk] (rows) and [0, Tq] (columns), list entries outside the
- * tensors read as zero rows, and order entries out of range are skipped.
+ * sa2_build_mask writes all these arrays (sa2_mask_plans remakes the plans
+ * of a mask whose lists the caller wrote); the attention calls read row_cnt /
+ * row_idx (forward, dQ), col_cnt / col_idx (dK, dV) and, for bf16 with
+ * d = 128, the plans.  A caller may supply its own mask to the attention
+ * calls as long as the lists are ascending, duplicate-free and in range and
+ * every row_cnt is at least 1.  A mask that breaks these rules, or whose
+ * plans were made for other counts, gives undefined outputs but no access
+ * out of range: counts are clamped to [0, Tk] (rows) and [0, Tq] (columns),
+ * list entries outside the tensors read as zero rows, and plan entries that
+ * do not fit the mask are skipped.
  */
 typedef struct sa2_mask {
   int32_t B, H, N, bq, bk, Tq, Tk;
@@ -96,8 +99,8 @@ typedef struct sa2_mask {
   int32_t* row_idx;
   int32_t* col_cnt;
   int32_t* col_idx;
-  int32_t* row_order;
-  int32_t* col_order;
+  int32_t* row_plan;
+  int32_t* col_plan;
 } sa2_mask;
 
 /* Library version string, e.g. "sa2 0.1.0 gfx950". */
@@ -112,6 +115,19 @@ const char* sa2_last_error(void);
  * (B*H*(Tq*d + Tk*d + Tq*Tk) doubles).  Returns 0 for an invalid geometry.
  */
 size_t sa2_mask_workspace_bytes(int B, int H, int N, int d, int bq, int bk);
+
+/*
+ * Bytes of a mask's work plan: columns = 0 for the row plan (query blocks),
+ * 1 for the column plan (key blocks).  About 20 bytes per list plus 25 KB.
+ * Returns 0 for an invalid geometry.
+ */
+size_t sa2_mask_plan_bytes(int B, int H, int N, int bq, int bk, int columns);
+
+/*
+ * Remakes the work plans of `mask` from its row_cnt and col_cnt (which the
+ * caller wrote; sa2_build_mask makes them itself).  Asynchronous on `stream`.
+ */
+sa2_status sa2_mask_plans(const sa2_mask* mask, void* stream);
 
 /*
  * Hybrid Top-k + Top-p block mask (gist.science, section 2A; Top-p as the
@@ -132,7 +148,7 @@ size_t sa2_mask_workspace_bytes(int B, int H, int N, int d, int bq, int bk);
  * q, k: device [B, H, N, d] in `dtype`, 16-byte aligned, d a multiple of 8 and
  * at most 256.  The pooled values and scores are computed in fp64 from the
  * inputs exactly as stored.  mask: geometry fields filled in by the caller
- * (Tq, Tk as above) and all five arrays allocated.  workspace: at least
+ * (Tq, Tk as above) and all seven arrays allocated.  workspace: at least
  * sa2_mask_workspace_bytes(...) bytes of device memory, 256-byte aligned.
  * Limits: Tq, Tk <= 4096 and B*H <= 65535 (else SA2_EUNSUPPORTED).  k_frac <= 0
  * together with p <= 0 (both rules off)
@@ -166,6 +182,14 @@ sa2_status sa2_build_mask_noalloc(const void* q, const void* k, int dtype,
                                   void* stream);
 
 /*
+ * Bytes of device workspace sa2_attn_fwd needs: for d = 128, 1024
+ * partial-sum slots of 66 KB (unnormalised output rows, running maxima and
+ * row sums of the segments of long rows; 67.6 MB); 0 for d = 64, whose
+ * kernels need none.  Returns 0 for an invalid geometry too.
+ */
+size_t sa2_fwd_workspace_bytes(int B, int H, int N, int d);
+
+/*
  * Block-sparse attention forward (gist.science, section 2C: tiles are kept or
  * dropped whole; dropped tiles cost neither the matmuls nor the softmax).
  *
@@ -174,25 +198,36 @@ sa2_status sa2_build_mask_noalloc(const void* q, const void* k, int dtype,
  *   key blocks listed in row_idx for row i (non-causal);
  *   lse_t = log sum_u exp(q_t . k_u / sqrt(d)) over the same keys.
  *
+ * For bf16 with d = 128 the kernel follows the mask's row plan: a row list
+ * much longer than the mean load of the kernel's resident workgroups (a
+ * skewed head under Top-p keeps most key blocks in a few rows, gist.science
+ * section 1) is walked in segments in parallel; each segment leaves its
+ * unnormalised output, running maximum and row sum in the workspace, and the
+ * last segment of the row combines them in segment order (the same softmax,
+ * bitwise reproducible).
+ *
  * q, k, v: device [B, H, N, d]; o: device [B, H, N, d] (written); lse: device
  * fp32 [B, H, N] (written).  mask: as produced by sa2_build_mask (row lists
- * used).  Limits: d in {64, 128}, bq in {64, 128}, bk = 64.
+ * used).  workspace: at least sa2_fwd_workspace_bytes(...) bytes of device
+ * memory, 256-byte aligned (may be NULL when that is 0); scratch between
+ * calls, no initialisation needed.  Limits: d in {64, 128}, bq in {64, 128},
+ * bk = 64.
  */
 sa2_status sa2_attn_fwd(const void* q, const void* k, const void* v, int dtype,
                         int B, int H, int N, int d, const sa2_mask* mask,
-                        void* o, float* lse, void* stream);
+                        void* o, float* lse, void* workspace, size_t workspace_bytes,
+                        void* stream);
 
 /*
  * Bytes of device workspace the backward calls need: two fp32 per token
- * row, the row sums Delta_t = sum_c dO_tc * O_tc and the LSE in base 2
+ * row, the row sums Delta_t = sum_c dO_tc O_tc and the LSE in base 2
  * (lse_t * log2(e)), for every row of every 128-row query block (padding
  * rows past N included): B*H*4*ceil(N/128) groups of 32 rows x 2 x 4 bytes,
- * rounded up to 256 bytes.  For d = 128 it also holds the dK/dV work plan:
- * column lists longer than a fair share of the kernel's resident workgroups
- * are cut into segments, each segment's fp32 partial dK, dV goes to one of
- * 2048 slots of 64 KB, and the partials are added in segment order (128 MB
- * plus about 18 bytes per key block and 36 KB).  The contents need no
- * initialisation and are scratch between calls.
+ * rounded up to 256 bytes.  For d = 128 it also holds the partial-sum slots
+ * of the lists the mask's plans cut into segments: 1024 slots of 64 KB for
+ * dQ rows and 2048 of 64 KB for dK/dV columns (192 MB); the partials are
+ * added in segment order.  The contents need no initialisation and are
+ * scratch between calls.
  */
 size_t sa2_bwd_workspace_bytes(int B, int H, int N, int d);
 
@@ -204,8 +239,9 @@ size_t sa2_bwd_workspace_bytes(int B, int H, int N, int d);
  *   dS = P * (dP - Delta);  dQ = dS K / sqrt(d);  dK = dS^T Q / sqrt(d).
  * P is recomputed from q, k and lse.  dK and dV of a key block are summed over
  * the query blocks in its col_idx list, dQ of a query block over its row_idx
- * list (a long column list is summed in segments, then across segments in
- * a fixed order); no atomics are used, so results are bitwise reproducible.  Key
+ * list (long lists of either kind are summed in segments, then across
+ * segments in a fixed order); no atomics are used, so results are bitwise
+ * reproducible.  Key
  * blocks that no query block keeps get dK = dV = 0.
  *
  * q, k, v, o, dout: device [B, H, N, d] (o and lse from sa2_attn_fwd on the
@@ -223,10 +259,9 @@ sa2_status sa2_attn_bwd(const void* q, const void* k, const void* v,
 /*
  * First half of sa2_attn_bwd: dQ = dS K / sqrt(d) over each query block's
  * row list, and Delta_t = sum_c dO_tc O_tc and lse_t * log2(e), which it
- * leaves in `workspace` for sa2_attn_bwd_dkdv, together with (bf16, d = 128)
- * the dK/dV work plan made from the mask's column counts.  Arguments as for
- * sa2_attn_bwd; it reads row_cnt and row_idx, and for bf16 with d = 128 also
- * col_cnt (SA2_EINVAL if that is NULL).
+ * leaves in `workspace` for sa2_attn_bwd_dkdv.  Arguments as for
+ * sa2_attn_bwd; it reads row_cnt and row_idx, and for bf16 with d = 128 the
+ * row plan (SA2_EINVAL if that is NULL).
  */
 sa2_status sa2_attn_bwd_dq(const void* q, const void* k, const void* v,
                            const void* o, const float* lse, const void* dout,
@@ -236,12 +271,12 @@ sa2_status sa2_attn_bwd_dq(const void* q, const void* k, const void* v,
 
 /*
  * Second half of sa2_attn_bwd: dV = P^T dO and dK = dS^T Q / sqrt(d) over
- * each key block's column list.  Reads Delta, the base-2 LSE and the work
- * plan from `workspace` (lse itself is still checked), so it must follow
- * sa2_attn_bwd_dq on the same inputs, mask and workspace, on the same stream
- * (or after it completes).  Called otherwise, dK and dV are undefined, but
- * plan entries that do not fit the call are skipped, so nothing is read or
- * written out of range.  Arguments as for sa2_attn_bwd.
+ * each key block's column list (for bf16 with d = 128 following the mask's
+ * column plan).  Reads Delta and the base-2 LSE from `workspace` (lse itself
+ * is still checked), so it must follow sa2_attn_bwd_dq on the same inputs,
+ * mask and workspace, on the same stream (or after it completes).  Called
+ * otherwise, dK and dV are undefined, but nothing is read or written out of
+ * range.  Arguments as for sa2_attn_bwd.
  */
 sa2_status sa2_attn_bwd_dkdv(const void* q, const void* k, const void* v,
                              const float* lse, const void* dout,

@@ -22,6 +22,8 @@ int main(void) {
   CHECK(sa2_mask_workspace_bytes(1, 12, 32760, 128, 128, 64) > 0);
   CHECK(sa2_mask_workspace_bytes(0, 12, 32760, 128, 128, 64) == 0);
   CHECK(sa2_bwd_workspace_bytes(1, 12, 32760, 128) > sa2_bwd_workspace_bytes(1, 12, 32760, 64));
+  CHECK(sa2_fwd_workspace_bytes(1, 12, 32760, 128) > 0);
+  CHECK(sa2_fwd_workspace_bytes(1, 12, 32760, 64) == 0);
 
   sa2_mask m;
   memset(&m, 0, sizeof m);
@@ -34,7 +36,7 @@ int main(void) {
   /* d = 96 is not implemented by the attention kernels */
   char dummy[64];
   void* p = (void*)(((uintptr_t)dummy + 15) & ~(uintptr_t)15);
-  st = sa2_attn_fwd(p, p, p, SA2_BF16, 1, 1, 256, 96, &m, p, (float*)p, NULL);
+  st = sa2_attn_fwd(p, p, p, SA2_BF16, 1, 1, 256, 96, &m, p, (float*)p, NULL, 0, NULL);
   CHECK(st == SA2_EUNSUPPORTED);
   st = sa2_attn_bwd(p, p, p, p, (const float*)p, p, SA2_BF16, 1, 1, 256, 64, &m, p, p, p, p, 16,
                     NULL);

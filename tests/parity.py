@@ -113,24 +113,90 @@ def check_lists(bitmap: np.ndarray, row_cnt, row_idx, col_cnt, col_idx):
         assert np.array_equal(col_idx[j, :len(want)], want), f"column {j} list"
 
 
-def check_orders(row_cnt: np.ndarray, col_cnt: np.ndarray, row_order, col_order):
-    """Work orders: permutations of the flat row / column indices in which the
-    slots of XCD x (slot % 8 == x) hold the x-th contiguous eighth of the
-    indices (the split of the fixed XCD-aware order) with non-increasing
-    counts; the order among equal counts is free."""
-    for cnt, order in ((row_cnt.reshape(-1), row_order), (col_cnt.reshape(-1), col_order)):
-        if order is None:
-            continue
-        order = np.asarray(order)
-        n = cnt.size
-        assert np.array_equal(np.sort(order), np.arange(n)), "order is not a permutation"
-        q, r = divmod(n, 8)
-        for x in range(8):
-            c0, ln = x * q + min(x, r), q + (1 if x < r else 0)
-            share = order[x::8]
-            assert share.size == ln, f"XCD {x}: {share.size} slots, expected {ln}"
-            assert np.array_equal(np.sort(share), np.arange(c0, c0 + ln)), f"XCD {x}: wrong share"
-            assert np.all(np.diff(cnt[share]) <= 0), f"XCD {x}: not by decreasing count"
+ROW_PLAN = dict(slots=512, fair=1, extra=64, balanced=False, counters=2)
+COL_PLAN = dict(slots=1024, fair=2, extra=128, balanced=True, counters=1)
+
+
+def _items_per_xcd(n: int, kd: dict) -> int:
+    slack = ((n + 7) // 8 + 15) // 16 if kd["balanced"] else 0
+    return (n + 7) // 8 + 2 * slack + kd["extra"]
+
+
+def check_plan(cnt, plan, kd: dict, cap: int) -> int:
+    """A work plan (the int32 array the mask builder wrote) against the list
+    counts it was made from: every list is covered by its items in order, as
+    one item or as nearly equal segments; a list is cut exactly when it is
+    longer than L = max(8, fair * ceil(total / slots), ceil(share / extra)) of
+    its XCD share, into ceil(n / L) segments; XCD x's items are the x-th
+    contiguous share of the lists (equal counts for rows), longest first; each
+    split owns partial slots inside its share's range; every completion
+    counter is zero.  Returns the number of split lists."""
+    cnt = np.clip(np.asarray(cnt).reshape(-1).astype(np.int64), 0, cap)
+    n, ex = cnt.size, kd["extra"]
+    J = _items_per_xcd(n, kd)
+    buf = np.asarray(plan).reshape(-1).view(np.int32)
+    items = buf[:8 * J * 4].reshape(J, 8, 4)
+    splits = buf[8 * J * 4:8 * J * 4 + 8 * ex * 4].reshape(8 * ex, 4)
+    done = buf[8 * J * 4 + 8 * ex * 4:8 * J * 4 + 8 * ex * 4 + kd["counters"] * 8 * ex]
+    assert np.all(done == 0), "completion counters not zero"
+    total = int(cnt.sum())
+    per_list: dict[int, list] = {}
+    lo = 0
+    nsplit = 0
+    slot_owner = {}
+    for x in range(8):
+        its = items[:, x, :]
+        k = int(np.count_nonzero(its[:, 0] >= 0))
+        assert np.all(its[:k, 0] >= 0) and np.all(its[k:, 0] == -1), f"XCD {x}: gaps in items"
+        valid = its[:k]
+        keys = np.minimum(valid[:, 2], 4095)
+        assert np.all(np.diff(keys) <= 0), f"XCD {x}: not longest first"
+        lists = np.unique(valid[:, 0])
+        if lists.size:
+            assert lists[0] == lo and lists[-1] == lo + lists.size - 1, f"XCD {x}: share not contiguous"
+        if not kd["balanced"]:
+            q, r = divmod(n, 8)
+            assert lists.size == q + (1 if x < r else 0), f"XCD {x}: share size"
+        lo += lists.size
+        share = int(cnt[lists].sum()) if lists.size else 0
+        L = max(8, kd["fair"] * -(-total // kd["slots"]), -(-share // ex))
+        for it in valid:
+            per_list.setdefault(int(it[0]), []).append(tuple(int(v) for v in it))
+        for lst in lists:
+            its_l = sorted(per_list[int(lst)], key=lambda t: t[1])
+            c = int(cnt[lst])
+            if c <= L:
+                assert len(its_l) == 1 and its_l[0] == (lst, 0, c, -1), f"list {lst}: {its_l}"
+                continue
+            nsplit += 1
+            ns = -(-c // L)
+            assert len(its_l) == ns, f"list {lst}: {len(its_l)} segments, expected {ns}"
+            entries = {t[3] >> 10 for t in its_l}
+            assert len(entries) == 1, f"list {lst}: several split entries"
+            e = entries.pop()
+            assert e // ex == x, f"list {lst}: split entry outside its share"
+            sp = splits[e]
+            assert sp[0] == lst and sp[2] == ns, f"list {lst}: split entry {sp}"
+            assert sorted(t[3] & 1023 for t in its_l) == list(range(ns))
+            assert its_l[0][1] == 0 and its_l[-1][1] + its_l[-1][2] == c
+            for a, b in zip(its_l, its_l[1:]):
+                assert a[1] + a[2] == b[1], f"list {lst}: segments not contiguous"
+            sl = [t[2] for t in its_l]
+            assert max(sl) - min(sl) <= 1, f"list {lst}: segments {sl}"
+            assert 2 * ex * x <= sp[1] and sp[1] + ns <= 2 * ex * (x + 1), f"list {lst}: slots"
+            for slot in range(sp[1], sp[1] + ns):
+                assert slot not in slot_owner, f"slot {slot} shared"
+                slot_owner[slot] = lst
+    assert lo == n and sorted(per_list) == list(range(n)), "lists missing from the plan"
+    return nsplit
+
+
+def check_plans(mask) -> tuple[int, int]:
+    """Both plans of a BlockMask; returns (split rows, split columns)."""
+    return (check_plan(mask.row_cnt.cpu().numpy(), mask.row_plan.cpu().numpy(), ROW_PLAN,
+                       mask.Tk),
+            check_plan(mask.col_cnt.cpu().numpy(), mask.col_plan.cpu().numpy(), COL_PLAN,
+                       mask.Tq))
 
 
 def rel_fro(a: np.ndarray, b: np.ndarray) -> float:

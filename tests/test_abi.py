@@ -39,22 +39,30 @@ def test_workspace_sizes():
     assert L.sa2_mask_workspace_bytes(B, H, N, d, bq, bk) == want
     assert L.sa2_mask_workspace_bytes(0, H, N, d, bq, bk) == 0
     stats = up(B * H * 4 * (-(-N // 128)) * 32 * 2 * 4)
-    # d = 128 adds the dK/dV plan: items, split entries, their completion
-    # counters, partial-sum slots
-    ncols = B * H * Tk
-    slack = ((ncols + 7) // 8 + 15) // 16        # cost-balanced XCD shares
-    items = up(8 * ((ncols + 7) // 8 + 2 * slack + 128) * 16)
-    splits = up(8 * 128 * 16)
-    done = up(8 * 128 * 4)
-    partials = up(8 * 2 * 128 * 2 * 64 * 128 * 4)
-    assert L.sa2_bwd_workspace_bytes(B, H, N, d) == stats + items + splits + done + partials
+    # d = 128 adds the partial-sum slots of split lists: 2 x 64 per XCD share
+    # for dQ rows (128 x 128 fp32 each), 2 x 128 for dK/dV columns (64 keys
+    # of dV and dK); the forward's slots also hold each row's max and sum
+    dq_slots = up(8 * 2 * 64 * 128 * 128 * 4)
+    dkdv_slots = up(8 * 2 * 128 * 2 * 64 * 128 * 4)
+    assert L.sa2_bwd_workspace_bytes(B, H, N, d) == stats + dq_slots + dkdv_slots
     assert L.sa2_bwd_workspace_bytes(B, H, N, 64) == stats
+    assert L.sa2_fwd_workspace_bytes(B, H, N, d) == up(8 * 2 * 64 * (128 * 128 + 256) * 4)
+    assert L.sa2_fwd_workspace_bytes(B, H, N, 64) == 0
+    # the mask's plans: items (one per list, plus slack for cost-balanced
+    # column shares and the extra segments), split entries, counters
+    nrows, ncols = B * H * Tq, B * H * Tk
+    row_plan = 8 * ((nrows + 7) // 8 + 64) * 16 + 8 * 64 * 16 + 2 * 8 * 64 * 4
+    slack = ((ncols + 7) // 8 + 15) // 16
+    col_plan = 8 * ((ncols + 7) // 8 + 2 * slack + 128) * 16 + 8 * 128 * 16 + 8 * 128 * 4
+    assert L.sa2_mask_plan_bytes(B, H, N, bq, bk, 0) == row_plan
+    assert L.sa2_mask_plan_bytes(B, H, N, bq, bk, 1) == col_plan
+    assert L.sa2_mask_plan_bytes(B, H, N, bq, bk, 2) == 0
 
 
 def _mask(B=1, H=1, N=256, bq=64, bk=64):
     Tq, Tk = -(-N // bq), -(-N // bk)
     fake = 1 << 20   # never dereferenced: validation fails first
-    return _lib.Sa2Mask(B, H, N, bq, bk, Tq, Tk, fake, fake, fake, fake, fake, None, None)
+    return _lib.Sa2Mask(B, H, N, bq, bk, Tq, Tk, fake, fake, fake, fake, fake, fake, fake)
 
 
 FAKE = ctypes.c_void_p(1 << 20)
@@ -87,7 +95,7 @@ def test_build_mask_validation():
     ]
     # more (batch, head) pairs than a grid dimension holds
     big = _lib.Sa2Mask(1, 70000, 256, 64, 64, 4, 4, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20,
-                       None, None)
+                       1 << 20, 1 << 20)
     st = L.sa2_build_mask(FAKE, FAKE, 0, 1, 70000, 256, 64, 64, 64, 0.1, 0.5, ctypes.byref(big),
                           ws, 1 << 40, None)
     assert st == _lib.SA2_EUNSUPPORTED, st
@@ -101,36 +109,60 @@ def test_attention_validation():
     L = _lib.lib()
     m = _mask()
     st, msg = _status_and_msg(L.sa2_attn_fwd(FAKE, FAKE, FAKE, 0, 1, 1, 256, 96,
-                                             ctypes.byref(m), FAKE, FAKE, None))
+                                             ctypes.byref(m), FAKE, FAKE, None, 0, None))
     assert st == _lib.SA2_EUNSUPPORTED and "d must be" in msg
     m2 = _mask(bk=32)
     st, msg = _status_and_msg(L.sa2_attn_fwd(FAKE, FAKE, FAKE, 0, 1, 1, 256, 64,
-                                             ctypes.byref(m2), FAKE, FAKE, None))
+                                             ctypes.byref(m2), FAKE, FAKE, None, 0, None))
     assert st == _lib.SA2_EUNSUPPORTED and "key blocks" in msg
     st, msg = _status_and_msg(L.sa2_attn_fwd(FAKE, FAKE, None, 0, 1, 1, 256, 64,
-                                             ctypes.byref(m), FAKE, FAKE, None))
+                                             ctypes.byref(m), FAKE, FAKE, None, 0, None))
     assert st == _lib.SA2_EINVAL
+    # d = 128 needs the forward workspace (row plan and partial slots)
+    m3 = _mask(bq=128)
+    need = L.sa2_fwd_workspace_bytes(1, 1, 256, 128)
+    assert need > 0 and L.sa2_fwd_workspace_bytes(1, 1, 256, 64) == 0
+    st, msg = _status_and_msg(L.sa2_attn_fwd(FAKE, FAKE, FAKE, 0, 1, 1, 256, 128,
+                                             ctypes.byref(m3), FAKE, FAKE, None, 0, None))
+    assert st == _lib.SA2_EINVAL and "workspace" in msg, msg
+    st, msg = _status_and_msg(L.sa2_attn_fwd(FAKE, FAKE, FAKE, 0, 1, 1, 256, 128,
+                                             ctypes.byref(m3), FAKE, FAKE, FAKE, need - 1, None))
+    assert st == _lib.SA2_EINVAL and "workspace" in msg, msg
     st, msg = _status_and_msg(L.sa2_attn_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 1, 1, 256,
                                              64, ctypes.byref(m), FAKE, FAKE, FAKE, FAKE, 16,
                                              None))
     assert st == _lib.SA2_EINVAL and "workspace" in msg
 
 
-def test_dq_refuses_a_mask_without_column_counts():
-    """bf16, d = 128: the dQ call writes the dK/dV plan from col_cnt, so a
-    mask without it is refused before any launch (fake pointers, never read)."""
+def test_attention_refuses_a_mask_without_plans():
+    """bf16, d = 128: the kernels walk the mask's plans, so a mask without
+    them (or with a misaligned one) is refused before any launch (fake
+    pointers, never read); the mask builder refuses one too."""
     L = _lib.lib()
     B, H, N, bq, bk = 1, 1, 256, 128, 64
-    m = _lib.Sa2Mask(B, H, N, bq, bk, 2, 4, 1 << 20, 1 << 20, 1 << 20, None, 1 << 20, None, None)
-    ws = ctypes.c_void_p(1 << 20)
+    f = 1 << 20
+    no_rows = _lib.Sa2Mask(B, H, N, bq, bk, 2, 4, f, f, f, f, f, None, f)
+    no_cols = _lib.Sa2Mask(B, H, N, bq, bk, 2, 4, f, f, f, f, f, f, None)
+    odd = _lib.Sa2Mask(B, H, N, bq, bk, 2, 4, f, f, f, f, f, f + 4, f)
+    ws = ctypes.c_void_p(f)
     wsb = L.sa2_bwd_workspace_bytes(B, H, N, 128)
-    st, msg = _status_and_msg(L.sa2_attn_bwd_dq(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, B, H, N,
-                                                128, ctypes.byref(m), FAKE, ws, wsb, None))
-    assert st == _lib.SA2_EINVAL and "column counts" in msg, msg
-    st, msg = _status_and_msg(L.sa2_attn_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, B, H, N,
-                                             128, ctypes.byref(m), FAKE, FAKE, FAKE, ws, wsb,
-                                             None))
-    assert st == _lib.SA2_EINVAL and "column counts" in msg, msg
+    fwb = L.sa2_fwd_workspace_bytes(B, H, N, 128)
+    for m in (no_rows, odd):
+        st, msg = _status_and_msg(L.sa2_attn_fwd(FAKE, FAKE, FAKE, 0, B, H, N, 128,
+                                                 ctypes.byref(m), FAKE, FAKE, ws, fwb, None))
+        assert st == _lib.SA2_EINVAL and "row plan" in msg, msg
+        st, msg = _status_and_msg(L.sa2_attn_bwd_dq(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, B, H,
+                                                    N, 128, ctypes.byref(m), FAKE, ws, wsb, None))
+        assert st == _lib.SA2_EINVAL and "row plan" in msg, msg
+    st, msg = _status_and_msg(L.sa2_attn_bwd_dkdv(FAKE, FAKE, FAKE, FAKE, FAKE, 0, B, H, N, 128,
+                                                  ctypes.byref(no_cols), FAKE, FAKE, ws, wsb,
+                                                  None))
+    assert st == _lib.SA2_EINVAL and "column plan" in msg, msg
+    st, msg = _status_and_msg(L.sa2_build_mask(FAKE, FAKE, 0, B, H, N, 128, bq, bk, 0.1, 0.5,
+                                               ctypes.byref(no_cols), ws, 1 << 30, None))
+    assert st == _lib.SA2_EINVAL and "null" in msg, msg
+    st, msg = _status_and_msg(L.sa2_mask_plans(ctypes.byref(no_rows), None))
+    assert st == _lib.SA2_EINVAL, msg
 
 
 def test_noalloc_mask_refuses_a_geometry_beyond_the_scratch():
@@ -140,7 +172,7 @@ def test_noalloc_mask_refuses_a_geometry_beyond_the_scratch():
     B, H, N, d, bq, bk = 1, 40, 75600, 128, 128, 64
     assert L.sa2_mask_workspace_bytes(B, H, N, d, bq, bk) > _lib.SA2_MASK_NOALLOC_MAX_BYTES
     m = _lib.Sa2Mask(B, H, N, bq, bk, -(-N // bq), -(-N // bk), 1 << 20, 1 << 20, 1 << 20,
-                     1 << 20, 1 << 20, None, None)
+                     1 << 20, 1 << 20, 1 << 20, 1 << 20)
     st, msg = _status_and_msg(L.sa2_build_mask_noalloc(FAKE, FAKE, 0, B, H, N, d, bq, bk, 0.03,
                                                        0.1, ctypes.byref(m), None))
     assert st == _lib.SA2_EUNSUPPORTED and "static scratch" in msg, msg

@@ -33,7 +33,7 @@ import block_sparse_attention_sa2_amd as sa2
 import oracle as O
 import workloads as W
 
-from parity import (GRAD_REL_FRO, check_forward, check_grad, check_lists, check_orders,
+from parity import (GRAD_REL_FRO, check_forward, check_grad, check_lists, check_plans,
                     compare_mask, device_inputs, f64, log_mask_exceptions, log_parity)
 
 pytestmark = pytest.mark.gpu
@@ -127,8 +127,7 @@ def wan13(request):
 
 def test_wan13_mask_all_heads(wan13):
     w, mask, ref = wan13["w"], wan13["mask"], wan13["ref"]
-    check_orders(mask.row_cnt.cpu().numpy(), mask.col_cnt.cpu().numpy(),
-                 mask.row_order.cpu().numpy(), mask.col_order.cpu().numpy())
+    check_plans(mask)
     _mask_all_heads("wan13_mask_all_heads", w, mask, ref, wan13["k_frac"], wan13["p"],
                     range(w.H))
     dens = mask.density()

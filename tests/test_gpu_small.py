@@ -18,7 +18,7 @@ import block_sparse_attention_sa2_amd as sa2
 import oracle as O
 import workloads as W
 
-from parity import (check_forward, check_grad, check_lists, check_orders, compare_mask,
+from parity import (check_forward, check_grad, check_lists, check_plans, compare_mask,
                     device_inputs, f64, log_parity)
 
 pytestmark = pytest.mark.gpu
@@ -54,7 +54,7 @@ def run_case(w: W.Workload, k_frac: float, p: float, backward: bool = True,
     bm = mask.bitmap.cpu().numpy()
     rc, ri = mask.row_cnt.cpu().numpy(), mask.row_idx.cpu().numpy()
     cc, ci = mask.col_cnt.cpu().numpy(), mask.col_idx.cpu().numpy()
-    check_orders(rc, cc, mask.row_order.cpu().numpy(), mask.col_order.cpu().numpy())
+    check_plans(mask)   # after the attention calls, which leave the counters zeroed
     stats = []
     worst = dict(o_max=0.0, o_mean=0.0, dq=0.0, dk=0.0, dv=0.0)
     for b in range(w.B):
@@ -167,11 +167,27 @@ def test_long_column_lists_are_split(N, bq):
     assert int(mask.col_cnt.min().item()) > 8
 
 
+@pytest.mark.parametrize("N,bq", [(2000, 128), (1100, 64)])
+def test_long_row_lists_are_split(N, bq):
+    """Dense masks on a small grid: every query block's row list is longer
+    than the row plan's segment length, so every row of the forward and of
+    dQ is cut into segments whose partials the last segment combines (and
+    every column of dK/dV); the plans check out against the counts, and O,
+    LSE, dQ, dK, dV match the oracle."""
+    w = W.Workload(f"rowsplit{bq}", 1, 2, N, 128, bq, 64, "normal", 32, "bf16", 1.0, 0.0)
+    dev, _ = device_inputs(w)
+    mask = sa2.build_mask(dev["q"], dev["k"], w.bq, w.bk, 1.0, 0.0)
+    torch.cuda.synchronize()
+    rows_split, cols_split = check_plans(mask)
+    assert rows_split == 2 * mask.Tq and cols_split == 2 * mask.Tk
+    run_case(w, 1.0, 0.0)
+
+
 @pytest.mark.parametrize("k_frac,p", [(0.1, 0.5), (1.0, 0.0)], ids=["hybrid", "dense_split"])
 def test_reproducible_and_fully_written(k_frac, p):
     """Two runs agree bit for bit; outputs pre-filled with NaN are fully
-    overwritten (with every block kept, every dK/dV column list is split and
-    summed by its last segment)."""
+    overwritten (with every block kept, every row list of the forward and dQ
+    and every dK/dV column list is split and combined by its last segment)."""
     w = W.Workload("repro", 1, 2, 1500, 128, 128, 64, "normal", 23, "bf16", k_frac, p)
     dev, _ = device_inputs(w)
     q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
@@ -191,18 +207,24 @@ def test_reproducible_and_fully_written(k_frac, p):
         assert torch.equal(a, b)
 
 
-def test_without_work_orders():
-    """With no work orders the kernels use their fixed order: same results."""
-    w = W.Workload("noorder", 1, 2, 1000, 128, 128, 64, "normal", 25, "bf16", 0.1, 0.5)
+def test_caller_written_lists_get_plans():
+    """A mask whose lists the caller wrote (here copied from a built mask)
+    gets its plans from sa2_mask_plans; the attention results are the same."""
+    w = W.Workload("ownlists", 1, 2, 1000, 128, 128, 64, "normal", 25, "bf16", 0.1, 0.5)
     dev, _ = device_inputs(w)
     q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
+    built = sa2.build_mask(q, k, w.bq, w.bk, w.k_frac, w.p)
+    own = sa2.BlockMask(1, 2, w.N, w.bq, w.bk, q.device)
+    for name in ("bitmap", "row_cnt", "row_idx", "col_cnt", "col_idx"):
+        getattr(own, name).copy_(getattr(built, name))
+    own.remake_plans()
     outs = []
-    for wo in (True, False):
-        mask = sa2.build_mask(q, k, w.bq, w.bk, w.k_frac, w.p, work_order=wo)
-        o, lse = sa2.attn_fwd(q, k, v, mask)
-        grads = sa2.attn_bwd(q, k, v, o, lse, do, mask)
+    for m in (built, own):
+        o, lse = sa2.attn_fwd(q, k, v, m)
+        grads = sa2.attn_bwd(q, k, v, o, lse, do, m)
         torch.cuda.synchronize()
-        outs.append([mask.bitmap.clone(), o, lse, *grads])
+        outs.append([o, lse, *grads])
+    assert torch.equal(built.row_plan, own.row_plan) and torch.equal(built.col_plan, own.col_plan)
     for a, b in zip(*outs):
         assert torch.equal(a, b)
 
@@ -357,12 +379,13 @@ def test_graph_replay():
     mws = torch.empty(sa2.mask_workspace_bytes(B, H, N, d, w.bq, w.bk), dtype=torch.uint8,
                       device=q.device)
     bws = torch.empty(sa2.bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=q.device)
+    fws = torch.empty(sa2.fwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=q.device)
     o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
 
     def step():
         sa2.build_mask(q, k, w.bq, w.bk, w.k_frac, w.p, mask=mask, workspace=mws)
-        sa2.attn_fwd(q, k, v, mask, o=o, lse=lse)
+        sa2.attn_fwd(q, k, v, mask, o=o, lse=lse, workspace=fws)
         sa2.attn_bwd(q, k, v, o, lse, do, mask, dq=dq, dk=dk, dv=dv, workspace=bws)
 
     side = torch.cuda.Stream()

@@ -12,7 +12,7 @@ import torch
 import block_sparse_attention_sa2_amd as sa2
 from block_sparse_attention_sa2_amd import _lib
 
-from parity import check_orders
+from parity import check_plans
 
 pytestmark = pytest.mark.gpu
 
@@ -29,7 +29,7 @@ def _noalloc():
 
 def _filled_mask(B, H, N, bq, bk, dev):
     m = sa2.BlockMask(B, H, N, bq, bk, dev)
-    for t in (m.bitmap, m.row_cnt, m.row_idx, m.col_cnt, m.col_idx, m.row_order, m.col_order):
+    for t in (m.bitmap, m.row_cnt, m.row_idx, m.col_cnt, m.col_idx, m.row_plan, m.col_plan):
         t.fill_(7)   # list tails are left untouched: both masks start alike
     return m
 
@@ -37,10 +37,9 @@ def _filled_mask(B, H, N, bq, bk, dev):
 def _same(a: sa2.BlockMask, b: sa2.BlockMask):
     for name in ("bitmap", "row_cnt", "row_idx", "col_cnt", "col_idx"):
         assert torch.equal(getattr(a, name), getattr(b, name)), name
-    # work orders: equal counts may come in any order
+    # plans: list order among equal lengths within an XCD share may differ
     for m in (a, b):
-        check_orders(m.row_cnt.cpu().numpy(), m.col_cnt.cpu().numpy(),
-                     m.row_order.cpu().numpy(), m.col_order.cpu().numpy())
+        check_plans(m)
 
 
 def test_noalloc_matches_workspace_build():
