@@ -24,7 +24,7 @@ __device__ inline int list_len(int n, int cap) { return min(max(n, 0), cap); }
 // atomically and the order of every sum is fixed, so results are
 // reproducible bit for bit; no workgroup waits for another.
 //
-// L is the larger of kMinSegment and `fair` times the mean load of the
+// L is the larger of `min_segment` and `fair` times the mean load of the
 // kernel's resident workgroups (`slots`), so that only lists that would set
 // the kernel's time are cut (each cut costs a partial write, a device-scope
 // release and the final combine), and per XCD share at least total / `extra`,
@@ -35,22 +35,30 @@ __device__ inline int list_len(int n, int cap) { return min(max(n, 0), cap); }
 // split entry * 1024 + segment}; item j of XCD x sits at 8j + x (the
 // workgroup slots that run on XCD x), longest first; unused items have list
 // -1.  Each XCD takes a contiguous share of the lists, so its L2 sees a
-// narrow band of heads.  Column shares are cut at equal cost rather than
-// equal count (densities differ from head to head, and the XCD with the most
-// dK/dV work would set the kernel's time); row shares keep equal counts (the
-// cost-balanced cut measured 1% slower for the forward and dQ).  Split
-// entries: int4 {list, first partial slot, segments}, `extra` per XCD share,
-// with one completion counter each, which the plan zeroes.
+// narrow band of heads.  Shares are cut at equal cost (list length + 1)
+// rather than equal count where the equal-count shares are unbalanced:
+// densities differ from head to head, and under a skewed mask the long lists
+// of one head would otherwise all fall to one XCD, whose share would set the
+// kernel's time.  Split entries: int4 {list, first partial slot, segments},
+// `extra` per XCD share.
 // ---------------------------------------------------------------------------
 struct PlanKind {
-  int slots;      // resident workgroups of the kernel that walks the lists
-  int fair;       // lists up to this many mean loads stay whole
-  int extra;      // extra segments (and split lists) per XCD share
-  bool balanced;  // XCD shares cut at equal cost (else at equal count)
+  int slots;        // resident workgroups of the kernel that walks the lists
+  int fair;         // lists up to this many mean loads stay whole
+  int extra;        // extra segments (and split lists) per XCD share
+  int min_segment;  // shortest segment worth its own workgroup
+  int imbalance;    // XCD shares are cut at equal cost when the costliest
+                    // equal-count share exceeds the mean by more than this
+                    // many percent (0: always), else at equal count
 };
-constexpr PlanKind kColPlan{1024, 2, 128, true};   // dK/dV: 256 CUs x 4 workgroups
-constexpr PlanKind kRowPlan{512, 1, 64, false};    // forward, dQ: 256 CUs x 2
-constexpr int kMinSegment = 8;
+// dK/dV: 256 CUs x 4 workgroups.  Forward and dQ: 256 CUs x 2; a row
+// segment also pays a combine pass over every segment of its row, so rows
+// are cut no finer than 16 key blocks.  Equal-count row shares keep whole
+// heads together in an XCD's L2 (the cost-balanced cut measured 4% slower
+// on a mask whose heads differ by a few percent), so rows are balanced only
+// when a share would carry over 10% more than its part.
+constexpr PlanKind kColPlan{1024, 2, 128, 8, 0};
+constexpr PlanKind kRowPlan{512, 1, 64, 16, 10};
 constexpr int kPlanBuckets = 4096;   // list lengths are ranked by min(length, 4095)
 constexpr size_t kPartialFloats = 2 * 64 * 128;           // dV and dK of one key block
 constexpr size_t kFwdPartialFloats = 128 * 128 + 2 * 128;  // O of a query block, m, l
@@ -60,7 +68,7 @@ constexpr size_t kDqPartialFloats = 128 * 128;             // dQ of a query bloc
 // equal-count one.
 __host__ __device__ inline int share_slack(int n) { return ((n + 7) / 8 + 15) / 16; }
 __host__ __device__ inline int plan_items_per_xcd(int n, PlanKind k) {
-  return (n + 7) / 8 + (k.balanced ? 2 * share_slack(n) : 0) + k.extra;
+  return (n + 7) / 8 + 2 * share_slack(n) + k.extra;
 }
 
 // XCD share x of n items: [b(x), b(x + 1)), where b(x) is the first item whose
@@ -118,12 +126,36 @@ static __device__ void plan_share(int x, const int32_t* __restrict__ cnt, int n,
                            int* __restrict__ done, int ndone, int* hist, int* scan,
                            long long* red, int* ctr) {
   const int tid = threadIdx.x, nt = blockDim.x, nw = nt / 64;
+  // the costs (list length + 1) of the eight equal-count shares
+  const int q8 = n / 8, r8 = n % 8;
+  auto eq_share = [&](int c) { return c < r8 * (q8 + 1) ? c / (q8 + 1) : r8 + (c - r8 * (q8 + 1)) / max(q8, 1); };
+  long long part[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) part[i] = 0;
+  for (int c = tid; c < n; c += nt) {
+    const int ln = list_len(cnt[c], cap) + 1, e = eq_share(c);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) part[i] += i == e ? ln : 0;
+  }
+  long long worst = 0, sum = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    long long v = part[i];
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    if ((tid & 63) == 0) red[tid >> 6] = v;
+    __syncthreads();
+    long long t = 0;
+    for (int w = 0; w < nw; ++w) t += red[w];
+    __syncthreads();
+    worst = max(worst, t);
+    sum += t;
+  }
+  const bool balanced = kd.imbalance == 0 || worst * 800 > sum * (800 + 8 * kd.imbalance);
   int2 sh;
-  if (kd.balanced) {
+  if (balanced) {
     sh = balanced_share(x, cnt, n, cap, red, ctr);
   } else {
-    const int q = n / 8, r = n % 8;
-    sh = make_int2(x * q + min(x, r), q + (x < r ? 1 : 0));
+    sh = make_int2(x * q8 + min(x, r8), q8 + (x < r8 ? 1 : 0));
   }
   const int c0 = sh.x, len = sh.y;
 
@@ -150,7 +182,7 @@ static __device__ void plan_share(int x, const int32_t* __restrict__ cnt, int n,
   long long share = 0;
   for (int w = 0; w < nw; ++w) share += red[w];
   const long long Lg =
-      max((long long)kMinSegment, kd.fair * ((total + kd.slots - 1) / kd.slots));
+      max((long long)kd.min_segment, kd.fair * ((total + kd.slots - 1) / kd.slots));
   const int L = (int)max(Lg, (share + kd.extra - 1) / kd.extra);
   auto nseg = [&](int ln) { return ln > L ? (ln + L - 1) / L : 1; };
   auto seg = [&](int ln, int ns, int s, int& start) {

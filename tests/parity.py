@@ -113,22 +113,26 @@ def check_lists(bitmap: np.ndarray, row_cnt, row_idx, col_cnt, col_idx):
         assert np.array_equal(col_idx[j, :len(want)], want), f"column {j} list"
 
 
-ROW_PLAN = dict(slots=512, fair=1, extra=64, balanced=False, counters=2)
-COL_PLAN = dict(slots=1024, fair=2, extra=128, balanced=True, counters=1)
+ROW_PLAN = dict(slots=512, fair=1, extra=64, min_segment=16, imbalance=10, counters=2)
+COL_PLAN = dict(slots=1024, fair=2, extra=128, min_segment=8, imbalance=0, counters=1)
 
 
 def _items_per_xcd(n: int, kd: dict) -> int:
-    slack = ((n + 7) // 8 + 15) // 16 if kd["balanced"] else 0
-    return (n + 7) // 8 + 2 * slack + kd["extra"]
+    return (n + 7) // 8 + 2 * (((n + 7) // 8 + 15) // 16) + kd["extra"]
+
+
+def _equal_count_shares(n: int):
+    q, r = divmod(n, 8)
+    return [(x * q + min(x, r), q + (1 if x < r else 0)) for x in range(8)]
 
 
 def check_plan(cnt, plan, kd: dict, cap: int) -> int:
     """A work plan (the int32 array the mask builder wrote) against the list
     counts it was made from: every list is covered by its items in order, as
     one item or as nearly equal segments; a list is cut exactly when it is
-    longer than L = max(8, fair * ceil(total / slots), ceil(share / extra)) of
-    its XCD share, into ceil(n / L) segments; XCD x's items are the x-th
-    contiguous share of the lists (equal counts for rows), longest first; each
+    longer than L = max(min_segment, fair * ceil(total / slots),
+    ceil(share / extra)) of its XCD share, into ceil(n / L) segments; XCD x's
+    items are the x-th contiguous share of the lists, longest first; each
     split owns partial slots inside its share's range; every completion
     counter is zero.  Returns the number of split lists."""
     cnt = np.clip(np.asarray(cnt).reshape(-1).astype(np.int64), 0, cap)
@@ -140,6 +144,8 @@ def check_plan(cnt, plan, kd: dict, cap: int) -> int:
     done = buf[8 * J * 4 + 8 * ex * 4:8 * J * 4 + 8 * ex * 4 + kd["counters"] * 8 * ex]
     assert np.all(done == 0), "completion counters not zero"
     total = int(cnt.sum())
+    costs = [int((cnt[a:a + ln] + 1).sum()) for a, ln in _equal_count_shares(n)]
+    balanced = kd["imbalance"] == 0 or max(costs) * 800 > sum(costs) * (800 + 8 * kd["imbalance"])
     per_list: dict[int, list] = {}
     lo = 0
     nsplit = 0
@@ -154,12 +160,11 @@ def check_plan(cnt, plan, kd: dict, cap: int) -> int:
         lists = np.unique(valid[:, 0])
         if lists.size:
             assert lists[0] == lo and lists[-1] == lo + lists.size - 1, f"XCD {x}: share not contiguous"
-        if not kd["balanced"]:
-            q, r = divmod(n, 8)
-            assert lists.size == q + (1 if x < r else 0), f"XCD {x}: share size"
+        if not balanced:
+            assert lists.size == _equal_count_shares(n)[x][1], f"XCD {x}: share size"
         lo += lists.size
         share = int(cnt[lists].sum()) if lists.size else 0
-        L = max(8, kd["fair"] * -(-total // kd["slots"]), -(-share // ex))
+        L = max(kd["min_segment"], kd["fair"] * -(-total // kd["slots"]), -(-share // ex))
         for it in valid:
             per_list.setdefault(int(it[0]), []).append(tuple(int(v) for v in it))
         for lst in lists:

@@ -51,7 +51,8 @@ def test_workspace_sizes():
     # the mask's plans: items (one per list, plus slack for cost-balanced
     # column shares and the extra segments), split entries, counters
     nrows, ncols = B * H * Tq, B * H * Tk
-    row_plan = 8 * ((nrows + 7) // 8 + 64) * 16 + 8 * 64 * 16 + 2 * 8 * 64 * 4
+    row_slack = ((nrows + 7) // 8 + 15) // 16
+    row_plan = 8 * ((nrows + 7) // 8 + 2 * row_slack + 64) * 16 + 8 * 64 * 16 + 2 * 8 * 64 * 4
     slack = ((ncols + 7) // 8 + 15) // 16
     col_plan = 8 * ((ncols + 7) // 8 + 2 * slack + 128) * 16 + 8 * 128 * 16 + 8 * 128 * 4
     assert L.sa2_mask_plan_bytes(B, H, N, bq, bk, 0) == row_plan
