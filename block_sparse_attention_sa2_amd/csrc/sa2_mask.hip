@@ -530,9 +530,10 @@ void plan_kernel(const int32_t* __restrict__ row_cnt, int nrows, int Tk,
                  int32_t* __restrict__ row_plan, const int32_t* __restrict__ col_cnt, int ncols,
                  int Tq, int32_t* __restrict__ col_plan) {
   __shared__ int hist[kPlanBuckets];
-  __shared__ int scan[kPlanThreads];
-  __shared__ long long red[kPlanThreads];
+  __shared__ int itot[kPlanThreads / 64];
+  __shared__ long long red[kPlanThreads / 64];
   __shared__ int ctr[2];
+  __shared__ long long pos[20];
   const int x = blockIdx.x % 8;
   const bool rows = blockIdx.x < 8;
   const PlanKind kd = rows ? kRowPlan : kColPlan;
@@ -541,7 +542,7 @@ void plan_kernel(const int32_t* __restrict__ row_cnt, int nrows, int Tk,
   char* b = reinterpret_cast<char*>(rows ? row_plan : col_plan);
   plan_share(x, rows ? row_cnt : col_cnt, n, rows ? Tk : Tq, kd,
              reinterpret_cast<int4*>(b + l.items), reinterpret_cast<int4*>(b + l.splits),
-             reinterpret_cast<int*>(b + l.done), ndone, hist, scan, red, ctr);
+             reinterpret_cast<int*>(b + l.done), ndone, hist, itot, red, ctr, pos);
 }
 
 static int next_pow2(int x) {

@@ -71,118 +71,112 @@ __host__ __device__ inline int plan_items_per_xcd(int n, PlanKind k) {
   return (n + 7) / 8 + 2 * share_slack(n) + k.extra;
 }
 
-// XCD share x of n items: [b(x), b(x + 1)), where b(x) is the first item whose
-// predecessors cost at least x / 8 of the total (an item costs its list length
-// plus one), clamped to within share_slack(n) of the equal-count boundary
-// x n / 8.  Every workgroup computes the same boundaries.  pre: blockDim.x
-// entries of LDS.
-static __device__ int2 balanced_share(int x, const int32_t* __restrict__ cnt, int n, int cap,
-                               long long* pre, int* bnd) {
-  const int tid = threadIdx.x, nt = blockDim.x;
-  const int per = (n + nt - 1) / nt;
-  const int lo = min(n, tid * per), hi = min(n, lo + per);
-  long long s = 0;
-  for (int i = lo; i < hi; ++i) s += list_len(cnt[i], cap) + 1;
-  pre[tid] = s;
-  if (tid < 2) bnd[tid] = 0;
-  __syncthreads();
-  for (int off = 1; off < nt; off <<= 1) {
-    const long long add = tid >= off ? pre[tid - off] : 0;
-    __syncthreads();
-    pre[tid] += add;
-    __syncthreads();
-  }
-  const long long total = pre[nt - 1], run = pre[tid] - s;
+// Inclusive scan of v over the workgroup (threads in order): a shuffle scan
+// in each wave, then the wave totals through LDS (tot: one entry per wave).
+// Returns the thread's inclusive sum and sets *all to the workgroup's total.
+template <typename T>
+__device__ inline T block_scan(T v, T* tot, T* all) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const long long target = ((long long)(x + k) * total + 7) / 8;
-    if (target > 0 && run < target && target <= run + s) {
-      long long acc = run;
-      int b = hi;
-      for (int i = lo; i < hi; ++i) {
-        if (acc >= target) { b = i; break; }
-        acc += list_len(cnt[i], cap) + 1;
-      }
-      bnd[k] = b;
-    }
+  for (int off = 1; off < 64; off <<= 1) {
+    const T u = __shfl_up(v, off);
+    if (lane >= off) v += u;
   }
+  if (lane == 63) tot[w] = v;
   __syncthreads();
-  const int H = share_slack(n);
-  int b[2];
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int e = (int)((long long)(x + k) * n / 8);
-    b[k] = min(max(bnd[k], max(0, e - H)), min(n, e + H));
+  T before = 0, sum = 0;
+  for (int i = 0; i < nw; ++i) {
+    const T t = tot[i];
+    before += i < w ? t : 0;
+    sum += t;
   }
-  __syncthreads();
-  return make_int2(b[0], b[1] - b[0]);
+  __syncthreads();   // tot may be reused
+  *all = sum;
+  return v + before;
 }
 
 // The plan of XCD share x of n lists (lengths cnt, each at most cap), by one
 // workgroup of nt threads (a multiple of 64 that divides kPlanBuckets).
-// LDS: hist[kPlanBuckets] ints, scan[nt] ints, red[nt] 64-bit sums, ctr[2].
-static __device__ void plan_share(int x, const int32_t* __restrict__ cnt, int n, int cap, PlanKind kd,
-                           int4* __restrict__ items, int4* __restrict__ splits,
-                           int* __restrict__ done, int ndone, int* hist, int* scan,
-                           long long* red, int* ctr) {
-  const int tid = threadIdx.x, nt = blockDim.x, nw = nt / 64;
-  // the costs (list length + 1) of the eight equal-count shares
+// LDS: hist[kPlanBuckets] ints, itot and red (nt / 64 entries each), ctr[2],
+// pos[20] 64-bit.
+//
+// Shares.  One pass gives every thread the cost (list length + 1) of a
+// contiguous chunk of the lists; a scan of the chunks gives the total and,
+// at the equal-count boundaries E(k) = k n / 8 (rounded as the lists are
+// dealt), the eight equal-count share costs.  Cost-balanced boundaries are
+// the first list whose predecessors cost at least k / 8 of the total,
+// clamped to within share_slack(n) lists of E(k).
+static __device__ void plan_share(int x, const int32_t* __restrict__ cnt, int n, int cap,
+                                  PlanKind kd, int4* __restrict__ items,
+                                  int4* __restrict__ splits, int* __restrict__ done, int ndone,
+                                  int* hist, int* itot, long long* red, int* ctr,
+                                  long long* pos) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int per = (n + nt - 1) / nt;
+  const int lo = min(n, tid * per), hi = min(n, lo + per);
+  auto cost = [&](int i) { return (long long)list_len(cnt[i], cap) + 1; };
+  long long csum = 0;
+#pragma unroll 4
+  for (int i = lo; i < hi; ++i) csum += cost(i);
+  if (tid < 20) pos[tid] = 0;
+  long long total;
+  const long long run = block_scan(csum, red, &total) - csum;
   const int q8 = n / 8, r8 = n % 8;
-  auto eq_share = [&](int c) { return c < r8 * (q8 + 1) ? c / (q8 + 1) : r8 + (c - r8 * (q8 + 1)) / max(q8, 1); };
-  long long part[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) part[i] = 0;
-  for (int c = tid; c < n; c += nt) {
-    const int ln = list_len(cnt[c], cap) + 1, e = eq_share(c);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) part[i] += i == e ? ln : 0;
+  auto eq = [&](int k) { return k * q8 + min(k, r8); };
+  // pos[k] (k = 0..8): prefix cost at E(k), by the thread whose chunk holds it
+  for (int k = 0; k <= 8; ++k) {
+    const int e = eq(k);
+    if ((e < n && e >= lo && e < hi) || (e == n && tid == nt - 1)) {
+      long long acc = run;
+      for (int i = lo; i < min(e, hi); ++i) acc += cost(i);
+      pos[k] = e == n ? total : acc;
+    }
   }
-  long long worst = 0, sum = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    long long v = part[i];
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-    if ((tid & 63) == 0) red[tid >> 6] = v;
-    __syncthreads();
-    long long t = 0;
-    for (int w = 0; w < nw; ++w) t += red[w];
-    __syncthreads();
-    worst = max(worst, t);
-    sum += t;
-  }
-  const bool balanced = kd.imbalance == 0 || worst * 800 > sum * (800 + 8 * kd.imbalance);
-  int2 sh;
-  if (balanced) {
-    sh = balanced_share(x, cnt, n, cap, red, ctr);
-  } else {
-    sh = make_int2(x * q8 + min(x, r8), q8 + (x < r8 ? 1 : 0));
-  }
-  const int c0 = sh.x, len = sh.y;
-
-  // totals over all lists and over this share
-  long long all = 0, mine = 0;
-  for (int c = tid; c < n; c += nt) {
-    const int ln = list_len(cnt[c], cap);
-    all += ln;
-    if (c >= c0 && c < c0 + len) mine += ln;
-  }
-  for (int off = 32; off > 0; off >>= 1) {
-    all += __shfl_xor(all, off);
-    mine += __shfl_xor(mine, off);
-  }
-  if ((tid & 63) == 0) red[tid >> 6] = all;
   __syncthreads();
-  long long total = 0;
-  for (int w = 0; w < nw; ++w) total += red[w];
+  long long worst = 0;
+  for (int k = 0; k < 8; ++k) worst = max(worst, pos[k + 1] - pos[k]);
+  const bool balanced = kd.imbalance == 0 || worst * 800 > total * (800 + 8 * kd.imbalance);
+  int b[2] = {eq(x), eq(x + 1)};
+  if (balanced) {
+    // pos[10 + k]: first list whose predecessors cost at least (x + k) / 8 of the total
+    if (tid < 2) pos[10 + tid] = (x + tid) == 0 ? 0 : n;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const long long target = ((long long)(x + k) * total + 7) / 8;
+      if (target > 0 && run < target && target <= run + csum) {
+        long long acc = run;
+        int bb = hi;
+        for (int i = lo; i < hi; ++i) {
+          if (acc >= target) { bb = i; break; }
+          acc += cost(i);
+        }
+        pos[10 + k] = bb;
+      }
+    }
+    __syncthreads();
+    const int H = share_slack(n);
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      b[k] = min(max((int)pos[10 + k], max(0, b[k] - H)), min(n, b[k] + H));
+  }
+  const int c0 = b[0], len = b[1] - b[0];
+  // pairs over all lists and over this share
+  long long mine = 0;
+  for (int j = tid; j < len; j += nt) mine += list_len(cnt[c0 + j], cap);
+  for (int off = 32; off > 0; off >>= 1) mine += __shfl_xor(mine, off);
   __syncthreads();
   if ((tid & 63) == 0) red[tid >> 6] = mine;
   for (int c = tid; c < kPlanBuckets; c += nt) hist[c] = 0;
   if (tid == 0) ctr[0] = ctr[1] = 0;
   __syncthreads();
   long long share = 0;
-  for (int w = 0; w < nw; ++w) share += red[w];
+  for (int w = 0; w < nt / 64; ++w) share += red[w];
+  const long long all = total - n;
+
+
   const long long Lg =
-      max((long long)kd.min_segment, kd.fair * ((total + kd.slots - 1) / kd.slots));
+      max((long long)kd.min_segment, kd.fair * ((all + kd.slots - 1) / kd.slots));
   const int L = (int)max(Lg, (share + kd.extra - 1) / kd.extra);
   auto nseg = [&](int ln) { return ln > L ? (ln + L - 1) / L : 1; };
   auto seg = [&](int ln, int ns, int s, int& start) {
@@ -202,25 +196,17 @@ static __device__ void plan_share(int x, const int32_t* __restrict__ cnt, int n,
     }
   }
   __syncthreads();
-  const int per = kPlanBuckets / nt;   // nt divides kPlanBuckets
-  const int lo = tid * per, hi = lo + per;
+  const int bper = kPlanBuckets / nt;   // nt divides kPlanBuckets
+  const int blo = tid * bper, bhi = blo + bper;
   int local = 0;
-  for (int r = lo; r < hi; ++r) local += hist[kPlanBuckets - 1 - r];
-  scan[tid] = local;
-  __syncthreads();
-  for (int off = 1; off < nt; off <<= 1) {
-    const int add = tid >= off ? scan[tid - off] : 0;
-    __syncthreads();
-    scan[tid] += add;
-    __syncthreads();
-  }
-  const int nitems = scan[nt - 1];
-  int run = scan[tid] - local;
-  for (int r = lo; r < hi; ++r) {
+  for (int r = blo; r < bhi; ++r) local += hist[kPlanBuckets - 1 - r];
+  int nitems;
+  int brun = block_scan(local, itot, &nitems) - local;
+  for (int r = blo; r < bhi; ++r) {
     const int c = kPlanBuckets - 1 - r;
     const int h = hist[c];
-    hist[c] = run;
-    run += h;
+    hist[c] = brun;
+    brun += h;
   }
   __syncthreads();
   for (int j = tid; j < len; j += nt) {
