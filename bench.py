@@ -186,6 +186,32 @@ def dense_baseline(sa2, q, k, v, do, w, sparse_attn_ms, args):
                     "attention time (forward + backward, mask excluded)"}
 
 
+def atomic_dq_backward(sa2, q, k, v, o, lse, do, mask, det_bwd_ms, steps, warmup):
+    """The alternative backward: dQ formed inside the dK/dV pass and added to
+    an fp32 accumulator with atomics (sa2_attn_bwd_atomic_dq), timed beside
+    the deterministic dQ + dK/dV passes on the same inputs and mask."""
+    import torch
+    B, H, N, d = q.shape
+    ws = torch.empty(sa2.bwd_atomic_workspace_bytes(B, H, N, d), dtype=torch.uint8,
+                     device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    times = []
+    for it in range(warmup + steps):
+        ev[0].record()
+        sa2.attn_bwd_atomic_dq(q, k, v, o, lse, do, mask, dq=dq, dk=dk, dv=dv, workspace=ws)
+        ev[1].record()
+        torch.cuda.synchronize()
+        if it >= warmup:
+            times.append(ev[0].elapsed_time(ev[1]))
+    ms = sum(times) / len(times)
+    return {"ms": round(ms, 4), "deterministic_ms": round(det_bwd_ms, 4),
+            "speedup_vs_deterministic": round(det_bwd_ms / ms, 3),
+            "note": "dQ by fp32 atomic adds inside the dK/dV pass (prep + fused pass + "
+                    "rounding); not bitwise reproducible; the default backward is the "
+                    "deterministic one"}
+
+
 def graph_replay(step, steps, warmup):
     """ms per step of the same step captured once in a HIP graph (the library
     allocates nothing and records no memset) and replayed back to back: the
@@ -563,6 +589,10 @@ def main():
         "eager_ms_per_step": round(eager_ms, 4),
         "note": "stages_ms and the roofline come from the eager run, with HIP events between "
                 "the stages"}
+    if backward:
+        out["atomic_dq_backward"] = atomic_dq_backward(
+            sa2, q, k, v, o, lse, do, mask, per["bwd_dq"] + per["bwd_dkdv"], args.steps,
+            args.warmup)
     if not args.no_dense_baseline and backward:
         out["dense_baseline"] = dense_baseline(sa2, q, k, v, do, w, attn_ms, args)
     if args.workload == "c2" and not args.no_second_geometry:

@@ -235,6 +235,29 @@ def attn_bwd(q, k, v, o, lse, dout, mask: BlockMask, dq=None, dk=None, dv=None,
     return dq, dk, dv
 
 
+def bwd_atomic_workspace_bytes(B, H, N, d) -> int:
+    return int(_lib.lib().sa2_bwd_atomic_workspace_bytes(B, H, N, d))
+
+
+def attn_bwd_atomic_dq(q, k, v, o, lse, dout, mask: BlockMask, dq=None, dk=None, dv=None,
+                       workspace=None):
+    """The backward with dQ accumulated by fp32 atomics inside the dK/dV pass
+    (sa2_attn_bwd_atomic_dq; bf16, d = 128) -> (dq, dk, dv)."""
+    dt, B, H, N, d = _bwd_prep(q, k, v, dout, lse, (o,))
+    _same_device(mask, q.device)
+    dq = torch.empty_like(q) if dq is None else _out(dq, q.shape, q.dtype, q.device, "dq")
+    dk = torch.empty_like(k) if dk is None else _out(dk, k.shape, k.dtype, k.device, "dk")
+    dv = torch.empty_like(v) if dv is None else _out(dv, v.shape, v.dtype, v.device, "dv")
+    workspace = _workspace(workspace, bwd_atomic_workspace_bytes(B, H, N, d), q.device)
+    st = _lib.lib().sa2_attn_bwd_atomic_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                           _ptr(dout), dt, B, H, N, d,
+                                           ctypes.byref(mask.c_struct()), _ptr(dq), _ptr(dk),
+                                           _ptr(dv), _ptr(workspace), workspace.numel(),
+                                           _stream(q.device))
+    check("sa2_attn_bwd_atomic_dq", st)
+    return dq, dk, dv
+
+
 def _bwd_prep(q, k, v, dout, lse, extra):
     dt = _dtype_code(q, k, v, dout, *extra)
     B, H, N, d = _shape(q)

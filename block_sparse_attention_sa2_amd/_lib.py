@@ -44,6 +44,9 @@ SIGNATURES = {
     "sa2_attn_bwd": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _MP, _P, _P, _P, _P, _Z, _P], _I),
     "sa2_attn_bwd_dq": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _MP, _P, _P, _Z, _P], _I),
     "sa2_attn_bwd_dkdv": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _MP, _P, _P, _P, _Z, _P], _I),
+    "sa2_bwd_atomic_workspace_bytes": ([_I, _I, _I, _I], _Z),
+    "sa2_attn_bwd_atomic_dq": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _MP, _P, _P, _P, _P,
+                                _Z, _P], _I),
     "sa2_distill_workspace_bytes": ([_I, _I, _I, _I], _Z),
     "sa2_distill_loss_grad": ([_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _Z, _P], _I),
 }

@@ -984,7 +984,13 @@ void dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
 // workgroups share a CU, so the two waves on a SIMD belong to different
 // workgroups and overlap their phases freely.
 // ---------------------------------------------------------------------------
-template <int BQ>
+//
+// With DQ set (the fused variant, sa2_attn_bwd_atomic_dq), each step also
+// forms dQ^T of the slice's rows over this block's 64 keys, dQ^T = K^T dS^T,
+// and adds it to the fp32 accumulator dq_acc with vector atomics: K is kept
+// in LDS for the transposed operand, and dS goes through LDS to be read one
+// row per lane.  The order of those additions is not fixed.
+template <int BQ, bool DQ>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void dkdv_pair_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                       const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
@@ -992,7 +998,8 @@ void dkdv_pair_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
                       const int32_t* __restrict__ col_idx, int N, int Tq, int Tk,
                       float scale_log2, float scale, bf16_t* __restrict__ dk,
                       bf16_t* __restrict__ dv, const int4* __restrict__ splits,
-                      int* __restrict__ done, float* __restrict__ partials, int ncols) {
+                      int* __restrict__ done, float* __restrict__ partials, int ncols,
+                      float* __restrict__ dq_acc) {
   constexpr int D = 128;
   using ST = Tile<D, kBoth>;   // slices: permuted, unpadded rows of 256 bytes
   static_assert(ST::kSwizzled, "slices are copied as whole 256-byte rows");
@@ -1003,6 +1010,9 @@ void dkdv_pair_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
   __shared__ __attribute__((aligned(16))) uint16_t so0[SLICE], so1[SLICE];   // dO slices
   __shared__ __attribute__((aligned(16))) float st0[64], st1[64];            // [lse | Delta]
   __shared__ int last_segment;
+  // fused variant only: the K tile (64 keys, permuted rows) and dS [32 rows][64 keys]
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[DQ ? 64 * D : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t ds_lds[DQ ? 32 * 64 : 8];
 
   // {block, first list entry, entries, -1 or split entry * 1024 + segment};
   // an entry that does not fit this call (a plan written for another mask,
@@ -1058,6 +1068,9 @@ void dkdv_pair_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
 
   const SwzAddr addr0(lane);
 
+  if constexpr (DQ) {   // the K tile, eight groups of four rows per wave (waited at step 0)
+    if (steps > 0) copy_groups<2>(make_rsrc(k + base, (uint32_t)N * D * 2), key0, 8 * kb, k_lds, uo);
+  }
   int row_cur = slice_row(0);
   if (steps > 0) copy(row_cur, sq0, so0, st0);
   int row_nxt = slice_row(1);
@@ -1140,6 +1153,44 @@ void dkdv_pair_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
         if (g + 2 < 2 * ND) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // reads of g + 2
       }
     }
+    if constexpr (DQ) {
+      // dS of rows 8gg + 4h + i at this lane's key, into [row][key] LDS
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bf16x8& sv = sb[gg >> 1];
+          reinterpret_cast<__bf16*>(ds_lds)[(8 * gg + 4 * h + i) * 64 + 32 * kb + l32] =
+              sv[4 * (gg & 1) + i];
+        }
+      __syncthreads();
+      // dQ (rows x d) over the 64 keys: wave kb takes d = 64kb .. 64kb + 63.
+      // The A operand dS takes this lane's row from ds_lds at the keys of
+      // k-slots 8h + i <-> 16t + 8(i/4) + 4h + i%4; the B operand K (keys x
+      // d) comes from the K tile by transposed reads with the same slots.
+      // Lanes run along d, so each atomic instruction covers two rows of 32
+      // consecutive floats.
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int db = 2 * kb + j;
+        f32x16 acc = zero16();
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint16_t* r = ds_lds + l32 * 64 + 16 * t + 4 * h;
+          const bf16x8 aop = cat(*reinterpret_cast<const bf16x4*>(r),
+                                 *reinterpret_cast<const bf16x4*>(r + 8));
+          acc = mfma32(aop, rd_tr(k_lds, A, t, db), acc);
+        }
+        // element e: row row0 + 8(e/4) + 4h + e%4, d = 32db + l32
+        float* dst = dq_acc + base + (size_t)row0 * D + 32 * db + l32;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int r = 8 * (e >> 2) + 4 * h + (e & 3);
+          if (row0 + r < N) unsafeAtomicAdd(dst + (size_t)r * D, acc[e]);
+        }
+      }
+    }
   });
 
   // Element e of block db is d = 32db + 8(e/4) + 4h + e%4 at key 32kb + l32:
@@ -1204,6 +1255,47 @@ void dkdv_pair_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
         store4(rk + c, acck[db][e] * scale, acck[db][e + 1] * scale, acck[db][e + 2] * scale,
                acck[db][e + 3] * scale);
       }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Fused-variant helpers (bf16, d = 128).  dq_prep_kernel: per 128-row group
+// of a head, Delta (from the bf16 dO that enters dP) and the base-2 LSE of
+// every row into the statistics (zeros for padding rows), and the rows' fp32
+// dQ accumulator zeroed; two threads per row, half of d each.
+// dq_finish_kernel: dQ = accumulator / sqrt(d), rounded to bf16.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256)
+void dq_prep_kernel(const bf16_t* __restrict__ o, const bf16_t* __restrict__ dout,
+                    const float* __restrict__ lse, float* __restrict__ stats,
+                    float* __restrict__ dq_acc, int N, int G4) {
+  constexpr int D = 128;
+  const int bh = blockIdx.x / G4, grp = blockIdx.x % G4;
+  const int tid = threadIdx.x, r = grp * 128 + (tid >> 1), half = tid & 1;
+  const size_t base = (size_t)bh * N * D;
+  float dpart = 0.f;
+  if (r < N) {
+    const size_t off = base + (size_t)r * D + 64 * half;
+#pragma unroll
+    for (int c = 0; c < 64; c += 8) dpart += delta_part(o + off + c, load8(dout + off + c));
+    float* acc = dq_acc + off;
+#pragma unroll
+    for (int c = 0; c < 64; c += 4) store4(acc + c, 0.f, 0.f, 0.f, 0.f);
+  }
+  dpart += __shfl_xor(dpart, 1);
+  if (half == 0) {
+    const int G = stat_groups(N);
+    stats[stat_delta(bh, G, r)] = r < N ? dpart : 0.f;
+    stats[stat_lse2(bh, G, r)] = r < N ? lse[(size_t)bh * N + r] * kLog2e : 0.f;
+  }
+}
+
+__global__ __launch_bounds__(256)
+void dq_finish_kernel(const float* __restrict__ dq_acc, size_t n4, float scale,
+                      bf16_t* __restrict__ dq) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(dq_acc + 4 * i);
+    store4(dq + 4 * i, a[0] * scale, a[1] * scale, a[2] * scale, a[3] * scale);
   }
 }
 
@@ -1446,8 +1538,8 @@ static void launch_dkdv(const BwdArgs& a) {
       static_cast<bf16_t*>(a.dk), static_cast<bf16_t*>(a.dv), a.cols.splits, a.cols.done,      \
       a.cols.partials, ncols
     const int grid = 8 * plan_items_per_xcd(ncols, kColPlan);
-    if (m->bq == 128) dkdv_pair_kernel<128><<<grid, 128, 0, a.s>>>(SA2_DKDV_PAIR_ARGS);
-    else dkdv_pair_kernel<64><<<grid, 128, 0, a.s>>>(SA2_DKDV_PAIR_ARGS);
+    if (m->bq == 128) dkdv_pair_kernel<128, false><<<grid, 128, 0, a.s>>>(SA2_DKDV_PAIR_ARGS, nullptr);
+    else dkdv_pair_kernel<64, false><<<grid, 128, 0, a.s>>>(SA2_DKDV_PAIR_ARGS, nullptr);
 #undef SA2_DKDV_PAIR_ARGS
     return;
   }
@@ -1608,6 +1700,55 @@ extern "C" sa2_status sa2_attn_bwd_dkdv(const void* q, const void* k, const void
                 "sa2_attn_bwd_dkdv: mask column plan is null or misaligned (bf16, d = 128)");
   by_type<DkdvLaunch>(dtype, d, bwd_args(q, k, v, nullptr, lse, dout, B, H, N, d, m, nullptr, dk, dv, ws, stream));
   return check_launch("dkdv_kernel");
+}
+
+extern "C" size_t sa2_bwd_atomic_workspace_bytes(int B, int H, int N, int d) {
+  if (B <= 0 || H <= 0 || N <= 0 || d != 128) return 0;
+  return sa2::bwd_workspace(B, H, N, d).total + up256((size_t)B * H * N * d * sizeof(float));
+}
+
+extern "C" sa2_status sa2_attn_bwd_atomic_dq(const void* q, const void* k, const void* v,
+                                             const void* o, const float* lse, const void* dout,
+                                             int dtype, int B, int H, int N, int d,
+                                             const sa2_mask* m, void* dq, void* dk, void* dv,
+                                             void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "sa2_attn_bwd_atomic_dq";
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !ws)
+    return fail(SA2_EINVAL, std::string(fn) + ": null pointer");
+  if (sa2_status st = check_common(fn, dtype, B, H, N, d, m)) return st;
+  if (dtype != SA2_BF16 || d != 128)
+    return fail(SA2_EUNSUPPORTED, std::string(fn) + ": bf16 with d = 128 only");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return fail(SA2_EINVAL, std::string(fn) + ": pointers must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+    return fail(SA2_EINVAL, std::string(fn) + ": workspace not 256-byte aligned");
+  if (ws_bytes < sa2_bwd_atomic_workspace_bytes(B, H, N, d))
+    return fail(SA2_EINVAL,
+                std::string(fn) + ": workspace smaller than sa2_bwd_atomic_workspace_bytes()");
+  if (!m->col_cnt || !m->col_idx || !m->col_plan || !aligned16(m->col_plan))
+    return fail(SA2_EINVAL, std::string(fn) + ": mask column lists or plan missing");
+  const BwdArgs a = bwd_args(q, k, v, o, lse, dout, B, H, N, d, m, dq, dk, dv, ws, stream);
+  float* dq_acc =
+      reinterpret_cast<float*>(static_cast<char*>(ws) + bwd_workspace(B, H, N, d).total);
+  const int G4 = stat_groups(N) / 4;
+  dq_prep_kernel<<<a.BH * G4, 256, 0, a.s>>>(static_cast<const bf16_t*>(o),
+                                             static_cast<const bf16_t*>(dout), lse, a.stats,
+                                             dq_acc, N, G4);
+  const int ncols = a.BH * m->Tk;
+  const int grid = 8 * plan_items_per_xcd(ncols, kColPlan);
+#define SA2_DKDV_FUSED_ARGS                                                                  \
+  static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), \
+      static_cast<const bf16_t*>(dout), a.stats, a.cols.items, m->col_idx, N, m->Tq, m->Tk,    \
+      a.sl2, a.scale, static_cast<bf16_t*>(dk), static_cast<bf16_t*>(dv), a.cols.splits,       \
+      a.cols.done, a.cols.partials, ncols, dq_acc
+  if (m->bq == 128) dkdv_pair_kernel<128, true><<<grid, 128, 0, a.s>>>(SA2_DKDV_FUSED_ARGS);
+  else dkdv_pair_kernel<64, true><<<grid, 128, 0, a.s>>>(SA2_DKDV_FUSED_ARGS);
+#undef SA2_DKDV_FUSED_ARGS
+  const size_t n4 = (size_t)a.BH * N * d / 4;
+  dq_finish_kernel<<<(unsigned)std::min<size_t>((n4 + 255) / 256, 8192), 256, 0, a.s>>>(
+      dq_acc, n4, a.scale, static_cast<bf16_t*>(dq));
+  return check_launch("dkdv_pair_kernel (fused dQ)");
 }
 
 extern "C" sa2_status sa2_attn_bwd(const void* q, const void* k, const void* v, const void* o,

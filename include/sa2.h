@@ -285,6 +285,27 @@ sa2_status sa2_attn_bwd_dkdv(const void* q, const void* k, const void* v,
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The same gradients as sa2_attn_bwd (bf16, d = 128 only), with dQ formed
+ * inside the dK/dV pass and accumulated in fp32 with atomic additions
+ * instead of by a separate pass over the row lists: the alternative to the
+ * deterministic backward, which recomputes S and dP for dQ (two more of the
+ * seven matrix products per kept pair).  The order of the atomic additions
+ * is not fixed, so dQ may differ in its last bits from call to call; dK and
+ * dV are as in sa2_attn_bwd.  The call runs three kernels: Delta, the base-2
+ * LSE and a zeroed fp32 dQ accumulator; dK, dV and dQ over the column lists;
+ * dQ scaled and rounded.  workspace: at least
+ * sa2_bwd_atomic_workspace_bytes(...) bytes (sa2_bwd_workspace_bytes plus
+ * 4 B*H*N*d for the accumulator), 256-byte aligned.  Other arguments as for
+ * sa2_attn_bwd; SA2_EUNSUPPORTED for other element types or d.
+ */
+size_t sa2_bwd_atomic_workspace_bytes(int B, int H, int N, int d);
+sa2_status sa2_attn_bwd_atomic_dq(const void* q, const void* k, const void* v,
+                                  const void* o, const float* lse, const void* dout,
+                                  int dtype, int B, int H, int N, int d,
+                                  const sa2_mask* mask, void* dq, void* dk, void* dv,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Layer-level velocity distillation (gist.science, section 2B: the student,
  * with sparse attention, is fitted to the frozen full-attention teacher by
  * the squared difference of their outputs).  At the level of one attention

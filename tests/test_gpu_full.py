@@ -148,6 +148,20 @@ def test_wan13_attention_whole_layer(wan13):
     log_parity("wan13_attention_whole_layer", w.name, heads=w.H, **worst)
 
 
+def test_wan13_atomic_dq_backward(wan13):
+    """The fused backward (dQ by fp32 atomics in the dK/dV pass) on the
+    full-size layer: dQ, dK, dV of heads 0 and H-1 against the oracle."""
+    w, ref, dev = wan13["w"], wan13["ref"], wan13["dev"]
+    q, k, v, do = (dev[t] for t in ("q", "k", "v", "do"))
+    grads = sa2.attn_bwd_atomic_dq(q, k, v, wan13["o"], wan13["lse"], do, wan13["mask"])
+    torch.cuda.synchronize()
+    bm = wan13["mask"].bitmap.cpu().numpy()
+    worst = {}
+    for h in (0, w.H - 1):
+        _worst(worst, _whole_head(w, ref, h, bm[0, h], wan13["o"], wan13["lse"], grads))
+    log_parity("wan13_atomic_dq_backward", w.name, heads=2, **worst)
+
+
 def test_wan13_gradient_invariants(wan13):
     w, dev = wan13["w"], wan13["dev"]
     dq, dk, dv = wan13["grads"]

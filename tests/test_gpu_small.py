@@ -151,6 +151,38 @@ def test_single_rule(k_frac, p):
     run_case(w, k_frac, p)
 
 
+ATOMIC_DQ = [w for w in SMALL if w.dtype == "bf16" and w.d == 128] + [
+    W.Workload("atomic_split", 1, 2, 2000, 128, 128, 64, "normal", 33, "bf16", 1.0, 0.0)]
+
+
+@pytest.mark.parametrize("w", ATOMIC_DQ, ids=[w.name for w in ATOMIC_DQ])
+def test_atomic_dq_backward(w):
+    """The fused backward (dQ by fp32 atomics inside the dK/dV pass): dQ, dK,
+    dV against the oracle; dK and dV also against the deterministic backward
+    (the same arithmetic apart from Delta's summation order)."""
+    _say(f"[atomic dQ] {w.name} B{w.B} H{w.H} N{w.N} bq{w.bq} k{w.k_frac} p{w.p}")
+    dev, ref = device_inputs(w) if w.B == 1 else _multi_batch(w)
+    q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
+    mask = sa2.build_mask(q, k, w.bq, w.bk, w.k_frac, w.p)
+    o, lse = sa2.attn_fwd(q, k, v, mask)
+    gq, gk, gv = sa2.attn_bwd_atomic_dq(q, k, v, o, lse, do, mask)
+    dq, dk, dv = sa2.attn_bwd(q, k, v, o, lse, do, mask)
+    torch.cuda.synchronize()
+    bm = mask.bitmap.cpu().numpy()
+    worst = dict(dq=0.0, dk=0.0, dv=0.0)
+    for b in range(w.B):
+        for h in range(w.H):
+            Q, K, V, dO = (ref[t][b, h] for t in ("q", "k", "v", "do"))
+            _, _, P = O.attention_dense(Q, K, V, bm[b, h], w.bq, w.bk)
+            for name, mine, want in zip(("dq", "dk", "dv"), (gq, gk, gv),
+                                        O.attention_dense_bwd(Q, K, V, dO, P)):
+                worst[name] = max(worst[name], check_grad(f64(mine[b, h]), want,
+                                                          f"atomic {w.name} b{b}h{h} {name}"))
+    for a_, b_ in ((gk, dk), (gv, dv), (gq, dq)):
+        assert float((a_.float() - b_.float()).norm() / b_.float().norm()) <= 1e-2
+    log_parity("atomic_dq", w.name, **worst)
+
+
 def test_both_rules_off_is_an_error():
     q = torch.zeros(1, 1, 128, 64, device="cuda", dtype=torch.bfloat16)
     with pytest.raises(RuntimeError, match="SA2_EINVAL"):
