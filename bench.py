@@ -47,6 +47,7 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "wan13_layer_hbm_traffic.md")
 KERNEL_SOURCES = ("block_sparse_attention_sa2_amd/csrc/sa2_attn.hip",
                   "block_sparse_attention_sa2_amd/csrc/sa2_common.h",
+                  "block_sparse_attention_sa2_amd/csrc/sa2_plan.h",
                   "block_sparse_attention_sa2_amd/build.py")   # compiler flags
 
 
