@@ -556,10 +556,16 @@ def main():
     dom = max(kernels, key=lambda st: per[st])
     name, alg, exe = kernels[dom]
     achieved = alg / (per[dom] * 1e-3) / 1e12
+    traffic = recorded_traffic(name, args.workload)
     roofline = {"bound": "mfma", "kernel": name, "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": recorded_traffic(name, args.workload),
+                "traffic": traffic,
                 "per_launch": {"algorithmic_flop": alg, "executed_flop": exe, "ms": round(per[dom], 4)}}
+    if traffic is not None:
+        # the memory side of the same launch: measured HBM bytes over its live duration
+        gbps = traffic / (per[dom] * 1e-3) / 1e9
+        roofline["traffic_GBps"] = round(gbps, 1)
+        roofline["traffic_frac_of_hbm_peak"] = round(gbps / PEAK_HBM_GBPS, 4)
     qk_bytes = 2.0 * B * H * N * d * q.element_size()
     mask_gbps = qk_bytes / (per["mask"] * 1e-3) / 1e9
     executed = sum(kernels[st][2] for st in kernels)
