@@ -21,14 +21,16 @@
 //
 // Kernels: fwd_async_kernel, dq_async_kernel and dkdv_pair_kernel serve bf16
 // and d = 128 (K/V tiles and Q/dO slices copied straight to LDS through
-// buffer resources, double-buffered).  dq_async_kernel's first workgroups
-// also write the dK/dV work plan (dkdv_plan_share): column lists longer than
-// a fair share are cut into segments whose fp32 partials the last segment
-// adds in order.  fwd_kernel, dq_kernel and dkdv_kernel, staged through
-// registers, serve fp32 inputs and d = 64 (in dkdv_kernel each wave owns a
-// 32-row slice of every listed query block and the four partial tiles are
-// summed in LDS in a fixed order).  No value is accumulated atomically: the
-// results are bitwise reproducible.
+// buffer resources, double-buffered).  They walk the mask's work plans (the
+// row plan for the forward and dQ, the column plan for dK/dV; see
+// sa2_plan.h): a list longer than a fair share is cut into segments whose
+// partial results the list's last segment combines in order.  fwd_kernel,
+// dq_kernel and dkdv_kernel, staged through registers, serve fp32 inputs and
+// d = 64 (in dkdv_kernel each wave owns a 32-row slice of every listed query
+// block and the four partial tiles are summed in LDS in a fixed order).  On
+// these paths no value is accumulated atomically, so the results are bitwise
+// reproducible; the fused variant of sa2_attn_bwd_atomic_dq is the one
+// exception (dQ added with fp32 atomics).
 #include <math.h>
 
 #include "sa2_common.h"
@@ -187,7 +189,7 @@ template <typename T, int D, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4 ? 2 : 1, 2)))
 void fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                 const int32_t* __restrict__ row_cnt, const int32_t* __restrict__ row_idx,
-                const int32_t* __restrict__ order, int N, int Tq, int Tk, float scale_log2,
+                int N, int Tq, int Tk, float scale_log2,
                 T* __restrict__ o, float* __restrict__ lse) {
   constexpr int NT = NW * 64;
   using KT = Tile<D, kRows>;
@@ -197,8 +199,7 @@ void fwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[64 * KT::kRowElems];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[64 * VT::kRowElems];
 
-  const int wg = order ? order[blockIdx.x] : xcd_remap(blockIdx.x, gridDim.x);
-  if ((unsigned)wg >= gridDim.x) return;   // a malformed work order
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = wg / Tq, qi = wg % Tq;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
@@ -792,7 +793,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                  const T* __restrict__ dout, const float* __restrict__ stats,
                  const int32_t* __restrict__ col_cnt,
-                 const int32_t* __restrict__ col_idx, const int32_t* __restrict__ order, int N,
+                 const int32_t* __restrict__ col_idx, int N,
                  int Tq, int Tk, float scale_log2, float scale, T* __restrict__ dk,
                  T* __restrict__ dv) {
   constexpr int NT = 256;
@@ -815,8 +816,7 @@ void dkdv_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
   uint16_t* v_lds = k_lds + 64 * KT::kRowElems;
   uint16_t* slices = v_lds + 64 * KT::kRowElems;               // [pair][Q | dO][32 rows]
 
-  const int wg = order ? order[blockIdx.x] : xcd_remap(blockIdx.x, gridDim.x);
-  if ((unsigned)wg >= gridDim.x) return;   // a malformed work order
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = wg / Tk, kj = wg % Tk;
   const int key0 = kj * 64;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -1307,7 +1307,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4
 void dq_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                const T* __restrict__ o, const T* __restrict__ dout, const float* __restrict__ lse,
                float* __restrict__ stats, const int32_t* __restrict__ row_cnt,
-               const int32_t* __restrict__ row_idx, const int32_t* __restrict__ order, int N,
+               const int32_t* __restrict__ row_idx, int N,
                int Tq, int Tk, float scale_log2, float scale, T* __restrict__ dq) {
   constexpr int NT = NW * 64;
   using KT = Tile<D, kPad16>;  // K: fragment and transposed reads
@@ -1317,8 +1317,7 @@ void dq_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __rest
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[64 * KT::kRowElems];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[64 * VT::kRowElems];
 
-  const int wg = order ? order[blockIdx.x] : xcd_remap(blockIdx.x, gridDim.x);
-  if ((unsigned)wg >= gridDim.x) return;   // a malformed work order
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = wg / Tq, qi = wg % Tq;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
@@ -1460,7 +1459,7 @@ static void launch_fwd(const void* q, const void* k, const void* v, const sa2_ma
                        int N, float sl2, void* o, float* lse, hipStream_t s) {
   fwd_kernel<T, D, NW><<<BH * m->Tq, NW * 64, 0, s>>>(
       static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), m->row_cnt,
-      m->row_idx, nullptr, N, m->Tq, m->Tk, sl2, static_cast<T*>(o), lse);
+      m->row_idx, N, m->Tq, m->Tk, sl2, static_cast<T*>(o), lse);
 }
 
 template <int NW>
@@ -1520,7 +1519,7 @@ static void launch_dq(const BwdArgs& a) {
   static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),          \
       static_cast<const T*>(a.o), static_cast<const T*>(a.dout), a.lse, a.stats,              \
       m->row_cnt,                                                                             \
-      m->row_idx, nullptr, a.N, m->Tq, m->Tk, a.sl2, a.scale, static_cast<T*>(a.dq)
+      m->row_idx, a.N, m->Tq, m->Tk, a.sl2, a.scale, static_cast<T*>(a.dq)
   if (m->bq == 128) dq_kernel<T, D, 4><<<a.BH * m->Tq, 256, 0, a.s>>>(SA2_DQ_ARGS);
   else dq_kernel<T, D, 2><<<a.BH * m->Tq, 128, 0, a.s>>>(SA2_DQ_ARGS);
 #undef SA2_DQ_ARGS
@@ -1545,7 +1544,7 @@ static void launch_dkdv(const BwdArgs& a) {
   }
 #define SA2_DKDV_ARGS                                                                         \
   static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),          \
-      static_cast<const T*>(a.dout), a.stats, m->col_cnt, m->col_idx, nullptr, a.N,          \
+      static_cast<const T*>(a.dout), a.stats, m->col_cnt, m->col_idx, a.N,          \
       m->Tq, m->Tk, a.sl2, a.scale, static_cast<T*>(a.dk), static_cast<T*>(a.dv)
   if (m->bq == 128) dkdv_kernel<T, D, 128><<<a.BH * m->Tk, 256, 0, a.s>>>(SA2_DKDV_ARGS);
   else dkdv_kernel<T, D, 64><<<a.BH * m->Tk, 256, 0, a.s>>>(SA2_DKDV_ARGS);

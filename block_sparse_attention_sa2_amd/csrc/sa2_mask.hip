@@ -512,17 +512,9 @@ void columns_kernel(const uint8_t* __restrict__ bitmap, int Tq, int Tk,
 }
 
 // ---------------------------------------------------------------------------
-// Work orders.  Workgroup slot i of an attention kernel runs on XCD i % 8.
-// XCD x takes the contiguous share of the natural (b, h, block) order that
-// the fixed XCD-aware mapping (xcd_remap) gives it, so that its L2 sees the
-// inputs of a narrow band of heads; within that share its slots are filled
-// by decreasing list length, so that each XCD starts its longest lists first.
-// One workgroup per (order, XCD) counts, scans and places in LDS; the order
-// among equal counts is whatever the LDS atomics give (it affects scheduling
-// only).
-// ---------------------------------------------------------------------------
 // The mask's work plans (see sa2_plan.h), one workgroup per XCD share and
 // kind of list: workgroups 0..7 the row plan, 8..15 the column plan.
+// ---------------------------------------------------------------------------
 constexpr int kPlanThreads = 1024;
 
 __global__ __launch_bounds__(kPlanThreads)

@@ -187,7 +187,7 @@ static __device__ void plan_share(int x, const int32_t* __restrict__ cnt, int n,
   auto bucket = [](int ln) { return min(ln, kPlanBuckets - 1); };
 
   // histogram of segment lengths, then first position of each bucket in
-  // descending order (as in the mask's work orders)
+  // descending order (longest first)
   for (int j = tid; j < len; j += nt) {
     const int ln = list_len(cnt[c0 + j], cap), ns = nseg(ln);
     for (int s2 = 0; s2 < ns; ++s2) {
