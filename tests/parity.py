@@ -1,6 +1,6 @@
 """Helpers for the GPU-vs-oracle parity tests (imported by the gpu tests).
 
-Tolerances (from the statement of the problem this build answers):
+Tolerances:
   mask   bit-exact, except blocks whose pooled score lies within 1e-6 of
          the row's selection threshold (the score of the row's last kept
          block), and rows whose cumulative mass at the Top-p cut lies within
