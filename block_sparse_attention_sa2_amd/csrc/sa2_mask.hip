@@ -214,10 +214,37 @@ __device__ inline void in_lane_stage(uint64_t* key, uint32_t* idx, int lane, int
     if ((e & J) == 0) cx(key[e], idx[e], key[e + J], idx[e + J], ((lane * E + e) & kk) == 0);
 }
 
+// One network stage (block size KK, partner distance JJ entries), its
+// lane distance and direction known at compile time.
+template <int E, int KK, int JJ>
+__device__ inline void net_stage(uint64_t* key, uint32_t* idx, int lane) {
+  if constexpr (JJ >= E) {
+    cross_lane_stage<E, JJ / E>(key, idx, lane, KK);
+  } else {
+    in_lane_stage<E, JJ>(key, idx, lane, KK);
+  }
+}
+// The merge of blocks of KK entries (distances KK/2 .. JJ_MIN), then the
+// next block size up to KMAX, all unrolled.
+template <int E, int KK, int JJ, int KMAX>
+__device__ inline void net_from(uint64_t* key, uint32_t* idx, int lane) {
+  net_stage<E, KK, JJ>(key, idx, lane);
+  if constexpr (JJ > 1) {
+    net_from<E, KK, JJ / 2, KMAX>(key, idx, lane);
+  } else if constexpr (KK < KMAX) {
+    net_from<E, 2 * KK, KK, KMAX>(key, idx, lane);
+  }
+}
+
 // Bitonic network over a wave's 64E entries (entry E*lane + e in register e)
-// into ranking order.
+// into ranking order; unrolled up to 8 entries per lane, a loop over the
+// stages beyond (where unrolling costs occupancy).
 template <int E>
 __device__ inline void sort_wave(uint64_t* key, uint32_t* idx, int lane) {
+  if constexpr (E <= 8) {
+    net_from<E, 2, 1, 64 * E>(key, idx, lane);
+    return;
+  }
   for (int kk = 2; kk <= 64 * E; kk <<= 1) {
     for (int jj = kk >> 1; jj > 0; jj >>= 1) {
       if (jj >= E) {
@@ -241,9 +268,14 @@ __device__ inline void sort_wave(uint64_t* key, uint32_t* idx, int lane) {
   }
 }
 
-// A lane's E entries among themselves into ranking order.
+// A lane's E entries among themselves into ranking order (unrolled up to 8
+// entries, a loop over the stages beyond).
 template <int E>
 __device__ inline void sort_lane(uint64_t* key, uint32_t* idx) {
+  if constexpr (E <= 8) {
+    if constexpr (E >= 2) net_from<E, 2, 1, E>(key, idx, 0);
+    return;
+  }
   for (int kk = 2; kk <= E; kk <<= 1) {
     for (int jj = kk >> 1; jj > 0; jj >>= 1) {
       if constexpr (E >= 2) if (jj == 1) in_lane_stage<E, 1>(key, idx, 0, kk);
