@@ -515,7 +515,8 @@ void select_wave_kernel(const double* __restrict__ sbar, int nrows, int Tk, int 
 // ---------------------------------------------------------------------------
 // columns: workgroup per (b*h, 16 key blocks); thread (part, column) counts
 // its sixteenth of the query-block rows, then writes its entries at the
-// prefix of the parts before it, so each list comes out ascending.
+// prefix of the parts before it, so each list comes out ascending.  Up to
+// 64 rows per part the bitmap is read once (a bit mask in a register).
 // ---------------------------------------------------------------------------
 constexpr int kColsPerGroup = 16, kColParts = 256 / kColsPerGroup;
 
@@ -529,17 +530,35 @@ void columns_kernel(const uint8_t* __restrict__ bitmap, int Tq, int Tk,
   const int per = (Tq + kColParts - 1) / kColParts;
   const int i_lo = part * per, i_hi = min(Tq, i_lo + per);
   const uint8_t* bm = bitmap + (size_t)bh * Tq * Tk;
+  // up to 64 rows per part (Tq <= 1024): the part's flags are read once
+  // into a bit mask, counted, and walked for the writes
+  const bool in_regs = per <= 64;
+  uint64_t flags = 0;
   int n = 0;
-  if (j < Tk)
-    for (int i = i_lo; i < i_hi; ++i) n += bm[(size_t)i * Tk + j];
+  if (j < Tk) {
+    if (in_regs) {
+      for (int i = i_lo; i < i_hi; ++i)
+        flags |= (uint64_t)(bm[(size_t)i * Tk + j] != 0) << (i - i_lo);
+      n = __popcll(flags);
+    } else {
+      for (int i = i_lo; i < i_hi; ++i) n += bm[(size_t)i * Tk + j];
+    }
+  }
   cnt[part][c] = n;
   __syncthreads();
   if (j >= Tk) return;
   int off = 0;
   for (int q = 0; q < part; ++q) off += cnt[q][c];
   int32_t* out = col_idx + ((size_t)bh * Tk + j) * Tq;
-  for (int i = i_lo; i < i_hi; ++i)
-    if (bm[(size_t)i * Tk + j]) out[off++] = i;
+  if (in_regs) {
+    while (flags) {
+      out[off++] = i_lo + __ffsll((long long)flags) - 1;
+      flags &= flags - 1;
+    }
+  } else {
+    for (int i = i_lo; i < i_hi; ++i)
+      if (bm[(size_t)i * Tk + j]) out[off++] = i;
+  }
   if (part == kColParts - 1) col_cnt[(size_t)bh * Tk + j] = off;
 }
 
