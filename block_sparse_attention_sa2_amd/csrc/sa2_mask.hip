@@ -252,11 +252,15 @@ __device__ inline void net_stage(uint64_t* key, uint32_t* idx, int lane) {
     in_lane_stage<E, JJ>(key, idx, lane, KK);
   }
 }
-// The merge of blocks of KK entries (distances KK/2 .. JJ_MIN), then the
-// next block size up to KMAX, all unrolled.
+// The merge of blocks of KK entries (distances KK/2 .. 1), then the next
+// block size up to KMAX, all unrolled.  Networks of more than 8 entries per
+// lane are fenced stage by stage: scheduled across stages they held more
+// registers (the 32-entry lane sort of the long-row kernel: 387 against 182
+// VGPRs) and ran slower than the loop they replace.
 template <int E, int KK, int JJ, int KMAX>
 __device__ inline void net_from(uint64_t* key, uint32_t* idx, int lane) {
   net_stage<E, KK, JJ>(key, idx, lane);
+  if constexpr (E > 8) __builtin_amdgcn_sched_barrier(0);   // stage by stage, as a loop would
   if constexpr (JJ > 1) {
     net_from<E, KK, JJ / 2, KMAX>(key, idx, lane);
   } else if constexpr (KK < KMAX) {
@@ -296,11 +300,11 @@ __device__ inline void sort_wave(uint64_t* key, uint32_t* idx, int lane) {
   }
 }
 
-// A lane's E entries among themselves into ranking order (unrolled up to 8
+// A lane's E entries among themselves into ranking order (unrolled up to 32
 // entries, a loop over the stages beyond).
 template <int E>
 __device__ inline void sort_lane(uint64_t* key, uint32_t* idx) {
-  if constexpr (E <= 8) {
+  if constexpr (E <= 32) {
     if constexpr (E >= 2) net_from<E, 2, 1, E>(key, idx, 0);
     return;
   }
