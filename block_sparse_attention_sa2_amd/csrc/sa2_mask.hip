@@ -81,23 +81,26 @@ void pool_kernel(const T* __restrict__ q, const T* __restrict__ k, int BH, int N
 // i + 16k, B[k][j] from lane j + 16k, and D[i][j] lands in element i / 4 of
 // lane j + 16 (i % 4).  One workgroup of four waves per 64 x 64 tile of
 // S-bar, each wave a 32 x 32 sub-tile (four independent 16 x 16
-// accumulators); q-bar and k-bar rows are staged in LDS, d in chunks of 64,
-// rows padded by 16 bytes so that the 16 rows a read instruction touches fall
-// in distinct banks.  For MFMA pair (2u, 2u + 1) lane l holds d indices
+// accumulators); q-bar and k-bar rows go through two LDS buffers, d in
+// chunks of 32, the next chunk's loads in flight while a chunk's products
+// run, rows padded by 16 bytes so that the 16 rows a read instruction touches
+// fall in distinct banks.  For MFMA pair (2u, 2u + 1) lane l holds d indices
 // 8u + 2(l / 16) and the next one, so each product is a fp64 sum over d in a
 // fixed order.  A one-wave 16 x 32 version reading its operands from L2 was
-// 12% slower at the 14B-shaped layer (312 against 273 us).
+// 12% slower at the 14B-shaped layer (312 against 273 us), and one LDS
+// buffer of 64-index chunks 5% slower again in the whole mask build.
 // ---------------------------------------------------------------------------
 typedef double f64x2 __attribute__((ext_vector_type(2)));
 typedef double f64x4 __attribute__((ext_vector_type(4)));
-constexpr int kScoreTile = 64, kScoreChunk = 64;
+constexpr int kScoreTile = 64, kScoreChunk = 32;
 constexpr int kScoreRow = kScoreChunk + 2;   // doubles per LDS row (16 bytes of padding)
+constexpr int kScoreStage = kScoreTile * kScoreChunk / 2 / 256;   // f64x2 per thread and tensor
 
 __global__ __launch_bounds__(256)
 void score_tile_kernel(const double* __restrict__ qbar, const double* __restrict__ kbar, int Tq,
                        int Tk, int d, double sqrt_d, double* __restrict__ sbar) {
-  __shared__ __attribute__((aligned(16))) double qs[kScoreTile * kScoreRow];
-  __shared__ __attribute__((aligned(16))) double ks[kScoreTile * kScoreRow];
+  __shared__ __attribute__((aligned(16))) double qs[2][kScoreTile * kScoreRow];
+  __shared__ __attribute__((aligned(16))) double ks[2][kScoreTile * kScoreRow];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int bh = blockIdx.y;
   const int tk = (Tk + kScoreTile - 1) / kScoreTile;
@@ -111,27 +114,51 @@ void score_tile_kernel(const double* __restrict__ qbar, const double* __restrict
     for (int b = 0; b < 2; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
   const double* qh = qbar + (size_t)bh * Tq * d;
   const double* kh = kbar + (size_t)bh * Tk * d;
-  for (int c0 = 0; c0 < d; c0 += kScoreChunk) {
-    const int dc = min(kScoreChunk, d - c0);   // a multiple of 8
-    // stage rows i0.. and j0.. (past the end: the last row), 16 bytes a thread
-    const int per_row = dc / 2;
-    for (int x = tid; x < kScoreTile * per_row; x += 256) {
-      const int row = x / per_row, c = (x % per_row) * 2;
-      const int qi = min(i0 + row, Tq - 1), kj = min(j0 + row, Tk - 1);
-      *reinterpret_cast<f64x2*>(qs + row * kScoreRow + c) =
-          *reinterpret_cast<const f64x2*>(qh + (size_t)qi * d + c0 + c);
-      *reinterpret_cast<f64x2*>(ks + row * kScoreRow + c) =
-          *reinterpret_cast<const f64x2*>(kh + (size_t)kj * d + c0 + c);
+  // a chunk of 32 d indices (the last one possibly 8, 16 or 24) of rows i0..
+  // and j0.. (past the end: the last row), 16 bytes per thread and step
+  f64x2 rq[kScoreStage], rk[kScoreStage];
+  auto load = [&](int c0) {
+    const int dc = min(kScoreChunk, d - c0), per_row = dc / 2;
+#pragma unroll
+    for (int t = 0; t < kScoreStage; ++t) {
+      const int x = tid + 256 * t;
+      if (x < kScoreTile * per_row) {
+        const int row = x / per_row, c = (x % per_row) * 2;
+        rq[t] = *reinterpret_cast<const f64x2*>(qh + (size_t)min(i0 + row, Tq - 1) * d + c0 + c);
+        rk[t] = *reinterpret_cast<const f64x2*>(kh + (size_t)min(j0 + row, Tk - 1) * d + c0 + c);
+      }
     }
-    __syncthreads();
+  };
+  auto store = [&](int c0, int buf) {
+    const int dc = min(kScoreChunk, d - c0), per_row = dc / 2;
+#pragma unroll
+    for (int t = 0; t < kScoreStage; ++t) {
+      const int x = tid + 256 * t;
+      if (x < kScoreTile * per_row) {
+        const int row = x / per_row, c = (x % per_row) * 2;
+        *reinterpret_cast<f64x2*>(&qs[buf][row * kScoreRow + c]) = rq[t];
+        *reinterpret_cast<f64x2*>(&ks[buf][row * kScoreRow + c]) = rk[t];
+      }
+    }
+  };
+  load(0);
+  store(0, 0);
+  __syncthreads();
+  int buf = 0;
+  for (int c0 = 0; c0 < d; c0 += kScoreChunk) {
+    const bool more = c0 + kScoreChunk < d;
+    if (more) load(c0 + kScoreChunk);   // in flight while this chunk's products run
+    const int dc = min(kScoreChunk, d - c0);
+    const double* qb = qs[buf];
+    const double* kb = ks[buf];
     for (int u = 0; u < dc / 8; ++u) {
       f64x2 av[2], bv[2];
 #pragma unroll
       for (int a = 0; a < 2; ++a)
-        av[a] = *reinterpret_cast<const f64x2*>(qs + (wi + 16 * a + r) * kScoreRow + 8 * u + 2 * g);
+        av[a] = *reinterpret_cast<const f64x2*>(qb + (wi + 16 * a + r) * kScoreRow + 8 * u + 2 * g);
 #pragma unroll
       for (int b = 0; b < 2; ++b)
-        bv[b] = *reinterpret_cast<const f64x2*>(ks + (wj + 16 * b + r) * kScoreRow + 8 * u + 2 * g);
+        bv[b] = *reinterpret_cast<const f64x2*>(kb + (wj + 16 * b + r) * kScoreRow + 8 * u + 2 * g);
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -140,7 +167,9 @@ void score_tile_kernel(const double* __restrict__ qbar, const double* __restrict
           for (int b = 0; b < 2; ++b)
             acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a][h], bv[b][h], acc[a][b], 0, 0, 0);
     }
+    if (more) store(c0 + kScoreChunk, buf ^ 1);   // the other buffer: read a chunk ago, before the barrier
     __syncthreads();
+    buf ^= 1;
   }
   // element e of lane l: row 4e + l / 16, column l % 16 of its 16 x 16 block
 #pragma unroll
