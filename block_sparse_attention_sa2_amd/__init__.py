@@ -22,8 +22,10 @@ from . import _lib
 from ._lib import Sa2Mask, check
 
 __all__ = ["BlockMask", "build_mask", "build_mask_noalloc", "attn_fwd", "attn_bwd", "attn_bwd_dq",
-           "attn_bwd_dkdv", "sparse_attention", "SparseAttention", "version", "mask_workspace_bytes",
-           "bwd_workspace_bytes"]
+           "attn_bwd_dkdv", "attn_bwd_atomic_dq", "sparse_attention", "SparseAttention",
+           "distill_loss_grad", "distill_step", "version", "mask_workspace_bytes",
+           "fwd_workspace_bytes", "bwd_workspace_bytes", "bwd_atomic_workspace_bytes",
+           "distill_workspace_bytes"]
 
 _DTYPES = {torch.bfloat16: _lib.SA2_BF16, torch.float32: _lib.SA2_F32}
 
