@@ -625,7 +625,8 @@ void columns_kernel(const uint8_t* __restrict__ bitmap, int Tq, int Tk,
 
 // ---------------------------------------------------------------------------
 // The mask's work plans (see sa2_plan.h), one workgroup per XCD share and
-// kind of list: workgroups 0..7 the row plan, 8..15 the column plan.
+// kind of list: workgroups 0..7 the row plan, 8..15 the column plan (in a
+// group planned head by head, the group's first workgroup plans all four).
 // ---------------------------------------------------------------------------
 constexpr int kPlanThreads = 1024;
 
@@ -644,7 +645,7 @@ void plan_kernel(const int32_t* __restrict__ row_cnt, int nrows, int Tk,
   const int n = rows ? nrows : ncols, ndone = rows ? kRowCounters : kColCounters;
   const PlanLayout l = plan_layout(n, kd, ndone);
   char* b = reinterpret_cast<char*>(rows ? row_plan : col_plan);
-  plan_share(x, rows ? row_cnt : col_cnt, n, rows ? Tk : Tq, kd,
+  plan_share(x, rows ? row_cnt : col_cnt, n, rows ? Tk : Tq, rows ? Tq : Tk, kd,
              reinterpret_cast<int4*>(b + l.items), reinterpret_cast<int4*>(b + l.splits),
              reinterpret_cast<int*>(b + l.done), ndone, hist, itot, red, ctr, pos);
 }

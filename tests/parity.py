@@ -126,15 +126,64 @@ def _equal_count_shares(n: int):
     return [(x * q + min(x, r), q + (1 if x < r else 0)) for x in range(8)]
 
 
-def check_plan(cnt, plan, kd: dict, cap: int) -> int:
+def _cut(c: int, L: int):
+    """Segments of a list of c entries cut at L: nearly equal, in order."""
+    ns = -(-c // L) if c > L else 1
+    base, rem = divmod(c, ns)
+    return [(s * base + min(s, rem), base + (1 if s < rem else 0)) for s in range(ns)]
+
+
+def _check_items(cnt, lists, items, L, splits, ebase, ecap, slot_owner, what) -> int:
+    """Items of `lists` (each list exactly once, as one item or as nearly equal
+    segments of at most L entries) with split entries in [ebase, ebase + ecap)
+    and partial slots in [2 ebase, 2 (ebase + ecap)).  Returns the split lists."""
+    per_list: dict[int, list] = {}
+    for it in items:
+        per_list.setdefault(int(it[0]), []).append(tuple(int(v) for v in it))
+    assert sorted(per_list) == [int(v) for v in lists], f"{what}: lists of the items"
+    nsplit = 0
+    for lst in lists:
+        its_l = sorted(per_list[int(lst)], key=lambda t: t[1])
+        c = int(cnt[lst])
+        if c <= L:
+            assert len(its_l) == 1 and its_l[0] == (lst, 0, c, -1), f"list {lst}: {its_l}"
+            continue
+        nsplit += 1
+        want = _cut(c, L)
+        ns = len(want)
+        assert [(t[1], t[2]) for t in its_l] == want, f"list {lst}: segments {its_l}"
+        entries = {t[3] >> 10 for t in its_l}
+        assert len(entries) == 1, f"list {lst}: several split entries"
+        e = entries.pop()
+        assert ebase <= e < ebase + ecap, f"list {lst}: split entry outside its share"
+        sp = splits[e]
+        assert sp[0] == lst and sp[2] == ns, f"list {lst}: split entry {sp}"
+        assert sorted(t[3] & 1023 for t in its_l) == list(range(ns))
+        assert 2 * ebase <= sp[1] and sp[1] + ns <= 2 * (ebase + ecap), f"list {lst}: slots"
+        for slot in range(sp[1], sp[1] + ns):
+            assert slot not in slot_owner, f"slot {slot} shared"
+            slot_owner[slot] = lst
+    return nsplit
+
+
+def check_plan(cnt, plan, kd: dict, cap: int, per_head: int, head_major_out=None) -> int:
     """A work plan (the int32 array the mask builder wrote) against the list
-    counts it was made from: every list is covered by its items in order, as
-    one item or as nearly equal segments; a list is cut exactly when it is
-    longer than L = max(min_segment, fair * ceil(total / slots),
-    ceil(share / extra)) of its XCD share, into ceil(n / L) segments; XCD x's
-    items are the x-th contiguous share of the lists, longest first; each
-    split owns partial slots inside its share's range; every completion
-    counter is zero.  Returns the number of split lists."""
+    counts it was made from (per_head consecutive lists per (batch, head)).
+
+    Every list is covered by its items, as one item or as nearly equal
+    segments; XCD x holds a contiguous share of the lists, and XCDs 4g..4g+3
+    form group g, whose share is the union of theirs.  A group is head-major
+    when 4 x its longest item (its lists cut at Lg = max(L0, ceil(group
+    entries / (4 extra)))) x slots / 2 is at most the group's cost (entries +
+    lists), L0 = max(min_segment, fair * ceil(total / slots)): then the
+    group's items, in rank order k, sit at slot 8 (k // 4) + 4g + k % 4,
+    ordered by (batch, head) and longest first within each head (in the
+    shared length ranks of the plan: 4096 // heads per head), with split
+    entries and partial slots in the group's range.  Otherwise each XCD's
+    items are its share longest first, cut at max(L0, ceil(share / extra)),
+    with entries and slots in the XCD's range.  Every completion counter is
+    zero.  Returns the number of split lists; appends each group's head-major
+    decision to `head_major_out` when given."""
     cnt = np.clip(np.asarray(cnt).reshape(-1).astype(np.int64), 0, cap)
     n, ex = cnt.size, kd["extra"]
     J = _items_per_xcd(n, kd)
@@ -144,64 +193,88 @@ def check_plan(cnt, plan, kd: dict, cap: int) -> int:
     done = buf[8 * J * 4 + 8 * ex * 4:8 * J * 4 + 8 * ex * 4 + kd["counters"] * 8 * ex]
     assert np.all(done == 0), "completion counters not zero"
     total = int(cnt.sum())
+    L0 = max(kd["min_segment"], kd["fair"] * -(-total // kd["slots"]))
     costs = [int((cnt[a:a + ln] + 1).sum()) for a, ln in _equal_count_shares(n)]
     balanced = kd["imbalance"] == 0 or max(costs) * 800 > sum(costs) * (800 + 8 * kd["imbalance"])
-    per_list: dict[int, list] = {}
-    lo = 0
-    nsplit = 0
-    slot_owner = {}
+    cols = []
     for x in range(8):
         its = items[:, x, :]
         k = int(np.count_nonzero(its[:, 0] >= 0))
         assert np.all(its[:k, 0] >= 0) and np.all(its[k:, 0] == -1), f"XCD {x}: gaps in items"
-        valid = its[:k]
-        keys = np.minimum(valid[:, 2], 4095)
-        assert np.all(np.diff(keys) <= 0), f"XCD {x}: not longest first"
-        lists = np.unique(valid[:, 0])
-        if lists.size:
-            assert lists[0] == lo and lists[-1] == lo + lists.size - 1, f"XCD {x}: share not contiguous"
+        cols.append(its[:k])
+    lo, nsplit, slot_owner = 0, 0, {}
+    for g in range(2):
+        gcols = cols[4 * g:4 * g + 4]
+        glists = np.unique(np.concatenate([c[:, 0] for c in gcols])) if any(len(c) for c in gcols) \
+            else np.zeros(0, np.int64)
+        if glists.size:
+            assert glists[0] == lo and glists[-1] == lo + glists.size - 1, f"group {g}: not contiguous"
         if not balanced:
-            assert lists.size == _equal_count_shares(n)[x][1], f"XCD {x}: share size"
-        lo += lists.size
-        share = int(cnt[lists].sum()) if lists.size else 0
-        L = max(kd["min_segment"], kd["fair"] * -(-total // kd["slots"]), -(-share // ex))
-        for it in valid:
-            per_list.setdefault(int(it[0]), []).append(tuple(int(v) for v in it))
-        for lst in lists:
-            its_l = sorted(per_list[int(lst)], key=lambda t: t[1])
-            c = int(cnt[lst])
-            if c <= L:
-                assert len(its_l) == 1 and its_l[0] == (lst, 0, c, -1), f"list {lst}: {its_l}"
-                continue
-            nsplit += 1
-            ns = -(-c // L)
-            assert len(its_l) == ns, f"list {lst}: {len(its_l)} segments, expected {ns}"
-            entries = {t[3] >> 10 for t in its_l}
-            assert len(entries) == 1, f"list {lst}: several split entries"
-            e = entries.pop()
-            assert e // ex == x, f"list {lst}: split entry outside its share"
-            sp = splits[e]
-            assert sp[0] == lst and sp[2] == ns, f"list {lst}: split entry {sp}"
-            assert sorted(t[3] & 1023 for t in its_l) == list(range(ns))
-            assert its_l[0][1] == 0 and its_l[-1][1] + its_l[-1][2] == c
-            for a, b in zip(its_l, its_l[1:]):
-                assert a[1] + a[2] == b[1], f"list {lst}: segments not contiguous"
-            sl = [t[2] for t in its_l]
-            assert max(sl) - min(sl) <= 1, f"list {lst}: segments {sl}"
-            assert 2 * ex * x <= sp[1] and sp[1] + ns <= 2 * ex * (x + 1), f"list {lst}: slots"
-            for slot in range(sp[1], sp[1] + ns):
-                assert slot not in slot_owner, f"slot {slot} shared"
-                slot_owner[slot] = lst
-    assert lo == n and sorted(per_list) == list(range(n)), "lists missing from the plan"
+            want = sum(_equal_count_shares(n)[x][1] for x in range(4 * g, 4 * g + 4))
+            assert glists.size == want, f"group {g}: share size"
+        G0, G1 = lo, lo + glists.size
+        lo = G1
+        gshare = int(cnt[G0:G1].sum())
+        Lg = max(L0, -(-gshare // (4 * ex)))
+        glong = int(cnt[G0:G1].max()) if G1 > G0 else 0
+        gseg = max((s for _, s in _cut(glong, Lg)), default=0)
+        head_major = G1 > G0 and 4 * gseg * (kd["slots"] // 2) <= gshare + (G1 - G0)
+        if head_major_out is not None:
+            head_major_out.append(bool(head_major))
+        if head_major:
+            nitems = sum(len(c) for c in gcols)
+            for r in range(4):
+                assert len(gcols[r]) == (-(-(nitems - r) // 4) if nitems > r else 0), \
+                    f"group {g}: items not dealt in turn"
+            order = np.array([gcols[k % 4][k // 4] for k in range(nitems)]).reshape(-1, 4)
+            heads = order[:, 0] // per_head
+            h0 = G0 // per_head
+            nh = (G1 - 1) // per_head - h0 + 1
+            nb = 4096 // nh if nh <= 4096 else 1
+            hb = heads - h0 if nh <= 4096 else (heads - h0) * 4096 // nh
+            lr = nb - 1 - np.minimum(nb - 1, order[:, 2] * nb // (gseg + 1))
+            rank = hb * nb + lr
+            assert np.all(np.diff(rank) >= 0), f"group {g}: not head by head, longest first"
+            assert np.all(np.diff(heads) >= 0), f"group {g}: heads out of order"
+            if nb > gseg:
+                same = heads[1:] == heads[:-1]
+                assert np.all(np.diff(order[:, 2])[same] <= 0), f"group {g}: not longest first"
+            nsplit += _check_items(cnt, glists, order, Lg, splits, 4 * ex * g, 4 * ex,
+                                   slot_owner, f"group {g}")
+            continue
+        xlo = G0
+        for x in range(4 * g, 4 * g + 4):
+            valid = cols[x]
+            keys = np.minimum(valid[:, 2], 4095)
+            assert np.all(np.diff(keys) <= 0), f"XCD {x}: not longest first"
+            lists = np.unique(valid[:, 0])
+            if lists.size:
+                assert lists[0] == xlo and lists[-1] == xlo + lists.size - 1, \
+                    f"XCD {x}: share not contiguous"
+            if not balanced:
+                assert lists.size == _equal_count_shares(n)[x][1], f"XCD {x}: share size"
+            xlo += lists.size
+            share = int(cnt[lists].sum()) if lists.size else 0
+            L = max(L0, -(-share // ex))
+            nsplit += _check_items(cnt, lists, valid, L, splits, ex * x, ex, slot_owner,
+                                   f"XCD {x}")
+        assert xlo == G1
+    assert lo == n, "lists missing from the plan"
     return nsplit
 
 
-def check_plans(mask) -> tuple[int, int]:
-    """Both plans of a BlockMask; returns (split rows, split columns)."""
-    return (check_plan(mask.row_cnt.cpu().numpy(), mask.row_plan.cpu().numpy(), ROW_PLAN,
-                       mask.Tk),
-            check_plan(mask.col_cnt.cpu().numpy(), mask.col_plan.cpu().numpy(), COL_PLAN,
-                       mask.Tq))
+def check_plans(mask, head_major: dict | None = None) -> tuple[int, int]:
+    """Both plans of a BlockMask; returns (split rows, split columns) and,
+    when `head_major` is a dict, sets its "rows" and "cols" entries to the
+    two groups' head-major decisions."""
+    hr, hc = [], []
+    out = (check_plan(mask.row_cnt.cpu().numpy(), mask.row_plan.cpu().numpy(), ROW_PLAN,
+                      mask.Tk, mask.Tq, hr),
+           check_plan(mask.col_cnt.cpu().numpy(), mask.col_plan.cpu().numpy(), COL_PLAN,
+                      mask.Tq, mask.Tk, hc))
+    if head_major is not None:
+        head_major.update(rows=hr, cols=hc)
+    return out
 
 
 def rel_fro(a: np.ndarray, b: np.ndarray) -> float:

@@ -127,7 +127,11 @@ def wan13(request):
 
 def test_wan13_mask_all_heads(wan13):
     w, mask, ref = wan13["w"], wan13["mask"], wan13["ref"]
-    check_plans(mask)
+    hm = {}
+    check_plans(mask, hm)
+    # rows are short against a slot's load: planned head by head; the
+    # longest columns are as long as a slot's whole load: longest first
+    assert hm == {"rows": [True, True], "cols": [False, False]}, hm
     _mask_all_heads("wan13_mask_all_heads", w, mask, ref, wan13["k_frac"], wan13["p"],
                     range(w.H))
     dens = mask.density()
@@ -208,8 +212,12 @@ def test_wan14_heads_against_the_oracle(wan14):
 def test_wan14_union_every_head(wan14):
     """On all 40 heads: the hybrid mask contains the library's Top-k-only and
     Top-p-only masks and equals their union (gist.science 2A), and every row
-    keeps at least kc blocks."""
+    keeps at least kc blocks.  Both work plans check out against the counts,
+    and both are planned head by head."""
     w, mask, dev = wan14["w"], wan14["mask"], wan14["dev"]
+    hm = {}
+    check_plans(mask, hm)
+    assert hm == {"rows": [True, True], "cols": [True, True]}, hm
     q, k = dev["q"], dev["k"]
     hy = mask.bitmap
     ko = sa2.build_mask(q, k, w.bq, w.bk, wan14["k_frac"], 0.0).bitmap
