@@ -73,9 +73,13 @@ typedef enum { SA2_BF16 = 0, SA2_F32 = 1 } sa2_dtype;
  *            col_cnt (dK/dV).  A plan assigns the lists to workgroup slots,
  *            XCD by XCD (slot s runs on XCD s % 8; XCD x takes the x-th
  *            contiguous eighth of the lists, rows by count and columns by
- *            cost), longest first, and cuts a list much longer than the mean
- *            load of the kernel's resident workgroups into segments whose
- *            partial sums the list's last segment combines in a fixed order.
+ *            cost), longest first; where no list of a group of four XCDs'
+ *            shares is long against the group's load per workgroup, the
+ *            group's lists go head by head (longest first within a head),
+ *            dealt in turn to its four XCDs.  A list much longer than the
+ *            mean load of the kernel's resident workgroups is cut into
+ *            segments whose partial sums the list's last segment combines in
+ *            a fixed order.
  *            Each plan also holds the completion counters of the kernels
  *            that walk it (rows: forward and dQ; columns: dK/dV): the plan
  *            zeroes them and each kernel leaves them zeroed, so attention
