@@ -16,6 +16,8 @@ benchmark times (one call per step over all heads).
   hybrid mask contains the Top-k-only and Top-p-only masks on every head and
   equals their union; head 0 against the oracle in full.
 * The largest key-block count (4096) at one head.
+* Many short rows over two batch entries (B=2, H=16, N=8192): the row plan
+  goes head by head; one head per batch entry against the oracle.
 
 Mask-comparison totals (rows compared, exact rows, score near-tie blocks,
 mass near-tie rows) and the worst numeric errors are appended to the file
@@ -44,8 +46,8 @@ def _say(*a):
     sys.stdout.flush()
 
 
-def _head_np(ref, h):
-    return tuple(ref[t][0, h] for t in ("q", "k", "v", "do") if t in ref)
+def _head_np(ref, h, b=0):
+    return tuple(ref[t][b, h] for t in ("q", "k", "v", "do") if t in ref)
 
 
 def _row_lists(mask_np_bm):
@@ -56,7 +58,7 @@ def _whole_head(w, ref, h, bm_h, o, lse, grads, b=0):
     """Every element of O, LSE (and dQ, dK, dV) of head h against the oracle's
     gathered evaluation (each query block over its kept key blocks only);
     returns the worst errors."""
-    Q, K, V, dO = _head_np(ref, h)
+    Q, K, V, dO = _head_np(ref, h, b)
     rows = _row_lists(bm_h)
     if grads is None:
         Oo, L = O.attention_gathered(Q, K, V, rows, w.bq, w.bk)
@@ -235,6 +237,42 @@ def test_wan14_gradient_invariants_every_head(wan14):
     dq, dk, dv = wan14["grads"]
     for h in range(w.H):
         _invariants(dev["q"], dev["k"], dq, dk, dv, dev["do"], h)
+
+
+# ---------------------------------------------------------------------------
+# Many short rows over two batch entries: the row plan goes head by head
+# ---------------------------------------------------------------------------
+
+def test_head_major_rows_across_batches():
+    """B=2, H=16, N=8192, Top-k 4 of 128 key blocks: 2048 rows of four blocks
+    each, so both groups of the row plan are planned head by head, in (batch,
+    head) order; both plans check out against the counts, and the mask, O,
+    LSE, dQ, dK and dV of one head in each batch entry match the oracle."""
+    from dataclasses import replace
+    w = W.Workload("headmajor", 2, 16, 8192, 128, 128, 64, "normal", 41, "bf16", 4 / 128, 0.0)
+    _say(f"[head-major] generating B{w.B} H{w.H} N{w.N}")
+    dev1, ref1 = device_inputs(replace(w, B=1, H=w.B * w.H))
+    dev = {k_: t.reshape(w.B, w.H, w.N, w.d).contiguous() for k_, t in dev1.items()}
+    ref = {k_: a.reshape(w.B, w.H, w.N, w.d) for k_, a in ref1.items()}
+    q, k, v, do = (dev[t] for t in ("q", "k", "v", "do"))
+    mask = sa2.build_mask(q, k, w.bq, w.bk, w.k_frac, w.p)
+    o, lse = sa2.attn_fwd(q, k, v, mask)
+    grads = sa2.attn_bwd(q, k, v, o, lse, do, mask)
+    torch.cuda.synchronize()
+    hm = {}
+    check_plans(mask, hm)
+    assert hm["rows"] == [True, True], hm
+    assert int(mask.row_cnt.min().item()) == 4 and int(mask.row_cnt.max().item()) == 4
+    bm = mask.bitmap.cpu().numpy()
+    rc, ri = mask.row_cnt.cpu().numpy(), mask.row_idx.cpu().numpy()
+    cc, ci = mask.col_cnt.cpu().numpy(), mask.col_idx.cpu().numpy()
+    worst = {}
+    for b, h in ((0, 3), (1, 12)):
+        Q, K = ref["q"][b, h], ref["k"][b, h]
+        compare_mask(O.build_mask_head(Q, K, w.bq, w.bk, w.k_frac, w.p), bm[b, h], w.p)
+        check_lists(bm[b, h], rc[b, h], ri[b, h], cc[b, h], ci[b, h])
+        _worst(worst, _whole_head(w, ref, h, bm[b, h], o, lse, grads, b=b))
+    log_parity("head_major_rows_across_batches", w.name, heads=2, **worst)
 
 
 # ---------------------------------------------------------------------------
