@@ -15,7 +15,8 @@ benchmark times (one call per step over all heads).
   in fp64).
 * Mask-rule stress (H=8, N=16384): three score regimes x four densities; the
   hybrid mask contains the Top-k-only and Top-p-only masks on every head and
-  equals their union; head 0 against the oracle in full.
+  equals their union; the three masks of every head against the oracle's;
+  attention of head 0 against the oracle in full.
 * The largest key-block count (4096) at one head.
 * Many short rows over two batch entries (B=2, H=16, N=8192): the row plan
   goes head by head; one head per batch entry against the oracle.
@@ -320,16 +321,17 @@ def test_stress_union_and_oracle(name, stress_inputs):
     o, lse = sa2.attn_fwd(q, k, v, hy)
     grads = sa2.attn_bwd(q, k, v, o, lse, do, hy)
     torch.cuda.synchronize()
-    bm = hy_bm.cpu().numpy()
-    hm = O.build_mask_head(ref["q"][0, 0], ref["k"][0, 0], w.bq, w.bk, k_frac, p)
-    ex, ti, ma = compare_mask(hm, bm[0, 0], p)
-    log_mask_exceptions("stress_union_and_oracle", name, 1, w.Tq, ex, ti, ma)
-    # each rule on its own, as a mode of its own, against the oracle
-    ko_h = O.build_mask_head(ref["q"][0, 0], ref["k"][0, 0], w.bq, w.bk, k_frac, 0.0)
-    compare_mask(ko_h, ko.cpu().numpy()[0, 0], 0.0)
-    po_h = O.build_mask_head(ref["q"][0, 0], ref["k"][0, 0], w.bq, w.bk, 0.0, p)
-    ex, ti, ma = compare_mask(po_h, po.cpu().numpy()[0, 0], p)
-    log_mask_exceptions("stress_union_and_oracle/top-p only", name, 1, w.Tq, ex, ti, ma)
+    bm, ko_bm, po_bm = hy_bm.cpu().numpy(), ko.cpu().numpy(), po.cpu().numpy()
+    # the hybrid mask and each rule on its own, as a mode of its own, against
+    # the oracle on every head
+    for tag, kf_, p_, got in (("", k_frac, p, bm), ("/top-k only", k_frac, 0.0, ko_bm),
+                              ("/top-p only", 0.0, p, po_bm)):
+        ex = ti = ma = 0
+        for h in range(w.H):
+            hm = O.build_mask_head(ref["q"][0, h], ref["k"][0, h], w.bq, w.bk, kf_, p_)
+            e_, t_, m_ = compare_mask(hm, got[0, h], p_)
+            ex += e_; ti += t_; ma += m_
+        log_mask_exceptions("stress_union_and_oracle" + tag, name, w.H, w.H * w.Tq, ex, ti, ma)
     worst = _whole_head(w, ref, 0, bm[0, 0], o, lse, grads)
     log_parity("stress_union_and_oracle", name, heads=1, **worst)
     dens = hy.density()
