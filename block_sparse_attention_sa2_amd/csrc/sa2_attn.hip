@@ -21,16 +21,18 @@
 //
 // Kernels: fwd_async_kernel, dq_async_kernel and dkdv_pair_kernel serve bf16
 // and d = 128 (K/V tiles and Q/dO slices copied straight to LDS through
-// buffer resources, double-buffered).  They walk the mask's work plans (the
-// row plan for the forward and dQ, the column plan for dK/dV; see
-// sa2_plan.h): a list longer than a fair share is cut into segments whose
-// partial results the list's last segment combines in order.  fwd_kernel,
-// dq_kernel and dkdv_kernel, staged through registers, serve fp32 inputs and
-// d = 64 (in dkdv_kernel each wave owns a 32-row slice of every listed query
-// block and the four partial tiles are summed in LDS in a fixed order).  On
-// these paths no value is accumulated atomically, so the results are bitwise
-// reproducible; the fused variant of sa2_attn_bwd_atomic_dq is the one
-// exception (dQ added with fp32 atomics).
+// buffer resources, double-buffered); with 64-row query blocks the forward
+// and dQ run fwd_async32_kernel and dq_async32_kernel, which stage 32-key
+// tiles so that twice as many workgroups fit a CU.  They walk the mask's
+// work plans (the row plan for the forward and dQ, the column plan for
+// dK/dV; see sa2_plan.h): a list longer than a fair share is cut into
+// segments whose partial results the list's last segment combines in
+// order.  fwd_kernel, dq_kernel and dkdv_kernel, staged through registers,
+// serve fp32 inputs and d = 64 (in dkdv_kernel each wave owns a 32-row slice
+// of every listed query block and the four partial tiles are summed in LDS
+// in a fixed order).  On these paths no value is accumulated atomically, so
+// the results are bitwise reproducible; the fused variant of
+// sa2_attn_bwd_atomic_dq is the one exception (dQ added with fp32 atomics).
 #include <math.h>
 
 #include "sa2_common.h"
@@ -604,6 +606,208 @@ void fwd_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
   if (tid == 0) done[entry] = 0;   // ready for the next call
 }
 
+// Forward for 64-row query blocks (two waves) with 32-key tiles: K and V
+// double-buffered in 32 KB of LDS, so that four workgroups share a CU and
+// each SIMD runs two waves (the 64-key tiles of fwd_async_kernel allow two
+// such workgroups per CU, one wave per SIMD): 1.3B layer with 64 x 64
+// blocks, 0.515 -> 0.433 ms.  Each list entry (a 64-key block) is walked as
+// two 32-key steps.  With four-wave workgroups the same tiles gain 1.5% on
+// the benchmark masks and lose 6% on a sink mask, so 128-row blocks keep the
+// 64-key kernel.
+template <int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 3)))
+void fwd_async32_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                        const bf16_t* __restrict__ v, const int32_t* __restrict__ row_idx,
+                        const int4* __restrict__ items, const int4* __restrict__ splits,
+                        int* __restrict__ done, float* __restrict__ partials, int nrows, int N,
+                        int Tq, int Tk, float scale_log2, bf16_t* __restrict__ o,
+                        float* __restrict__ lse) {
+  static_assert(NW == 2, "wave 0 copies K, wave 1 copies V");
+  constexpr int D = 128;
+  constexpr int NK = D / 16, ND = D / 32;
+  constexpr int TILE = 32 * D;
+  constexpr int BQ = NW * 32;
+  __shared__ __attribute__((aligned(16))) uint16_t kb0[TILE], kb1[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t vb0[TILE], vb1[TILE];
+  __shared__ int last_segment;
+
+  const int4 item = items[blockIdx.x];
+  int4 sp;
+  if (!plan_item_ok(item, nrows, Tk, kRowPlan, splits, sp)) return;
+  const int wg = item.x;
+  const int bh = wg / Tq, qi = wg % Tq;
+  const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
+  const int h = lane >> 5, l32 = lane & 31;
+  const size_t base = (size_t)bh * N * D;
+  const rsrc_t rk = make_rsrc(k + base, (uint32_t)N * D * 2);
+  const rsrc_t rv = make_rsrc(v + base, (uint32_t)N * D * 2);
+  uint32_t uo[4];
+  unit_offsets(lane, uo);
+  const SwzAddr addr0(lane);
+  const int qrow = qi * (NW * 32) + w * 32 + l32;
+  const bool qvalid = qrow < N;
+
+  bf16x8 qf[NK];
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk)
+    qf[kk] = qvalid ? load8(q + base + (size_t)qrow * D + 16 * kk + 8 * h) : zero8();
+
+  f32x16 acc[ND];
+#pragma unroll
+  for (int db = 0; db < ND; ++db) acc[db] = zero16();
+  float m = -INFINITY, lsum = 0.f;
+
+  // half-steps u = 0 .. 2 cnt - 1: keys lst[u / 2] * 64 + 32 (u % 2)
+  const int cnt = item.z, steps = 2 * cnt;
+  const int32_t* lst = row_idx + (size_t)wg * Tk + item.y;
+  auto key_at = [&](int u) { return u < steps ? lst[u >> 1] * 64 + 32 * (u & 1) : 0; };
+  // wave 0 copies the 32 rows of K, wave 1 those of V
+  auto copy_half = [&](int key0, uint16_t* kd, uint16_t* vd) {
+    copy_groups<2>(w == 0 ? rk : rv, key0, 0, w == 0 ? kd : vd, uo);
+  };
+  int key_cur = key_at(0);
+  if (steps > 0) copy_half(key_cur, kb0, vb0);
+  int key_nxt = key_at(1);
+
+  double_buffered(steps, [&](int u, auto parity) {
+    constexpr bool odd = decltype(parity)::value == 1;
+    const uint16_t* kt = odd ? kb1 : kb0;
+    const uint16_t* vt = odd ? vb1 : vb0;
+    const int key0 = key_cur;
+    wait_vm_lgkm0<0>();
+    __syncthreads();
+    if (u + 1 < steps) copy_half(key_nxt, odd ? kb0 : kb1, odd ? vb0 : vb1);
+    key_cur = key_nxt;
+    key_nxt = key_at(u + 2);
+    if (key0 >= N) return;   // the second half of a partial last block, all past N
+    const SwzAddr A = addr0.fresh();
+
+    f32x16 s = zero16();
+    {
+      bf16x8 ka[NK];
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) ka[kk] = rd_row(kt, A.row(0, kk));
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) s = mfma32(ka[kk], qf[kk], s);
+    }
+    if (key0 + 32 > N) {
+      const int lim = N - key0 - 4 * h;
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (8 * (e >> 2) + (e & 3) >= lim) s[e] = -INFINITY;
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[e]);
+    mx = wave_max32(mx) * scale_log2;
+    if (__any(mx > m + kRescaleThreshold)) {
+      const float mnew = fmaxf(m, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+      m = mnew;
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < ND; ++db) acc[db] *= alpha;
+    }
+    bf16x8 va[ND];
+#pragma unroll
+    for (int db = 0; db < ND; ++db) va[db] = rd_tr(vt, A, 0, db);
+    float ps = 0.f;
+    bf16x8 pf[2];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], scale_log2, -m));
+      pf[e >> 3][e & 7] = (__bf16)pv;
+      ps += pv;
+    }
+    lsum += ps;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      bf16x8 vn[ND];
+#pragma unroll
+      for (int db = 0; db < ND; ++db) {
+        acc[db] = mfma32(va[db], pf[tt], acc[db]);
+        if (tt < 1) vn[db] = rd_tr(vt, A, tt + 1, db);
+      }
+      if (tt < 1)
+#pragma unroll
+        for (int db = 0; db < ND; ++db) va[db] = vn[db];
+    }
+  });
+
+  const float ltot = wave_sum32(lsum);
+  if (item.w < 0) {
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    if (qvalid) {
+      bf16_t* orow = o + base + (size_t)qrow * D;
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          store4(orow + 32 * db + 8 * g + 4 * h, acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv,
+                 acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv);
+      if (h == 0)
+        lse[(size_t)bh * N + qrow] = ltot > 0.f ? (m + __log2f(ltot)) * kLn2 : -INFINITY;
+    }
+    return;
+  }
+  // one segment of a split row: O^T rows, m and l into its partial slot
+  // ([BQ rows][D] unnormalised O, then m[BQ], l[BQ])
+  const int entry = item.w >> 10, seg = item.w & 1023;
+  {
+    const int r = w * 32 + l32;
+    float* part = partials + (size_t)(sp.y + seg) * kFwdPartialFloats;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        store4(part + (size_t)r * D + 32 * db + 8 * g + 4 * h, acc[db][4 * g],
+               acc[db][4 * g + 1], acc[db][4 * g + 2], acc[db][4 * g + 3]);
+    part[(size_t)BQ * D + (h == 0 ? r : BQ + r)] = h == 0 ? m : ltot;
+  }
+  // release the partial, count this segment done; the last one combines
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) last_segment = atomicAdd(&done[entry], 1) == sp.z - 1;
+  __syncthreads();
+  if (!last_segment) return;
+  __threadfence();
+  // two threads per row, each half of its D columns
+  const int r = tid >> 1, c0 = (tid & 1) * (D / 2);
+  const float* part0 = partials + (size_t)sp.y * kFwdPartialFloats;
+  float M = -INFINITY;
+  for (int s2 = 0; s2 < sp.z; ++s2)
+    M = fmaxf(M, part0[(size_t)s2 * kFwdPartialFloats + (size_t)BQ * D + r]);
+  float osum[D / 2];
+#pragma unroll
+  for (int c = 0; c < D / 2; ++c) osum[c] = 0.f;
+  float lt = 0.f;
+  if (M > -INFINITY) {
+    for (int s2 = 0; s2 < sp.z; ++s2) {
+      const float* ps = part0 + (size_t)s2 * kFwdPartialFloats;
+      const float wgt = __builtin_amdgcn_exp2f(ps[(size_t)BQ * D + r] - M);
+      lt += ps[(size_t)BQ * D + BQ + r] * wgt;
+#pragma unroll
+      for (int c = 0; c < D / 2; c += 4) {
+        const f32x4 x4 = *reinterpret_cast<const f32x4*>(ps + (size_t)r * D + c0 + c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) osum[c + i] += x4[i] * wgt;
+      }
+    }
+  }
+  const int row = qi * BQ + r;
+  if (row < N) {
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    bf16_t* orow = o + base + (size_t)row * D + c0;
+#pragma unroll
+    for (int c = 0; c < D / 2; c += 4)
+      store4(orow + c, osum[c] * inv, osum[c + 1] * inv, osum[c + 2] * inv, osum[c + 3] * inv);
+    if ((tid & 1) == 0)
+      lse[(size_t)bh * N + row] = lt > 0.f ? (M + __log2f(lt)) * kLn2 : -INFINITY;
+  }
+  if (tid == 0) done[entry] = 0;   // ready for the next call
+}
+
+
 // dQ for bf16 and d = 128 with the same K and V rings as the forward, one
 // workgroup per item of the row plan.  A segment of a split row leaves its
 // fp32 dQ^T rows in a partial slot; the last segment adds the slots in
@@ -775,6 +979,168 @@ void dq_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   }
   if (tid == 0) done[entry] = 0;   // ready for the next call
 }
+
+// dQ for 64-row query blocks with 32-key tiles (K and V double-buffered in
+// 32 KB of LDS), so that four two-wave workgroups share a CU instead of two:
+// 1.3B layer with 64 x 64 blocks, 0.714 -> 0.575 ms.  Otherwise as
+// dq_async_kernel.
+template <int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 3)))
+void dq_async32_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                       const bf16_t* __restrict__ v, const bf16_t* __restrict__ o,
+                       const bf16_t* __restrict__ dout, const float* __restrict__ lse,
+                       float* __restrict__ stats, const int32_t* __restrict__ row_idx,
+                       const int4* __restrict__ items, const int4* __restrict__ splits,
+                       int* __restrict__ done, float* __restrict__ partials, int nrows, int N,
+                       int Tq, int Tk, float scale_log2, float scale, bf16_t* __restrict__ dq) {
+  static_assert(NW == 2, "wave 0 copies K, wave 1 copies V");
+  constexpr int D = 128;
+  constexpr int NK = D / 16, ND = D / 32;
+  constexpr int TILE = 32 * D;
+  constexpr int BQ = NW * 32;
+  __shared__ __attribute__((aligned(16))) uint16_t kb0[TILE], kb1[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t vb0[TILE], vb1[TILE];
+  __shared__ int last_segment;
+
+  const int4 item = items[blockIdx.x];
+  int4 sp;
+  if (!plan_item_ok(item, nrows, Tk, kRowPlan, splits, sp)) return;
+  const int wg = item.x;
+  const int bh = wg / Tq, qi = wg % Tq;
+  const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
+  const int h = lane >> 5, l32 = lane & 31;
+  const size_t base = (size_t)bh * N * D;
+  const rsrc_t rk = make_rsrc(k + base, (uint32_t)N * D * 2);
+  const rsrc_t rv = make_rsrc(v + base, (uint32_t)N * D * 2);
+  uint32_t uo[4];
+  unit_offsets(lane, uo);
+  const SwzAddr addr0(lane);
+  const int qrow = qi * (NW * 32) + w * 32 + l32;
+  const bool qvalid = qrow < N;
+
+  // half-steps u = 0 .. 2 cnt - 1: keys lst[u / 2] * 64 + 32 (u % 2)
+  const int cnt = item.z, steps = 2 * cnt;
+  const int32_t* lst = row_idx + (size_t)wg * Tk + item.y;
+  auto key_at = [&](int u) { return u < steps ? lst[u >> 1] * 64 + 32 * (u & 1) : 0; };
+  auto copy_half = [&](int key0, uint16_t* kd, uint16_t* vd) {
+    copy_groups<2>(w == 0 ? rk : rv, key0, 0, w == 0 ? kd : vd, uo);
+  };
+  int key_cur = key_at(0), key_nxt = key_at(1);
+  if (steps > 0) copy_half(key_cur, kb0, vb0);
+
+  bf16x8 qf[NK], df[NK];
+  float dpart = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk) {
+    const size_t off = base + (size_t)qrow * D + 16 * kk + 8 * h;
+    qf[kk] = qvalid ? load8(q + off) : zero8();
+    df[kk] = qvalid ? load8(dout + off) : zero8();
+    if (qvalid) dpart += delta_part(o + off, df[kk]);
+  }
+  const float dl = wave_sum32(dpart);
+  const float l2 = qvalid ? lse[(size_t)bh * N + qrow] * kLog2e : 0.f;
+  if (item.w < 0 || (item.w & 1023) == 0)
+    stats[stat_lse2(bh, stat_groups(N), qrow) + 32 * h] = h ? dl : l2;
+
+  f32x16 acc[ND];
+#pragma unroll
+  for (int db = 0; db < ND; ++db) acc[db] = zero16();
+
+  double_buffered(steps, [&](int u, auto parity) {
+    constexpr bool odd = decltype(parity)::value == 1;
+    const uint16_t* kt = odd ? kb1 : kb0;
+    const uint16_t* vt = odd ? vb1 : vb0;
+    const int key0 = key_cur;
+    wait_vm_lgkm0<0>();
+    __syncthreads();
+    if (u + 1 < steps) copy_half(key_nxt, odd ? kb0 : kb1, odd ? vb0 : vb1);
+    key_cur = key_nxt;
+    key_nxt = key_at(u + 2);
+    if (key0 >= N) return;   // the second half of a partial last block, all past N
+    const SwzAddr A = addr0.fresh();
+    f32x16 sb = zero16(), dpb = zero16();
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      sb = mfma32(rd_row(kt, A.row(0, kk)), qf[kk], sb);
+      dpb = mfma32(rd_row(vt, A.row(0, kk)), df[kk], dpb);
+    }
+    // dS = P * (dP - Delta)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[e], scale_log2, -l2));
+      sb[e] = pv * (dpb[e] - dl);
+    }
+    if (key0 + 32 > N) {  // keys past N (zero rows) enter the dQ contraction: zero their dS
+      const int lim = N - key0 - 4 * h;
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (8 * (e >> 2) + (e & 3) >= lim) sb[e] = 0.f;
+    }
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const bf16x8 sf = pack8(sb, 8 * t2);
+#pragma unroll
+      for (int db = 0; db < ND; ++db) acc[db] = mfma32(rd_tr(kt, A, t2, db), sf, acc[db]);
+    }
+  });
+
+  if (item.w < 0) {
+    if (qvalid) {
+      bf16_t* row = dq + base + (size_t)qrow * D;
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          store4(row + 32 * db + 8 * g + 4 * h, acc[db][4 * g] * scale,
+                 acc[db][4 * g + 1] * scale, acc[db][4 * g + 2] * scale,
+                 acc[db][4 * g + 3] * scale);
+    }
+    return;
+  }
+  // one segment of a split row: fp32 dQ^T rows into its partial slot
+  const int entry = item.w >> 10, seg = item.w & 1023;
+  {
+    const int r = w * 32 + l32;
+    float* part = partials + (size_t)(sp.y + seg) * kDqPartialFloats + (size_t)r * D;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        store4(part + 32 * db + 8 * g + 4 * h, acc[db][4 * g], acc[db][4 * g + 1],
+               acc[db][4 * g + 2], acc[db][4 * g + 3]);
+  }
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) last_segment = atomicAdd(&done[entry], 1) == sp.z - 1;
+  __syncthreads();
+  if (!last_segment) return;
+  __threadfence();
+  // two threads per row, each half of its D columns, segments in order
+  const int r = tid >> 1, c0 = (tid & 1) * (D / 2);
+  const float* part0 = partials + (size_t)sp.y * kDqPartialFloats + (size_t)r * D + c0;
+  float gsum[D / 2];
+#pragma unroll
+  for (int c = 0; c < D / 2; ++c) gsum[c] = 0.f;
+  for (int s2 = 0; s2 < sp.z; ++s2) {
+    const float* ps = part0 + (size_t)s2 * kDqPartialFloats;
+#pragma unroll
+    for (int c = 0; c < D / 2; c += 4) {
+      const f32x4 x4 = *reinterpret_cast<const f32x4*>(ps + c);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) gsum[c + i] += x4[i];
+    }
+  }
+  const int row = qi * BQ + r;
+  if (row < N) {
+    bf16_t* grow = dq + base + (size_t)row * D + c0;
+#pragma unroll
+    for (int c = 0; c < D / 2; c += 4)
+      store4(grow + c, gsum[c] * scale, gsum[c + 1] * scale, gsum[c + 2] * scale,
+             gsum[c + 3] * scale);
+  }
+  if (tid == 0) done[entry] = 0;   // ready for the next call
+}
+
 
 // ---------------------------------------------------------------------------
 // Backward dK, dV: one workgroup (4 waves) per key block of 64 keys.
@@ -1467,6 +1833,13 @@ static void launch_fwd_async(const void* q, const void* k, const void* v, const 
                              int BH, int N, float sl2, void* o, float* lse, const PlanPtrs& rp,
                              hipStream_t s) {
   const int nrows = BH * m->Tq;
+  if constexpr (NW == 2) {
+    fwd_async32_kernel<NW><<<8 * plan_items_per_xcd(nrows, kRowPlan), NW * 64, 0, s>>>(
+        static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
+        static_cast<const bf16_t*>(v), m->row_idx, rp.items, rp.splits, rp.done, rp.partials,
+        nrows, N, m->Tq, m->Tk, sl2, static_cast<bf16_t*>(o), lse);
+    return;
+  }
   fwd_async_kernel<NW><<<8 * plan_items_per_xcd(nrows, kRowPlan), NW * 64, 0, s>>>(
       static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
       static_cast<const bf16_t*>(v), m->row_idx, rp.items, rp.splits, rp.done, rp.partials,
@@ -1511,7 +1884,7 @@ static void launch_dq(const BwdArgs& a) {
       static_cast<bf16_t*>(a.dq)
     const int grid = 8 * plan_items_per_xcd(nrows, kRowPlan);
     if (m->bq == 128) dq_async_kernel<4><<<grid, 256, 0, a.s>>>(SA2_DQ_ASYNC_ARGS);
-    else dq_async_kernel<2><<<grid, 128, 0, a.s>>>(SA2_DQ_ASYNC_ARGS);
+    else dq_async32_kernel<2><<<grid, 128, 0, a.s>>>(SA2_DQ_ASYNC_ARGS);
 #undef SA2_DQ_ASYNC_ARGS
     return;
   }
