@@ -870,6 +870,12 @@ void dq_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   // of the row.  Both statistics of every row of the block, padding rows
   // (zeros) included, are kept for the dK/dV kernel.
   const float dl = wave_sum32(dpart);
+  // The dP accumulators start at -Delta, so that the MFMAs leave dP - Delta
+  // (the row's Delta is the same for all of a lane's elements): 32 fewer
+  // vector subtractions per 64-key step.
+  f32x16 neg_dl;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) neg_dl[e] = -dl;
   const float l2 = qvalid ? lse[(size_t)bh * N + qrow] * kLog2e : 0.f;
   if (item.w < 0 || (item.w & 1023) == 0)
     stats[stat_lse2(bh, stat_groups(N), qrow) + 32 * h] = h ? dl : l2;
@@ -895,7 +901,7 @@ void dq_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const bool tail = key0 + 64 > N;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      f32x16 sb = zero16(), dpb = zero16();
+      f32x16 sb = zero16(), dpb = neg_dl;
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
         sb = mfma32(rd_row(kt, A.row(b, kk)), qf[kk], sb);
@@ -905,7 +911,7 @@ void dq_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[e], scale_log2, -l2));
-        sb[e] = pv * (dpb[e] - dl);
+        sb[e] = pv * dpb[e];
       }
       if (tail) {  // keys past N (zero rows) enter the dQ contraction: zero their dS
         const int lim = N - key0 - 4 * h;
@@ -1038,6 +1044,12 @@ void dq_async32_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ 
     if (qvalid) dpart += delta_part(o + off, df[kk]);
   }
   const float dl = wave_sum32(dpart);
+  // The dP accumulators start at -Delta, so that the MFMAs leave dP - Delta
+  // (the row's Delta is the same for all of a lane's elements): 32 fewer
+  // vector subtractions per 64-key step.
+  f32x16 neg_dl;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) neg_dl[e] = -dl;
   const float l2 = qvalid ? lse[(size_t)bh * N + qrow] * kLog2e : 0.f;
   if (item.w < 0 || (item.w & 1023) == 0)
     stats[stat_lse2(bh, stat_groups(N), qrow) + 32 * h] = h ? dl : l2;
@@ -1058,7 +1070,7 @@ void dq_async32_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ 
     key_nxt = key_at(u + 2);
     if (key0 >= N) return;   // the second half of a partial last block, all past N
     const SwzAddr A = addr0.fresh();
-    f32x16 sb = zero16(), dpb = zero16();
+    f32x16 sb = zero16(), dpb = neg_dl;
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
       sb = mfma32(rd_row(kt, A.row(0, kk)), qf[kk], sb);
@@ -1068,7 +1080,7 @@ void dq_async32_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ 
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[e], scale_log2, -l2));
-      sb[e] = pv * (dpb[e] - dl);
+      sb[e] = pv * dpb[e];
     }
     if (key0 + 32 > N) {  // keys past N (zero rows) enter the dQ contraction: zero their dS
       const int lim = N - key0 - 4 * h;
