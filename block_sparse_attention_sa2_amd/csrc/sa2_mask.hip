@@ -427,21 +427,21 @@ __device__ inline double wave_sum_f64(double v) {
 // registers), and for longer rows by a second launch of the whole-row sort
 // (with `marked`) that finishes just the rows marked row_cnt = -1.  Either way
 // the kept set is the one the full ranking gives.
-template <int E, bool CAND>
-__global__ __launch_bounds__(64 * kSelectWaves)
-void select_wave_kernel(const double* __restrict__ sbar, int nrows, int Tk, int kc, double p,
-                        int all, int marked, uint8_t* __restrict__ bitmap,
-                        int32_t* __restrict__ row_cnt, int32_t* __restrict__ row_idx) {
+//
+// The selection of one row by wave threadIdx.x / 64 of a workgroup of NW
+// waves: s points at the row's Tk scores (global or LDS memory); writes the
+// bitmap row, the row count and the ascending row list of global row `row`.
+// The wave's row flags live in LDS (private to the wave).
+template <int E, bool CAND, int NW>
+__device__ inline void select_row(const double* s, int row, int Tk, int kc, double p, int all,
+                                  uint8_t* __restrict__ bitmap, int32_t* __restrict__ row_cnt,
+                                  int32_t* __restrict__ row_idx) {
   constexpr int P2 = 64 * E;
   constexpr int C = E >= 16 ? 8 : E / 2;   // candidates per lane
   static_assert(!CAND || C < E, "a lane keeps some of its entries back");
-  __shared__ uint8_t flags_all[kSelectWaves][P2];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int row = blockIdx.x * kSelectWaves + wv;
-  if (row >= nrows) return;
-  if (marked && row_cnt[row] != -1) return;   // settled by the candidate launch
-  uint8_t* flag = flags_all[wv];
-  const double* s = sbar + (size_t)row * Tk;
+  __shared__ uint8_t flags_all[NW][P2];
+  const int lane = threadIdx.x & 63;
+  uint8_t* flag = flags_all[threadIdx.x >> 6];
 
   for (int j = lane; j < P2; j += 64) flag[j] = all && j < Tk ? 1 : 0;
   wave_lds_sync();
@@ -571,6 +571,18 @@ void select_wave_kernel(const double* __restrict__ sbar, int nrows, int Tk, int 
   for (int e = 0; e < E; ++e)
     if (flag[lane * E + e]) out[pos++] = lane * E + e;
   if (lane == 0) row_cnt[row] = c;
+}
+
+template <int E, bool CAND>
+__global__ __launch_bounds__(64 * kSelectWaves)
+void select_wave_kernel(const double* __restrict__ sbar, int nrows, int Tk, int kc, double p,
+                        int all, int marked, uint8_t* __restrict__ bitmap,
+                        int32_t* __restrict__ row_cnt, int32_t* __restrict__ row_idx) {
+  const int row = blockIdx.x * kSelectWaves + (threadIdx.x >> 6);
+  if (row >= nrows) return;
+  if (marked && row_cnt[row] != -1) return;   // settled by the candidate launch
+  select_row<E, CAND, kSelectWaves>(sbar + (size_t)row * Tk, row, Tk, kc, p, all, bitmap,
+                                    row_cnt, row_idx);
 }
 
 // ---------------------------------------------------------------------------
