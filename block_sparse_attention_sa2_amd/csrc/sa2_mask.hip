@@ -649,7 +649,7 @@ void plan_kernel(const int32_t* __restrict__ row_cnt, int nrows, int Tk,
   __shared__ int hist[kPlanBuckets];
   __shared__ int itot[kPlanThreads / 64];
   __shared__ long long red[kPlanThreads / 64];
-  __shared__ int ctr[2];
+  __shared__ int ctr[6];
   __shared__ long long pos[20];
   const int x = blockIdx.x % 8;
   const bool rows = blockIdx.x < 8;

@@ -50,6 +50,8 @@ struct PlanKind {
   int imbalance;    // XCD shares are cut at equal cost when the costliest
                     // equal-count share exceeds the mean by more than this
                     // many percent (0: always), else at equal count
+  int quarters;     // head-major groups give XCD 4g + r the r-th quarter of
+                    // every head's lists (1), or deal their items in turn (0)
 };
 // dK/dV: 256 CUs x 4 workgroups.  Forward and dQ: 256 CUs x 2; a row
 // segment also pays a combine pass over every segment of its row, so rows
@@ -57,8 +59,8 @@ struct PlanKind {
 // heads together in an XCD's L2 (the cost-balanced cut measured 4% slower
 // on a mask whose heads differ by a few percent), so rows are balanced only
 // when a share would carry over 10% more than its part.
-constexpr PlanKind kColPlan{1024, 2, 128, 8, 0};
-constexpr PlanKind kRowPlan{512, 1, 64, 16, 10};
+constexpr PlanKind kColPlan{1024, 2, 128, 8, 0, 0};
+constexpr PlanKind kRowPlan{512, 1, 64, 16, 10, 1};
 constexpr int kPlanBuckets = 4096;   // list lengths are ranked by min(length, 4095)
 constexpr size_t kPartialFloats = 2 * 64 * 128;           // dV and dK of one key block
 constexpr size_t kFwdPartialFloats = 128 * 128 + 2 * 128;  // O of a query block, m, l
@@ -98,7 +100,7 @@ __device__ inline T block_scan(T v, T* tot, T* all) {
 // The plan of XCD share x of n lists (lengths cnt, each at most cap;
 // `per_head` consecutive lists belong to one (batch, head)), by one workgroup
 // of nt threads (a multiple of 64 that divides kPlanBuckets).  LDS:
-// hist[kPlanBuckets] ints, itot and red (nt / 64 entries each), ctr[2],
+// hist[kPlanBuckets] ints, itot and red (nt / 64 entries each), ctr[6],
 // pos[20] 64-bit.
 //
 // Shares.  One pass gives every thread the cost (list length + 1) of a
@@ -111,17 +113,25 @@ __device__ inline T block_scan(T v, T* tot, T* all) {
 //
 // Order.  A group is planned head by head when no item of its share is
 // longer than a quarter of the group's mean load per resident workgroup
-// (share cost over slots / 2): the group's items, one (batch, head) after
-// another and longest first within each, are dealt in turn to its four XCDs,
-// so that the four work on one head at a time and its tiles are shared
-// through the last-level cache while they are live (14B-shaped layer: forward
-// -14%, dQ -8%, dK/dV -19% against per-XCD longest-first order).  The group's
+// (share cost over slots / 2): the group's items go one (batch, head) after
+// another, longest first within each, so that the four XCDs work on one head
+// at a time and its tiles are shared through the last-level cache while they
+// are live (14B-shaped layer: forward -14%, dQ -8%, dK/dV -19% against
+// per-XCD longest-first order).  In the row plan XCD 4g + r takes the r-th
+// contiguous quarter of every head's lists, so that an XCD's query blocks of
+// a head are neighbours, which keep more K/V tiles in common (forward -1.3%
+// and -2.5%, dQ -1.7% and -1.2% at the 1.3B and 14B layers against dealing
+// the items to the four XCDs in turn); the column plan deals its items in
+// turn (quarters made dK/dV 8% slower at the 14B layer).  When a quarter
+// would hold more items than an XCD has slots (few lists per head, not a
+// multiple of four), the items are dealt in turn as well.  The group's
 // first workgroup writes the whole group.  Where some item is longer, a list
 // that starts late would set the kernel's time (the 1.3B layer's longest
 // columns are as long as a slot's whole load), so each XCD takes its own
-// share longest first.  Heads and lengths share the kPlanBuckets ranks: with
-// nh heads in the share, each head has kPlanBuckets / nh length ranks, exact
-// when that exceeds the longest item.
+// share longest first.  Quarters, heads and lengths share the kPlanBuckets
+// ranks: with nh heads in the share, each (quarter, head) has
+// kPlanBuckets / (4 nh) length ranks (kPlanBuckets / nh when dealt in turn),
+// exact when that exceeds the longest item.
 static __device__ void plan_share(int x, const int32_t* __restrict__ cnt, int n, int cap,
                                   int per_head, PlanKind kd, int4* __restrict__ items,
                                   int4* __restrict__ splits, int* __restrict__ done, int ndone,
@@ -238,23 +248,48 @@ static __device__ void plan_share(int x, const int32_t* __restrict__ cnt, int n,
     start = s * base + min(s, rem);
     return base + (s < rem ? 1 : 0);
   };
+  const int ph = max(per_head, 1);
+  auto quarter = [&](int id) { return (int)((long long)(id % ph) * 4 / ph); };
+  // items per quarter (head-major groups): ctr[2 + r]
+  const int J = plan_items_per_xcd(n, kd);
+  if (tid < 6) ctr[tid] = 0;
+  __syncthreads();
+  if (head_major && kd.quarters)
+    for (int j = tid; j < len; j += nt)
+      atomicAdd(&ctr[2 + quarter(c0 + j)], nseg(list_len(cnt[c0 + j], cap)));
+  __syncthreads();
+  const bool quarters =
+      head_major && kd.quarters && max(max(ctr[2], ctr[3]), max(ctr[4], ctr[5])) <= J;
+  int qstart[4];
+  qstart[0] = 0;
+#pragma unroll
+  for (int r = 1; r < 4; ++r) qstart[r] = qstart[r - 1] + ctr[1 + r];
   // rank bucket of an item (higher buckets are placed first): its length, or
-  // (head, length) for a head-major group
-  const int h0 = c0 / max(per_head, 1);
-  const int nh = len > 0 ? (c0 + len - 1) / max(per_head, 1) - h0 + 1 : 1;
-  const int nb = nh <= kPlanBuckets ? kPlanBuckets / nh : 1;
+  // for a head-major group (quarter, head, length), or (head, length) when
+  // dealt in turn
+  const int h0 = c0 / ph;
+  const int nh = len > 0 ? (c0 + len - 1) / ph - h0 + 1 : 1;
+  const int nr = quarters ? 4 * nh : nh;   // (quarter,) head ranks
+  const int nb = nr <= kPlanBuckets ? kPlanBuckets / nr : 1;
   auto bucket = [&](int id, int sl) {
     if (!head_major) return min(sl, kPlanBuckets - 1);
-    const int hh = id / max(per_head, 1) - h0;
-    const int hb = nh <= kPlanBuckets ? hh : (int)((long long)hh * kPlanBuckets / nh);
+    const int hh = (quarters ? quarter(id) * nh : 0) + id / ph - h0;
+    const int hb = nr <= kPlanBuckets ? hh : (int)((long long)hh * kPlanBuckets / nr);
     const int lr = nb - 1 - min(nb - 1, (int)((long long)sl * nb / (gseg + 1)));
     return kPlanBuckets - 1 - (hb * nb + lr);
   };
-  // item k of the order: slot 8k + x, or dealt in turn to the group's XCDs
-  auto slot_of = [&](int k) { return head_major ? 8 * (k >> 2) + 4 * grp + (k & 3) : 8 * k + x; };
+  // item k of the order (k counts from the first item of the item's
+  // quarter): slot 8k + x, or 8k + 4g + r in quarter r, or dealt in turn
+  auto slot_of = [&](int k, int id) {
+    if (!head_major) return 8 * k + x;
+    if (quarters) {
+      const int r = quarter(id);
+      return 8 * (k - qstart[r]) + 4 * grp + r;
+    }
+    return 8 * (k >> 2) + 4 * grp + (k & 3);
+  };
 
   for (int c = tid; c < kPlanBuckets; c += nt) hist[c] = 0;
-  if (tid == 0) ctr[0] = ctr[1] = 0;
   __syncthreads();
   // histogram of the items' buckets, then the first position of each bucket
   // in descending bucket order
@@ -290,15 +325,15 @@ static __device__ void plan_share(int x, const int32_t* __restrict__ cnt, int n,
     for (int s2 = 0; s2 < ns; ++s2) {
       int st;
       const int sl = seg(ln, ns, s2, st);
-      items[slot_of(atomicAdd(&hist[bucket(id, sl)], 1))] =
+      items[slot_of(atomicAdd(&hist[bucket(id, sl)], 1), id)] =
           make_int4(id, st, sl, ns > 1 ? entry * 1024 + s2 : -1);
     }
   }
   __syncthreads();
   // unused items of the XCDs planned here, unused split entries, counters
-  const int J = plan_items_per_xcd(n, kd);
   for (int r = 0; r < (head_major ? 4 : 1); ++r) {
-    const int used = head_major ? (nitems > r ? (nitems - r + 3) / 4 : 0) : nitems;
+    const int used = quarters ? ctr[2 + r]
+                     : head_major ? (nitems > r ? (nitems - r + 3) / 4 : 0) : nitems;
     const int col = head_major ? 4 * grp + r : x;
     for (int j = used + tid; j < J; j += nt) items[8 * j + col] = make_int4(-1, 0, 0, -1);
   }

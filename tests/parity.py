@@ -113,8 +113,9 @@ def check_lists(bitmap: np.ndarray, row_cnt, row_idx, col_cnt, col_idx):
         assert np.array_equal(col_idx[j, :len(want)], want), f"column {j} list"
 
 
-ROW_PLAN = dict(slots=512, fair=1, extra=64, min_segment=16, imbalance=10, counters=2)
-COL_PLAN = dict(slots=1024, fair=2, extra=128, min_segment=8, imbalance=0, counters=1)
+ROW_PLAN = dict(slots=512, fair=1, extra=64, min_segment=16, imbalance=10, counters=2, quarters=True)
+COL_PLAN = dict(slots=1024, fair=2, extra=128, min_segment=8, imbalance=0, counters=1,
+                quarters=False)
 
 
 def _items_per_xcd(n: int, kd: dict) -> int:
@@ -175,11 +176,16 @@ def check_plan(cnt, plan, kd: dict, cap: int, per_head: int, head_major_out=None
     form group g, whose share is the union of theirs.  A group is head-major
     when 4 x its longest item (its lists cut at Lg = max(L0, ceil(group
     entries / (4 extra)))) x slots / 2 is at most the group's cost (entries +
-    lists), L0 = max(min_segment, fair * ceil(total / slots)): then the
-    group's items, in rank order k, sit at slot 8 (k // 4) + 4g + k % 4,
-    ordered by (batch, head) and longest first within each head (in the
-    shared length ranks of the plan: 4096 // heads per head), with split
-    entries and partial slots in the group's range.  Otherwise each XCD's
+    lists), L0 = max(min_segment, fair * ceil(total / slots)): then, for a
+    plan kind with quarters, XCD 4g + r holds the items of the r-th
+    contiguous quarter of every (batch, head)'s lists (list index within its
+    head times 4 // lists per head = r), ordered by (batch, head) and longest
+    first within each head (in the shared ranks of the plan: 4096 // (4
+    heads) length ranks per quarter and head), unless a quarter holds more
+    items than an XCD has slots; otherwise, or for a kind without, the group's items,
+    in rank order k over (batch, head) and length (4096 // heads ranks per
+    head), sit at slot 8 (k // 4) + 4g + k % 4.  Split entries and partial
+    slots lie in the group's range.  Otherwise each XCD's
     items are its share longest first, cut at max(L0, ceil(share / extra)),
     with entries and slots in the XCD's range.  Every completion counter is
     zero.  Returns the number of split lists; appends each group's head-major
@@ -223,22 +229,48 @@ def check_plan(cnt, plan, kd: dict, cap: int, per_head: int, head_major_out=None
             head_major_out.append(bool(head_major))
         if head_major:
             nitems = sum(len(c) for c in gcols)
-            for r in range(4):
-                assert len(gcols[r]) == (-(-(nitems - r) // 4) if nitems > r else 0), \
-                    f"group {g}: items not dealt in turn"
-            order = np.array([gcols[k % 4][k // 4] for k in range(nitems)]).reshape(-1, 4)
-            heads = order[:, 0] // per_head
-            h0 = G0 // per_head
-            nh = (G1 - 1) // per_head - h0 + 1
-            nb = 4096 // nh if nh <= 4096 else 1
-            hb = heads - h0 if nh <= 4096 else (heads - h0) * 4096 // nh
-            lr = nb - 1 - np.minimum(nb - 1, order[:, 2] * nb // (gseg + 1))
-            rank = hb * nb + lr
-            assert np.all(np.diff(rank) >= 0), f"group {g}: not head by head, longest first"
-            assert np.all(np.diff(heads) >= 0), f"group {g}: heads out of order"
-            if nb > gseg:
-                same = heads[1:] == heads[:-1]
-                assert np.all(np.diff(order[:, 2])[same] <= 0), f"group {g}: not longest first"
+            ph = max(per_head, 1)
+            h0 = G0 // ph
+            nh = (G1 - 1) // ph - h0 + 1
+            qn = [0, 0, 0, 0]
+            for lid in range(G0, G1):
+                qn[(lid % ph) * 4 // ph] += len(_cut(int(cnt[lid]), Lg))
+            if kd["quarters"] and max(qn) <= J:
+                # XCD 4g + r: the r-th contiguous quarter of every head's lists
+                nr = 4 * nh
+                nb = 4096 // nr if nr <= 4096 else 1
+                for r in range(4):
+                    c = gcols[r]
+                    assert len(c) == qn[r], f"group {g}: XCD {4 * g + r} does not hold quarter {r}"
+                    assert np.all((c[:, 0] % ph) * 4 // ph == r), \
+                        f"group {g}: item outside quarter {r}"
+                    heads = c[:, 0] // ph
+                    hh = r * nh + heads - h0
+                    hb = hh if nr <= 4096 else hh * 4096 // nr
+                    lr = nb - 1 - np.minimum(nb - 1, c[:, 2] * nb // (gseg + 1))
+                    assert np.all(np.diff(hb * nb + lr) >= 0), \
+                        f"group {g}: XCD {4 * g + r} not head by head, longest first"
+                    assert np.all(np.diff(heads) >= 0), f"group {g}: heads out of order"
+                    if nb > gseg:
+                        same = heads[1:] == heads[:-1]
+                        assert np.all(np.diff(c[:, 2])[same] <= 0), f"group {g}: not longest first"
+                order = np.concatenate([c.reshape(-1, 4) for c in gcols])
+            else:
+                # a quarter larger than an XCD's slots: the items dealt in turn
+                for r in range(4):
+                    assert len(gcols[r]) == (-(-(nitems - r) // 4) if nitems > r else 0), \
+                        f"group {g}: items not dealt in turn"
+                order = np.array([gcols[k % 4][k // 4] for k in range(nitems)]).reshape(-1, 4)
+                heads = order[:, 0] // ph
+                nb = 4096 // nh if nh <= 4096 else 1
+                hb = heads - h0 if nh <= 4096 else (heads - h0) * 4096 // nh
+                lr = nb - 1 - np.minimum(nb - 1, order[:, 2] * nb // (gseg + 1))
+                rank = hb * nb + lr
+                assert np.all(np.diff(rank) >= 0), f"group {g}: not head by head, longest first"
+                assert np.all(np.diff(heads) >= 0), f"group {g}: heads out of order"
+                if nb > gseg:
+                    same = heads[1:] == heads[:-1]
+                    assert np.all(np.diff(order[:, 2])[same] <= 0), f"group {g}: not longest first"
             nsplit += _check_items(cnt, glists, order, Lg, splits, 4 * ex * g, 4 * ex,
                                    slot_owner, f"group {g}")
             continue

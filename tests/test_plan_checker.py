@@ -2,9 +2,11 @@
 host by a small planner written here from the plan rule, so that the checker
 that the GPU tests rely on is itself pinned: it accepts every valid plan of
 both orders (per-XCD longest first, and head by head over groups of four
-XCDs), with and without cut lists, and rejects each plausible defect (a
-missing or repeated item, items out of order, a group not dealt in turn, a
-split slot shared, a counter left set)."""
+XCDs, each XCD a quarter of every head or, where a quarter is too large, the
+group dealt in turn), with and without cut lists, and rejects each
+plausible defect (a missing or repeated item, items out of order, an item
+outside its quarter, a group not dealt in turn, a split slot shared, a
+counter left set)."""
 from __future__ import annotations
 
 import numpy as np
@@ -70,7 +72,12 @@ def make_plan(cnt, kd, cap, per_head, rng):
         for x, c0, c1, L, ebase in units:
             h0 = c0 // per_head
             nh = (c1 - 1) // per_head - h0 + 1 if c1 > c0 else 1
-            nb = NB // nh if nh <= NB else 1
+            qn = [0, 0, 0, 0]
+            for lid in range(c0, c1):
+                qn[(lid % per_head) * 4 // per_head] += len(_cut(int(cnt[lid]), L))
+            quarters = hm and kd["quarters"] and max(qn) <= J
+            nr = 4 * nh if quarters else nh
+            nb = NB // nr if nr <= NB else 1
             its, e_used, p_used = [], 0, 0
             for lid in range(c0, c1):
                 segs = _cut(int(cnt[lid]), L)
@@ -82,16 +89,22 @@ def make_plan(cnt, kd, cap, per_head, rng):
                     p_used += len(segs)
                 for s2, (st, sl) in enumerate(segs):
                     if hm:
-                        hh = lid // per_head - h0
-                        hb = hh if nh <= NB else hh * NB // nh
+                        hh = ((lid % per_head) * 4 // per_head) * nh if quarters else 0
+                        hh += lid // per_head - h0
+                        hb = hh if nr <= NB else hh * NB // nr
                         key = NB - 1 - (hb * nb + nb - 1 - min(nb - 1, sl * nb // (gseg + 1)))
                     else:
                         key = min(sl, NB - 1)
                     its.append((key, rng.random(),
                                 (lid, st, sl, entry * 1024 + s2 if len(segs) > 1 else -1)))
             its.sort(key=lambda t: (-t[0], t[1]))
+            qpos = [0, 0, 0, 0]
             for k, (_, _, it) in enumerate(its):
-                if hm:
+                if quarters:   # XCD 4g + r: quarter r of every head
+                    r = (it[0] % per_head) * 4 // per_head
+                    items[qpos[r], 4 * g + r] = it
+                    qpos[r] += 1
+                elif hm:       # a quarter too large: dealt in turn
                     items[k // 4, 4 * g + k % 4] = it
                 else:
                     items[k, x] = it
@@ -116,6 +129,9 @@ def _cases():
     out.append(("cols", c, 256, 128))
     # fewer lists than XCDs
     out.append(("rows", np.array([3, 0, 5]), 8, 3))
+    # five lists per head: quarter 0 holds two of them, more than an XCD's
+    # slots, so the head-major groups are dealt in turn
+    out.append(("rows", rng.integers(0, 3, 500 * 5), 8, 5))
     return out
 
 
@@ -190,8 +206,35 @@ def test_rejects_head_major_items_out_of_head_order():
     _rejects(kd, cnt, cap, ph, plan)
 
 
+def test_rejects_an_item_outside_its_quarter():
+    kd, cnt, cap, ph, plan, dec = _valid(0)   # rows: quarters
+    assert dec == [True, True] and kd["quarters"]
+    items, _, _ = _plan_views(plan, cnt.size, kd)
+    # move XCD 3's last item to the end of XCD 0's column
+    k3 = int(np.count_nonzero(items[:, 3, 0] >= 0))
+    k0 = int(np.count_nonzero(items[:, 0, 0] >= 0))
+    items[k0, 0] = items[k3 - 1, 3]
+    items[k3 - 1, 3] = (-1, 0, 0, -1)
+    _rejects(kd, cnt, cap, ph, plan)
+
+
+def test_quarter_and_dealt_layouts_are_exercised():
+    seen = set()
+    for kind, cnt, cap, per_head in _cases():
+        kd = P.ROW_PLAN if kind == "rows" else P.COL_PLAN
+        plan, dec = make_plan(cnt, kd, cap, per_head, np.random.default_rng(0))
+        items, _, _ = _plan_views(plan, cnt.size, kd)
+        for g in range(2):
+            if not dec[g]:
+                continue
+            lists = items[:, 4 * g, 0]
+            lists = lists[lists >= 0]
+            seen.add(bool(np.all((lists % per_head) * 4 // per_head == 0)))
+    assert seen == {True, False}
+
+
 def test_rejects_a_group_not_dealt_in_turn():
-    kd, cnt, cap, ph, plan, dec = _valid(1)
+    kd, cnt, cap, ph, plan, dec = _valid(len(_cases()) - 1)
     assert dec == [True, True]
     items, _, _ = _plan_views(plan, cnt.size, kd)
     # move XCD 3's last item to the end of XCD 0's column
