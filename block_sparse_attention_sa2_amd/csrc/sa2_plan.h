@@ -249,28 +249,21 @@ static __device__ void plan_share(int x, const int32_t* __restrict__ cnt, int n,
     return base + (s < rem ? 1 : 0);
   };
   const int ph = max(per_head, 1);
-  auto quarter = [&](int id) { return (int)((long long)(id % ph) * 4 / ph); };
-  // items per quarter (head-major groups): ctr[2 + r]
+  // quarter of list id within its (batch, head): (index in head) * 4 / ph,
+  // by comparisons rather than a division
+  auto quarter = [&](int id) {
+    const int j4 = 4 * (id - (id / ph) * ph);
+    return (j4 >= ph ? 1 : 0) + (j4 >= 2 * ph ? 1 : 0) + (j4 >= 3 * ph ? 1 : 0);
+  };
   const int J = plan_items_per_xcd(n, kd);
-  if (tid < 6) ctr[tid] = 0;
-  __syncthreads();
-  if (head_major && kd.quarters)
-    for (int j = tid; j < len; j += nt)
-      atomicAdd(&ctr[2 + quarter(c0 + j)], nseg(list_len(cnt[c0 + j], cap)));
-  __syncthreads();
-  const bool quarters =
-      head_major && kd.quarters && max(max(ctr[2], ctr[3]), max(ctr[4], ctr[5])) <= J;
-  int qstart[4];
-  qstart[0] = 0;
-#pragma unroll
-  for (int r = 1; r < 4; ++r) qstart[r] = qstart[r - 1] + ctr[1 + r];
   // rank bucket of an item (higher buckets are placed first): its length, or
   // for a head-major group (quarter, head, length), or (head, length) when
   // dealt in turn
   const int h0 = c0 / ph;
   const int nh = len > 0 ? (c0 + len - 1) / ph - h0 + 1 : 1;
-  const int nr = quarters ? 4 * nh : nh;   // (quarter,) head ranks
-  const int nb = nr <= kPlanBuckets ? kPlanBuckets / nr : 1;
+  bool quarters = head_major && kd.quarters;   // until a quarter overflows
+  int nr = quarters ? 4 * nh : nh;             // (quarter,) head ranks
+  int nb = nr <= kPlanBuckets ? kPlanBuckets / nr : 1;
   auto bucket = [&](int id, int sl) {
     if (!head_major) return min(sl, kPlanBuckets - 1);
     const int hh = (quarters ? quarter(id) * nh : 0) + id / ph - h0;
@@ -278,6 +271,43 @@ static __device__ void plan_share(int x, const int32_t* __restrict__ cnt, int n,
     const int lr = nb - 1 - min(nb - 1, (int)((long long)sl * nb / (gseg + 1)));
     return kPlanBuckets - 1 - (hb * nb + lr);
   };
+  // histogram of the items' buckets, with the items per quarter (ctr[2 + r])
+  auto histogram = [&](bool count_quarters) {
+    for (int c = tid; c < kPlanBuckets; c += nt) hist[c] = 0;
+    if (tid < 6) ctr[tid] = 0;
+    __syncthreads();
+    int qn[4] = {0, 0, 0, 0};
+    for (int j = tid; j < len; j += nt) {
+      const int id = c0 + j, ln = list_len(cnt[id], cap), ns = nseg(ln);
+      for (int s2 = 0; s2 < ns; ++s2) {
+        int st;
+        atomicAdd(&hist[bucket(id, seg(ln, ns, s2, st))], 1);
+      }
+      const int r = quarter(id);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qn[i] += r == i ? ns : 0;
+    }
+    if (count_quarters) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        for (int off = 32; off > 0; off >>= 1) qn[i] += __shfl_xor(qn[i], off);
+        if ((tid & 63) == 0) atomicAdd(&ctr[2 + i], qn[i]);
+      }
+    }
+    __syncthreads();
+  };
+  histogram(quarters);
+  if (quarters && max(max(ctr[2], ctr[3]), max(ctr[4], ctr[5])) > J) {
+    quarters = false;   // a quarter would overflow its XCD's item slots: deal in turn
+    nr = nh;
+    nb = nr <= kPlanBuckets ? kPlanBuckets / nr : 1;
+    __syncthreads();
+    histogram(false);
+  }
+  int qstart[4];
+  qstart[0] = 0;
+#pragma unroll
+  for (int r = 1; r < 4; ++r) qstart[r] = qstart[r - 1] + ctr[1 + r];
   // item k of the order (k counts from the first item of the item's
   // quarter): slot 8k + x, or 8k + 4g + r in quarter r, or dealt in turn
   auto slot_of = [&](int k, int id) {
@@ -288,19 +318,7 @@ static __device__ void plan_share(int x, const int32_t* __restrict__ cnt, int n,
     }
     return 8 * (k >> 2) + 4 * grp + (k & 3);
   };
-
-  for (int c = tid; c < kPlanBuckets; c += nt) hist[c] = 0;
-  __syncthreads();
-  // histogram of the items' buckets, then the first position of each bucket
-  // in descending bucket order
-  for (int j = tid; j < len; j += nt) {
-    const int id = c0 + j, ln = list_len(cnt[id], cap), ns = nseg(ln);
-    for (int s2 = 0; s2 < ns; ++s2) {
-      int st;
-      atomicAdd(&hist[bucket(id, seg(ln, ns, s2, st))], 1);
-    }
-  }
-  __syncthreads();
+  // the first position of each bucket in descending bucket order
   const int bper = kPlanBuckets / nt;   // nt divides kPlanBuckets
   const int blo = tid * bper, bhi = blo + bper;
   int local = 0;
