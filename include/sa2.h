@@ -75,8 +75,11 @@ typedef enum { SA2_BF16 = 0, SA2_F32 = 1 } sa2_dtype;
  *            contiguous eighth of the lists, rows by count and columns by
  *            cost), longest first; where no list of a group of four XCDs'
  *            shares is long against the group's load per workgroup, the
- *            group's lists go head by head (longest first within a head),
- *            dealt in turn to its four XCDs.  A list much longer than the
+ *            group's lists go head by head (longest first within a head):
+ *            in the row plan XCD 4g + r takes the r-th contiguous quarter of
+ *            every head's lists, in the column plan (or when a quarter
+ *            would not fit an XCD's slots) the items are dealt in turn to
+ *            the four XCDs.  A list much longer than the
  *            mean load of the kernel's resident workgroups is cut into
  *            segments whose partial sums the list's last segment combines in
  *            a fixed order.
