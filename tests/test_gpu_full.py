@@ -283,6 +283,48 @@ def test_head_major_rows_across_batches():
     log_parity("head_major_rows_across_batches", w.name, heads=2, **worst)
 
 
+@pytest.mark.parametrize("H, N, quarters", [(288, 768, True), (288, 640, False)])
+def test_head_major_rows_with_uneven_quarters(H, N, quarters):
+    """Top-k 2 of the key blocks, so the row plan is head by head.  With six
+    query blocks per head the quarters of a head hold 2, 1, 2 and 1 of them
+    and fit the XCDs' item slots: XCD 4g + r holds quarter r.  With five per
+    head, quarter 0 holds two of every five rows, more than an XCD's slots, so
+    the group is dealt in turn.  The plans check out, and the mask, O, LSE,
+    dQ, dK and dV of two heads match the oracle."""
+    from dataclasses import replace
+    Tk = -(-N // 64)
+    w = W.Workload(f"uneven{H}", 1, H, N, 128, 128, 64, "normal", 43, "bf16", 2 / Tk, 0.0)
+    _say(f"[head-major uneven] B1 H{H} N{N}")
+    dev, ref = device_inputs(w)
+    q, k, v, do = (dev[t] for t in ("q", "k", "v", "do"))
+    mask = sa2.build_mask(q, k, w.bq, w.bk, w.k_frac, w.p)
+    o, lse = sa2.attn_fwd(q, k, v, mask)
+    grads = sa2.attn_bwd(q, k, v, o, lse, do, mask)
+    torch.cuda.synchronize()
+    hm = {}
+    check_plans(mask, hm)
+    assert hm["rows"] == [True, True], hm
+    # XCD 0 holds only quarter-0 rows exactly when the plan uses quarters
+    Tq = mask.Tq
+    n = H * Tq
+    J = (n + 7) // 8 + 2 * (((n + 7) // 8 + 15) // 16) + 64
+    items = mask.row_plan.cpu().numpy()[:8 * J * 4].reshape(J, 8, 4)
+    lists = items[:, 0, 0]
+    lists = lists[lists >= 0]
+    assert bool(np.all((lists % Tq) * 4 // Tq == 0)) == quarters
+    bm = mask.bitmap.cpu().numpy()
+    worst = {}
+    exact = ties = mass = 0
+    for h in (1, H - 2):
+        e_, t_, m_ = compare_mask(O.build_mask_head(ref["q"][0, h], ref["k"][0, h], w.bq, w.bk,
+                                                    w.k_frac, w.p), bm[0, h], w.p)
+        exact += e_; ties += t_; mass += m_
+        _worst(worst, _whole_head(w, ref, h, bm[0, h], o, lse, grads))
+    log_mask_exceptions("head_major_rows_with_uneven_quarters", w.name, 2, 2 * Tq, exact, ties,
+                        mass)
+    log_parity("head_major_rows_with_uneven_quarters", w.name, heads=2, **worst)
+
+
 # ---------------------------------------------------------------------------
 # Mask-rule stress test
 # ---------------------------------------------------------------------------
