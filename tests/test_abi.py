@@ -214,3 +214,19 @@ def test_distill_validation():
         st, msg = _status_and_msg(call(**kw))
         assert st == want, (kw, st, msg)
         assert msg.startswith("sa2_distill_loss_grad"), msg
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path, monkeypatch):
+    """No CPU fallback: with libsa2.so absent, every call through the binding
+    raises ImportError before anything runs."""
+    import torch
+    import block_sparse_attention_sa2_amd as sa2
+    monkeypatch.setattr(_lib, "LIB_PATH", tmp_path / "libsa2.so")
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(ImportError, match="no fallback"):
+        sa2.version()
+    with pytest.raises(ImportError):
+        sa2.mask_workspace_bytes(1, 1, 64, 64, 64, 64)
+    q = torch.zeros(1, 1, 64, 64)
+    with pytest.raises((ImportError, ValueError)):
+        sa2.build_mask(q, q, 64, 64, 0.5, 0.5)
