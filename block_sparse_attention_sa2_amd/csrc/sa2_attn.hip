@@ -536,17 +536,11 @@ void fwd_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
   const float ltot = wave_sum32(lsum);
   if (item.w < 0) {
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-    if (qvalid) {
-      bf16_t* orow = o + base + (size_t)qrow * D;
+    bf16_t* orow = o + base + (size_t)(qvalid ? qrow : 0) * D;
 #pragma unroll
-      for (int db = 0; db < ND; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-          store4(orow + 32 * db + 8 * g + 4 * h, acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv,
-                 acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv);
-      if (h == 0)
-        lse[(size_t)bh * N + qrow] = ltot > 0.f ? (m + __log2f(ltot)) * kLn2 : -INFINITY;
-    }
+    for (int db = 0; db < ND; ++db) store_row32(orow + 32 * db, acc[db], inv, h, qvalid);
+    if (qvalid && h == 0)
+      lse[(size_t)bh * N + qrow] = ltot > 0.f ? (m + __log2f(ltot)) * kLn2 : -INFINITY;
     return;
   }
   // one segment of a split row: O^T rows, m and l into its partial slot
@@ -737,17 +731,11 @@ void fwd_async32_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__
   const float ltot = wave_sum32(lsum);
   if (item.w < 0) {
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-    if (qvalid) {
-      bf16_t* orow = o + base + (size_t)qrow * D;
+    bf16_t* orow = o + base + (size_t)(qvalid ? qrow : 0) * D;
 #pragma unroll
-      for (int db = 0; db < ND; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-          store4(orow + 32 * db + 8 * g + 4 * h, acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv,
-                 acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv);
-      if (h == 0)
-        lse[(size_t)bh * N + qrow] = ltot > 0.f ? (m + __log2f(ltot)) * kLn2 : -INFINITY;
-    }
+    for (int db = 0; db < ND; ++db) store_row32(orow + 32 * db, acc[db], inv, h, qvalid);
+    if (qvalid && h == 0)
+      lse[(size_t)bh * N + qrow] = ltot > 0.f ? (m + __log2f(ltot)) * kLn2 : -INFINITY;
     return;
   }
   // one segment of a split row: O^T rows, m and l into its partial slot
@@ -930,16 +918,9 @@ void dq_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   });
 
   if (item.w < 0) {
-    if (qvalid) {
-      bf16_t* row = dq + base + (size_t)qrow * D;
+    bf16_t* row = dq + base + (size_t)(qvalid ? qrow : 0) * D;
 #pragma unroll
-      for (int db = 0; db < ND; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-          store4(row + 32 * db + 8 * g + 4 * h, acc[db][4 * g] * scale,
-                 acc[db][4 * g + 1] * scale, acc[db][4 * g + 2] * scale,
-                 acc[db][4 * g + 3] * scale);
-    }
+    for (int db = 0; db < ND; ++db) store_row32(row + 32 * db, acc[db], scale, h, qvalid);
     return;
   }
   // one segment of a split row: fp32 dQ^T rows into its partial slot
@@ -1097,16 +1078,9 @@ void dq_async32_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ 
   });
 
   if (item.w < 0) {
-    if (qvalid) {
-      bf16_t* row = dq + base + (size_t)qrow * D;
+    bf16_t* row = dq + base + (size_t)(qvalid ? qrow : 0) * D;
 #pragma unroll
-      for (int db = 0; db < ND; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-          store4(row + 32 * db + 8 * g + 4 * h, acc[db][4 * g] * scale,
-                 acc[db][4 * g + 1] * scale, acc[db][4 * g + 2] * scale,
-                 acc[db][4 * g + 3] * scale);
-    }
+    for (int db = 0; db < ND; ++db) store_row32(row + 32 * db, acc[db], scale, h, qvalid);
     return;
   }
   // one segment of a split row: fp32 dQ^T rows into its partial slot
@@ -1621,18 +1595,15 @@ void dkdv_pair_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
       }
       if (tid == 0) done[entry] = 0;   // ready for the next call
     }
-  } else if (key < N) {
-    bf16_t* rv = dv + base + (size_t)key * D;
-    bf16_t* rk = dk + base + (size_t)key * D;
+  } else {
+    const bool kv = key < N;
+    bf16_t* rv = dv + base + (size_t)(kv ? key : 0) * D;
+    bf16_t* rk = dk + base + (size_t)(kv ? key : 0) * D;
 #pragma unroll
-    for (int db = 0; db < ND; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int c = 32 * db + 8 * g + 4 * h, e = 4 * g;
-        store4(rv + c, accv[db][e], accv[db][e + 1], accv[db][e + 2], accv[db][e + 3]);
-        store4(rk + c, acck[db][e] * scale, acck[db][e + 1] * scale, acck[db][e + 2] * scale,
-               acck[db][e + 3] * scale);
-      }
+    for (int db = 0; db < ND; ++db) {
+      store_row32(rv + 32 * db, accv[db], 1.f, h, kv);
+      store_row32(rk + 32 * db, acck[db], scale, h, kv);
+    }
   }
 }
 

@@ -121,6 +121,36 @@ __device__ inline void cross_half(float v, float& a, float& b) {
   a = __uint_as_float(r[0]);
   b = __uint_as_float(r[1]);
 }
+// Stores 32 consecutive columns of one row held in the MFMA accumulator
+// layout (element e of half-wave h at column 8(e/4) + 4h + e%4), scaled by
+// mul and rounded to bf16, as two 16-byte stores per lane instead of four
+// 8-byte ones: v_permlane32_swap hands each half-wave its partner's
+// neighbouring four columns, so half-wave h writes columns 16j + 8h .. +7.
+// The exchange runs on every lane; `valid` (the same for a lane and the lane
+// 32 apart) guards only the stores.
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  bf16x2_t v;
+  v[0] = (__bf16)a;
+  v[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ inline void store_row32(bf16_t* p, const f32x16& a, float mul, int h, bool valid) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    uint32_t x[2], y[2];
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const int e0 = 8 * j + 2 * w, e1 = e0 + 4;   // a word of group 2j, the same of 2j + 1
+      const auto r = __builtin_amdgcn_permlane32_swap(pack_bf16x2(a[e0] * mul, a[e0 + 1] * mul),
+                                                      pack_bf16x2(a[e1] * mul, a[e1 + 1] * mul),
+                                                      false, false);
+      x[w] = r[0];   // half 0: its own group 2j; half 1: the partner's group 2j + 1
+      y[w] = r[1];   // half 0: the partner's group 2j; half 1: its own group 2j + 1
+    }
+    if (valid) *reinterpret_cast<uint4*>(p + 16 * j + 8 * h) = make_uint4(x[0], x[1], y[0], y[1]);
+  }
+}
 __device__ inline float wave_max32(float v) {  // max with the lane 32 apart
   float a, b;
   cross_half(v, a, b);
