@@ -429,10 +429,11 @@ void fwd_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
   const int qrow = qi * (NW * 32) + w * 32 + l32;
   const bool qvalid = qrow < N;
 
-  bf16x8 qf[NK];
-#pragma unroll
-  for (int kk = 0; kk < NK; ++kk)
-    qf[kk] = qvalid ? load8(q + base + (size_t)qrow * D + 16 * kk + 8 * h) : zero8();
+  // this wave's 32 query rows are copied whole into the second K/V buffers
+  // (free until step 0 issues its copy) and read from there in the MFMA
+  // operand layout; rows past N arrive as zeros
+  uint16_t* qs = (w < 2 ? kb1 : vb1) + (w & 1) * 32 * D;
+  copy_groups<2>(make_rsrc(q + base, (uint32_t)N * D * 2), qi * BQ + w * 32, 0, qs, uo);
 
   f32x16 acc[ND];
 #pragma unroll
@@ -446,6 +447,13 @@ void fwd_async_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
   int key_cur = key_at(0);
   if (cnt > 0) copy_kv_tile<NW>(rk, rv, key_cur, kb0, vb0, w, uo);
   int key_nxt = key_at(1);
+  // the Q copy went out before the first tile's 2 * 16 / NW copy instructions
+  if (cnt > 0) wait_vm_lgkm0<2 * (16 / NW)>();
+  else wait_vm_lgkm0<0>();
+  wave_lds_sync();
+  bf16x8 qf[NK];
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk) qf[kk] = rd_row(qs, addr0.row(0, kk));
 
   double_buffered(cnt, [&](int t, auto parity) {
     constexpr bool odd = decltype(parity)::value == 1;
@@ -1379,14 +1387,22 @@ void dkdv_pair_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
   const int h = lane >> 5, l32 = lane & 31;
   const size_t base = (size_t)bh * N * D;
 
-  // K and V fragments of this wave's keys, zero past N
+  // K and V fragments of this wave's keys, zero past N.  Without the fused
+  // dQ, the K rows are copied whole into this wave's second slice buffer
+  // (free until step 0 issues its copy) and read from there once the first
+  // slice's copy is out.
+  uint32_t uo[4];
+  unit_offsets(lane, uo);
+  uint16_t* kst = kb == 0 ? sq1 : so1;
+  if constexpr (!DQ)
+    copy_groups<2>(make_rsrc(k + base, (uint32_t)N * D * 2), key0 + 32 * kb, 0, kst, uo);
   bf16x8 kf[NK], vf[NK];
   {
     const int key = key0 + 32 * kb + l32;
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
       const size_t off = base + (size_t)key * D + 16 * kk + 8 * h;
-      kf[kk] = key < N ? load8(k + off) : zero8();
+      if constexpr (DQ) kf[kk] = key < N ? load8(k + off) : zero8();
       vf[kk] = key < N ? load8(v + off) : zero8();
     }
   }
@@ -1399,8 +1415,6 @@ void dkdv_pair_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
   const rsrc_t rsrc = make_rsrc((kb == 0 ? q : dout) + base, (uint32_t)N * D * 2);
   const int G = stat_groups(N);
   const rsrc_t rst = make_rsrc(stats + (size_t)bh * G * 64, (uint32_t)G * 256);
-  uint32_t uo[4];
-  unit_offsets(lane, uo);
   auto slice_row = [&](int s) { return s < steps ? lst[s / SUB] * BQ + 32 * (s % SUB) : 0; };
   auto copy = [&](int row0, uint16_t* dq_, uint16_t* do_, float* ds_) {
     if (kb == 0) {
@@ -1426,6 +1440,15 @@ void dkdv_pair_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
   int row_cur = slice_row(0);
   if (steps > 0) copy(row_cur, sq0, so0, st0);
   int row_nxt = slice_row(1);
+  if constexpr (!DQ) {
+    // the K copy went out before the first slice's (at least 8) copy instructions
+    if (steps > 0) wait_vm_lgkm0<8>();
+    else wait_vm_lgkm0<0>();
+    wave_lds_sync();
+    const SwzAddr ka(lane);
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) kf[kk] = rd_row(kst, ka.row(0, kk));
+  }
   double_buffered(steps, [&](int s, auto parity) {
     constexpr bool odd = decltype(parity)::value == 1;
     const uint16_t* sq = odd ? sq1 : sq0;
