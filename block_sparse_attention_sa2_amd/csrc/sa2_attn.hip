@@ -1388,9 +1388,9 @@ void dkdv_pair_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
   const size_t base = (size_t)bh * N * D;
 
   // K and V fragments of this wave's keys, zero past N.  Without the fused
-  // dQ, the K rows are copied whole into this wave's second slice buffer
-  // (free until step 0 issues its copy) and read from there once the first
-  // slice's copy is out.
+  // dQ, the K rows and then the V rows are copied whole into this wave's
+  // second slice buffer (free until step 0 issues its copy) and read from
+  // there once the first slice's copy is out.
   uint32_t uo[4];
   unit_offsets(lane, uo);
   uint16_t* kst = kb == 0 ? sq1 : so1;
@@ -1402,8 +1402,10 @@ void dkdv_pair_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
       const size_t off = base + (size_t)key * D + 16 * kk + 8 * h;
-      if constexpr (DQ) kf[kk] = key < N ? load8(k + off) : zero8();
-      vf[kk] = key < N ? load8(v + off) : zero8();
+      if constexpr (DQ) {
+        kf[kk] = key < N ? load8(k + off) : zero8();
+        vf[kk] = key < N ? load8(v + off) : zero8();
+      }
     }
   }
 
@@ -1448,6 +1450,13 @@ void dkdv_pair_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
     const SwzAddr ka(lane);
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) kf[kk] = rd_row(kst, ka.row(0, kk));
+    // then the V rows through the same buffer, once the K reads are done
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    copy_groups<2>(make_rsrc(v + base, (uint32_t)N * D * 2), key0 + 32 * kb, 0, kst, uo);
+    wait_vm_lgkm0<0>();
+    wave_lds_sync();
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) vf[kk] = rd_row(kst, ka.row(0, kk));
   }
   double_buffered(steps, [&](int s, auto parity) {
     constexpr bool odd = decltype(parity)::value == 1;
